@@ -1,0 +1,237 @@
+"""CPU oracle for the speculative-decoding verify step -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the GPU library:
+``oracle.c`` is a plain single-threaded fp64 implementation of the rule stated
+in the encyclopedia entry "Speculative decoding" (glopedia, 推测解码), section
+"Basic steps of proposal and verification" (提议与核验的基本步骤), and
+``exact.py`` restates the same rule over exact rationals for tiny vocabularies.
+
+Logits are passed as numpy arrays: ``float32`` for fp32 logits, ``uint16``
+holding the raw bfloat16 bit patterns for bf16 logits.  Strides are taken from
+the arrays themselves, so ``numpy.broadcast_to`` views (stride 0 over the
+sequence axis) are accepted.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+
+F32, BF16 = 0, 1
+NEAR_ACCEPT, NEAR_SAMPLE, NEAR_TOPP = 1, 2, 4
+
+
+def _compile(src: str, out: str) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-I", _HERE, "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+
+
+def build(force: bool = False) -> str:
+    """Compile ``oracle.c`` with gcc into ``liboracle.so`` (IEEE semantics, no
+    FMA contraction, no fast-math)."""
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "oracle.h")))
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
+        _compile(_SRC, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_double
+    lib.orc_process_row.argtypes = [vp, i32, i32, f64, i32, f64, vp, vp]
+    lib.orc_process_row.restype = i32
+    lib.orc_sample_row.argtypes = [vp, i32, i32, f64, i32, f64, f64]
+    lib.orc_sample_row.restype = i32
+    lib.orc_argmax_row.argtypes = [vp, i32, i32]
+    lib.orc_argmax_row.restype = i32
+    lib.orc_verify_stochastic.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp,
+                                          i32, i32, i32, f64, i32, f64, vp, vp, vp, vp]
+    lib.orc_verify_stochastic.restype = i32
+    lib.orc_verify_greedy.argtypes = [vp, i64, i64, i32, vp, i32, i32, i32, vp, vp]
+    lib.orc_verify_greedy.restype = i32
+    return lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("logits must be float32 or uint16 (bfloat16 bits), got %s" % a.dtype)
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _row(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.ndim != 1:
+        raise ValueError("expected one row")
+    return a
+
+
+def _strides(a: np.ndarray):
+    if a.ndim != 3:
+        raise ValueError("logits must be [B][rows][V]")
+    if a.strides[2] != a.itemsize:
+        raise ValueError("the vocabulary axis must be contiguous")
+    return a.strides[0] // a.itemsize, a.strides[1] // a.itemsize
+
+
+class Oracle:
+    """The oracle's entry points bound to one compiled library."""
+
+    def __init__(self, lib):
+        self.lib = lib
+
+    @classmethod
+    def from_source(cls, src_path: str, lib_path: str) -> "Oracle":
+        """Compile another copy of the oracle source (used by tests that plant
+        mistakes in a copy, on the CPU, to check that the pins catch them)."""
+        _compile(src_path, lib_path)
+        return cls(_bind(lib_path))
+
+    def process_row(self, row, temperature=1.0, top_k=0, top_p=1.0):
+        """Return (valid, probs[V] float64, stats) for one logits row."""
+        row = _row(row)
+        V = row.shape[0]
+        probs = np.zeros(V, np.float64)
+        stats = np.zeros(5, np.float64)
+        valid = self.lib.orc_process_row(_ptr(row), _dtype_code(row), V, float(temperature),
+                                         int(top_k), float(top_p), _ptr(probs), _ptr(stats))
+        return bool(valid), probs, {"max_logit": stats[0], "threshold": stats[1],
+                                    "log_norm": stats[2], "mass_above_cut": stats[3],
+                                    "mass_at_cut": stats[4]}
+
+    def sample_row(self, row, u, temperature=1.0, top_k=0, top_p=1.0) -> int:
+        """Inverse-CDF draw (ascending vocabulary order) from the processed row."""
+        row = _row(row)
+        return int(self.lib.orc_sample_row(_ptr(row), _dtype_code(row), row.shape[0],
+                                           float(temperature), int(top_k), float(top_p),
+                                           float(u)))
+
+    def argmax_row(self, row) -> int:
+        row = _row(row)
+        return int(self.lib.orc_argmax_row(_ptr(row), _dtype_code(row), row.shape[0]))
+
+    def verify_stochastic(self, target, draft, tokens, uniforms, temperature=1.0, top_k=0,
+                          top_p=1.0):
+        """Stochastic verify of B sequences.  Returns a dict with ``accepted_len``
+        [B], ``out_tokens`` [B][k+1], ``accept_prob`` [B][k] and ``flags`` [B]."""
+        B, k1, V = target.shape
+        k = k1 - 1
+        if draft.shape != (B, k, V) or draft.dtype != target.dtype:
+            raise ValueError("draft must be [B][k][V] with the target's dtype")
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, k)
+        uniforms = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, k + 1)
+        ts, tp = _strides(target)
+        ds, dp = _strides(draft)
+        acc = np.zeros(B, np.int32)
+        out = np.zeros((B, k + 1), np.int32)
+        ap = np.zeros((B, k), np.float64)
+        flags = np.zeros(B, np.int32)
+        rc = self.lib.orc_verify_stochastic(_ptr(target), ts, tp, _ptr(draft), ds, dp,
+                                            _dtype_code(target), _ptr(tokens), _ptr(uniforms),
+                                            B, k, V, float(temperature), int(top_k),
+                                            float(top_p), _ptr(acc), _ptr(out), _ptr(ap),
+                                            _ptr(flags))
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+        return {"accepted_len": acc, "out_tokens": out, "accept_prob": ap, "flags": flags}
+
+    def verify_greedy(self, target, tokens):
+        """Greedy verify.  Returns (accepted_len [B], out_tokens [B][k+1])."""
+        B, k1, V = target.shape
+        k = k1 - 1
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, k)
+        ts, tp = _strides(target)
+        acc = np.zeros(B, np.int32)
+        out = np.zeros((B, k + 1), np.int32)
+        rc = self.lib.orc_verify_greedy(_ptr(target), ts, tp, _dtype_code(target),
+                                        _ptr(tokens), B, k, V, _ptr(acc), _ptr(out))
+        if rc != 0:
+            raise MemoryError("oracle allocation failed")
+        return acc, out
+
+    def sample_drafts(self, draft, u, temperature=1.0, top_k=0, top_p=1.0, threads=1):
+        """Draw one token per draft row ([B][k][V]) from the processed q with the
+        uniforms u [B][k] -- the proposer's own sampling, so that drafts meet the
+        precondition that they come from the processed q."""
+        B, k, V = draft.shape
+        u = np.asarray(u, np.float64).reshape(B, k)
+        out = np.zeros((B, k), np.int32)
+
+        def work(lo, hi):
+            for b in range(lo, hi):
+                for j in range(k):
+                    out[b, j] = self.sample_row(draft[b, j], u[b, j], temperature, top_k, top_p)
+
+        if threads <= 1 or B == 1:
+            work(0, B)
+        else:
+            step = (B + threads - 1) // threads
+            ths = [threading.Thread(target=work, args=(i, min(B, i + step)))
+                   for i in range(0, B, step)]
+            for t in ths:
+                t.start()
+            for t in ths:
+                t.join()
+        return out
+
+    def argmax_drafts(self, draft):
+        B, k, V = draft.shape
+        return np.array([[self.argmax_row(draft[b, j]) for j in range(k)] for b in range(B)],
+                        np.int32)
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    with _lock:
+        if _default is None:
+            _default = Oracle(_bind(build()))
+    return _default
+
+
+def process_row(row, temperature=1.0, top_k=0, top_p=1.0):
+    return default().process_row(row, temperature, top_k, top_p)
+
+
+def sample_row(row, u, temperature=1.0, top_k=0, top_p=1.0):
+    return default().sample_row(row, u, temperature, top_k, top_p)
+
+
+def argmax_row(row):
+    return default().argmax_row(row)
+
+
+def verify_stochastic(target, draft, tokens, uniforms, temperature=1.0, top_k=0, top_p=1.0):
+    return default().verify_stochastic(target, draft, tokens, uniforms, temperature, top_k,
+                                       top_p)
+
+
+def verify_greedy(target, tokens):
+    return default().verify_greedy(target, tokens)
+
+
+def sample_drafts(draft, u, temperature=1.0, top_k=0, top_p=1.0, threads=1):
+    return default().sample_drafts(draft, u, temperature, top_k, top_p, threads)
+
+
+def argmax_drafts(draft):
+    return default().argmax_drafts(draft)

@@ -1,0 +1,61 @@
+"""Plant plausible mistakes in copies of the oracle source (on the CPU) and
+check that the pins catch every one of them.  The real oracle is untouched;
+each mutant is compiled into a temporary library of its own."""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTATIONS = {
+    "ratio inverted (q/p)": ("double a = p / q;", "double a = q / p;", 1),
+    "residual sign flipped (q - p)": ("double d = pn[i] - qn[i];", "double d = qn[i] - pn[i];", 1),
+    "residual not clipped at zero": ("r[i] = d > 0.0 ? d : 0.0;", "r[i] = d;", 1),
+    "resample from p instead of the residual": ("if (S == 0.0)\n        for", "if (1)\n        for", 1),
+    "no stop at first rejection": ("alpha[j])) {\n        n = j;\n        break;",
+                                   "alpha[j])) {\n        n = j;", 1),
+    "non-strict accept (u <= alpha)": ("!((double)ub[j] < alpha[j])", "!((double)ub[j] <= alpha[j])", 1),
+    "bonus from the last drafted row": ("} else {\n      for (int i = 0; i < V; i++) r[i] = pn[i];",
+                                        "} else {\n      for (int i = 0; i < V; i++) r[i] = P[(size_t)(k - 1) * V + i];", 1),
+    "temperature multiplies": ("(l[i] - m) / T", "(l[i] - m) * T", None),
+    "top-k off by one": ("t_k = scratch[top_k - 1];", "t_k = scratch[top_k];", 1),
+    "top-p not renormalised after top-k": ("cum += exp((scratch[j] - m) / T) / z_k;",
+                                           "cum += exp((scratch[j] - m) / T) / (z_k * 1.5);", 1),
+    "inverse CDF uses >=": ("if (run > target) {", "if (run >= target) {", 1),
+    "greedy keeps the last maximum": ("l[i] > l[best]", "l[i] >= l[best]", 1),
+    "bf16 decoded with the wrong shift": ("((uint32_t)half) << 16", "((uint32_t)half) << 15", 1),
+    "max logit ignored in the exponent": ("if (l[i] >= thr) z += exp((l[i] - m) / T);",
+                                          "if (l[i] >= thr) z += exp((l[i] - m + 0.25) / T);", 1),
+    "q = 0 rejects a token p supports": ("return p > 0.0 ? 1.0 : 0.0;", "return 0.0;", 1),
+}
+
+FAST_PINS = [p for p in pins.ALL_PINS if p is not pins.pin_chi_square]
+
+
+def _mutant(tmp_path, name, old, new, count):
+    src = open(SRC).read()
+    assert old in src, name
+    if count is not None:
+        assert src.count(old) == count, (name, src.count(old))
+    mutated = src.replace(old, new)
+    path = tmp_path / "mutant.c"
+    path.write_text(mutated)
+    return oracle.Oracle.from_source(str(path), str(tmp_path / "libmutant.so"))
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(tmp_path, name):
+    old, new, count = MUTATIONS[name]
+    orc = _mutant(tmp_path, name, old, new, count)
+    caught = []
+    for pin in FAST_PINS + [lambda o: pins.pin_chi_square(o, n=200_000)]:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(getattr(pin, "__name__", "chi_square"))
+        except Exception as e:  # a crash or a NaN path also counts as caught
+            caught.append("%s raised %s" % (getattr(pin, "__name__", "?"), type(e).__name__))
+    assert caught, "no pin caught the planted mistake: %s" % name
