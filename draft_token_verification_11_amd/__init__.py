@@ -1,0 +1,242 @@
+"""libspecverify: the speculative-decoding verify step on one MI355X (gfx950).
+
+This package is a thin binding over the C ABI declared in
+``include/specverify.h``: it marshals torch tensors (device memory, strides,
+the current HIP stream) into the C calls; every step of the verify runs in the
+library's HIP kernels.  The raw C functions are reachable as
+``lib().spec_verify_stochastic`` etc.; the wrappers below keep the same names
+without the ``spec_`` prefix.
+
+The rule (encyclopedia entry "Speculative decoding", glopedia, section "Basic
+steps of proposal and verification"): accept each draft with probability
+min(1, p/q), stop at the first rejection, redraw that position from the
+normalised residual max(0, p - q), or draw a bonus token from the target when
+every draft passes; greedy mode compares argmaxes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = ["lib", "verify_stochastic", "verify_greedy", "logits_process", "workspace_size",
+           "status_string", "SpecError", "library_path"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = range(5)
+SPEC_DTYPE_F32, SPEC_DTYPE_BF16 = 0, 1
+SPEC_OP_STOCHASTIC, SPEC_OP_GREEDY, SPEC_OP_PROCESS = 0, 1, 2
+
+
+class spec_logits_t(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("seq_stride", ctypes.c_int64),
+                ("pos_stride", ctypes.c_int64)]
+
+
+class spec_sampling_t(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("top_p", ctypes.c_float)]
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: %s" % (where, status_string(status)))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libspecverify.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    "libspecverify.so is missing at %s; build it with "
+                    "`python -c 'import __graft_entry__ as g; g.build()'`" % _LIB_PATH)
+            L = ctypes.CDLL(_LIB_PATH)
+            vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+            P = ctypes.POINTER
+            L.spec_workspace_size.argtypes = [i32, i32, i32, i32, P(spec_sampling_t)]
+            L.spec_workspace_size.restype = sz
+            L.spec_verify_stochastic.argtypes = [spec_logits_t, spec_logits_t, vp, vp, i32, i32,
+                                                 i32, P(spec_sampling_t), vp, vp, vp, vp, sz, vp]
+            L.spec_verify_stochastic.restype = ctypes.c_int
+            L.spec_verify_greedy.argtypes = [spec_logits_t, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+            L.spec_verify_greedy.restype = ctypes.c_int
+            L.spec_logits_process.argtypes = [spec_logits_t, i32, i32, P(spec_sampling_t), vp, vp,
+                                              vp, sz, vp]
+            L.spec_logits_process.restype = ctypes.c_int
+            L.spec_status_string.argtypes = [ctypes.c_int]
+            L.spec_status_string.restype = ctypes.c_char_p
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().spec_status_string(int(status)).decode()
+
+
+def _sampling(temperature: float, top_k: int, top_p: float) -> spec_sampling_t:
+    return spec_sampling_t(float(temperature), int(top_k), float(top_p))
+
+
+def workspace_size(op: int, B: int, k: int, V: int, temperature: float = 1.0, top_k: int = 0,
+                   top_p: float = 1.0) -> int:
+    s = _sampling(temperature, top_k, top_p)
+    return int(lib().spec_workspace_size(int(op), int(B), int(k), int(V), ctypes.byref(s)))
+
+
+# One zero-filled workspace per device, grown on demand.  The library leaves
+# it zero-filled after every call, so calls ordered on one stream can share it.
+_ws = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    with _lock:
+        buf = _ws.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            _ws[key] = buf
+    return buf
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SPEC_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_DTYPE_BF16
+    raise TypeError("logits must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _logits(t: torch.Tensor, rows: int) -> spec_logits_t:
+    if t.dim() != 3 or t.shape[1] != rows:
+        raise ValueError("expected logits of shape [B][%d][V], got %s" % (rows, tuple(t.shape)))
+    if not t.is_cuda:
+        raise ValueError("logits must live in device memory")
+    if t.stride(2) != 1:
+        raise ValueError("the vocabulary axis must be contiguous")
+    return spec_logits_t(t.data_ptr(), _dtype_code(t), 0, t.stride(0), t.stride(1))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != SPEC_OK:
+        raise SpecError(rc, where)
+
+
+def verify_stochastic(target: torch.Tensor, draft: torch.Tensor, draft_tokens: torch.Tensor,
+                      uniforms: torch.Tensor, *, temperature: float = 1.0, top_k: int = 0,
+                      top_p: float = 1.0, return_accept_prob: bool = False, out=None,
+                      workspace: torch.Tensor | None = None, stream=None):
+    """Stochastic verify.  target [B][k+1][V], draft [B][k][V] (same dtype,
+    fp32 or bf16), draft_tokens [B][k] int32, uniforms [B][k+1] float32.
+    Returns (accepted_len [B], out_tokens [B][k+1]) and, on request,
+    accept_prob [B][k]."""
+    B, k = draft_tokens.shape
+    V = target.shape[2]
+    tgt, drf = _logits(target, k + 1), _logits(draft, k)
+    if draft.shape[0] != B or target.shape[0] != B or draft.shape[2] != V:
+        raise ValueError("target, draft and draft_tokens disagree on B or V")
+    tokens = draft_tokens.to(torch.int32).contiguous()
+    u = uniforms.to(torch.float32).contiguous()
+    if tuple(u.shape) != (B, k + 1):
+        raise ValueError("uniforms must be [B][k+1]")
+    dev = target.device
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+        ap = torch.empty((B, k), dtype=torch.float32, device=dev) if return_accept_prob else None
+    else:
+        acc, toks, ap = out
+    s = _sampling(temperature, top_k, top_p)
+    need = lib().spec_workspace_size(SPEC_OP_STOCHASTIC, B, k, V, ctypes.byref(s))
+    if need == 0:
+        _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size")
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    rc = lib().spec_verify_stochastic(tgt, drf, tokens.data_ptr(), u.data_ptr(), B, k, V,
+                                      ctypes.byref(s), acc.data_ptr(), toks.data_ptr(),
+                                      ap.data_ptr() if ap is not None else None,
+                                      ws.data_ptr(), ws.numel() * ws.element_size(),
+                                      _stream(stream))
+    _check(rc, "spec_verify_stochastic")
+    return (acc, toks, ap) if return_accept_prob else (acc, toks)
+
+
+def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out=None,
+                  workspace: torch.Tensor | None = None, stream=None):
+    """Greedy verify.  target [B][k+1][V], draft_tokens [B][k] int32.
+    Returns (accepted_len [B], out_tokens [B][k+1])."""
+    B, k = draft_tokens.shape
+    V = target.shape[2]
+    tgt = _logits(target, k + 1)
+    tokens = draft_tokens.to(torch.int32).contiguous()
+    dev = target.device
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    else:
+        acc, toks = out
+    need = lib().spec_workspace_size(SPEC_OP_GREEDY, B, k, V, None)
+    if need == 0:
+        _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size")
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    rc = lib().spec_verify_greedy(tgt, tokens.data_ptr(), B, k, V, acc.data_ptr(), toks.data_ptr(),
+                                  ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "spec_verify_greedy")
+    return acc, toks
+
+
+def logits_process(logits: torch.Tensor, *, temperature: float = 1.0, top_k: int = 0,
+                   top_p: float = 1.0, return_probs: bool = True,
+                   workspace: torch.Tensor | None = None, stream=None):
+    """Processes the rows of ``logits`` ([R][V] or [B][rows][V] with a
+    contiguous vocabulary axis and uniformly strided rows).  Returns a dict
+    with per-row ``max_logit``, ``threshold``, ``log_norm``, ``valid`` and,
+    if requested, the dense fp32 ``probs`` [R][V]."""
+    if logits.dim() == 3:
+        if logits.stride(0) != logits.shape[1] * logits.stride(1):
+            raise ValueError("rows must be uniformly strided")
+        logits2 = logits.reshape(-1, logits.shape[2]) if logits.is_contiguous() else None
+        if logits2 is None:
+            raise ValueError("rows must be uniformly strided")
+        logits = logits2
+    if logits.dim() != 2 or logits.stride(1) != 1 or not logits.is_cuda:
+        raise ValueError("logits must be a device tensor [R][V] with a contiguous last axis")
+    R, V = logits.shape
+    desc = spec_logits_t(logits.data_ptr(), _dtype_code(logits), 0, 0, logits.stride(0))
+    s = _sampling(temperature, top_k, top_p)
+    dev = logits.device
+    stats = torch.empty((R, 4), dtype=torch.float32, device=dev)
+    probs = torch.empty((R, V), dtype=torch.float32, device=dev) if return_probs else None
+    need = lib().spec_workspace_size(SPEC_OP_PROCESS, R, 0, V, ctypes.byref(s))
+    if need == 0:
+        _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size")
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    rc = lib().spec_logits_process(desc, R, V, ctypes.byref(s), stats.data_ptr(),
+                                   probs.data_ptr() if probs is not None else None,
+                                   ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "spec_logits_process")
+    out = {"max_logit": stats[:, 0], "threshold": stats[:, 1], "log_norm": stats[:, 2],
+           "valid": stats[:, 3].view(torch.int32)}
+    if probs is not None:
+        out["probs"] = probs
+    return out

@@ -1,0 +1,339 @@
+// sv_abi.hip -- the C ABI of libspecverify: argument validation, workspace
+// layout and kernel launches for gfx950.  See include/specverify.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "specverify.h"
+#include "sv_kernels.hpp"
+
+namespace {
+
+constexpr int kRowThreads = 256;     // split-V chunk kernels
+constexpr int kFilterThreads = 1024;  // one workgroup per filtered row
+constexpr int kTailThreads = 512;     // one workgroup per sequence
+constexpr int64_t kMinBlocks = 2048;  // split-V target occupancy (8 per CU)
+constexpr int64_t kMaxWorkItems = (int64_t(1) << 32) - 1;
+
+struct Layout {
+  bool filtered = false;
+  int vpt = 1;       // 8-element groups per thread in split-V kernels
+  int nchunks = 1;   // V-chunks per row
+  int64_t rows = 0;  // rows processed
+  size_t rowstat_off = 0, part_off = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t chunk_elems(int vpt) { return int64_t(kRowThreads) * vpt * 8; }
+
+int pick_vpt(int64_t rows, int64_t V) {
+  // Largest register tile that still gives the chip enough workgroups.
+  for (int vpt : {8, 4, 2}) {
+    const int64_t nch = (V + chunk_elems(vpt) - 1) / chunk_elems(vpt);
+    if (rows * nch >= kMinBlocks) return vpt;
+  }
+  return 1;
+}
+
+bool is_filtered(const spec_sampling_t& s, int64_t V) {
+  return (s.top_k > 0 && int64_t(s.top_k) < V) || s.top_p < 1.0f;
+}
+
+Layout make_layout(int op, int64_t B, int64_t k, int64_t V, const spec_sampling_t* s) {
+  Layout L;
+  if (op == SPEC_OP_STOCHASTIC) L.rows = B * (2 * k + 1);
+  else if (op == SPEC_OP_GREEDY) L.rows = B * (k + 1);
+  else L.rows = B;
+  L.filtered = (op != SPEC_OP_GREEDY) && is_filtered(*s, V);
+  L.vpt = pick_vpt(L.rows, V);
+  L.nchunks = int((V + chunk_elems(L.vpt) - 1) / chunk_elems(L.vpt));
+  size_t off = 0;
+  const bool need_rowstat = L.filtered || op == SPEC_OP_PROCESS;
+  const bool need_part = !L.filtered;
+  if (need_rowstat) {
+    L.rowstat_off = off;
+    off = align256(off + size_t(L.rows) * sizeof(sv::RowStat));
+  }
+  if (need_part) {
+    L.part_off = off;
+    off = align256(off + size_t(L.rows) * size_t(L.nchunks) * 16);
+  }
+  L.total = off < 256 ? 256 : off;
+  return L;
+}
+
+size_t elem_size(int dtype) { return dtype == SPEC_DTYPE_BF16 ? 2 : 4; }
+
+int check_logits(const spec_logits_t& t, int64_t V) {
+  if (t.dtype != SPEC_DTYPE_F32 && t.dtype != SPEC_DTYPE_BF16) return SPEC_ERR_UNSUPPORTED;
+  if (!t.data) return SPEC_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(t.data) % elem_size(t.dtype)) return SPEC_ERR_INVALID_ARG;
+  if (t.pos_stride < V || t.seq_stride < 0) return SPEC_ERR_INVALID_ARG;
+  return SPEC_OK;
+}
+
+bool vec_ok(const spec_logits_t& t) {
+  const size_t es = elem_size(t.dtype);
+  return reinterpret_cast<uintptr_t>(t.data) % 16 == 0 && (size_t(t.pos_stride) * es) % 16 == 0 &&
+         (size_t(t.seq_stride) * es) % 16 == 0;
+}
+
+int check_sampling(const spec_sampling_t* s) {
+  if (!s) return SPEC_ERR_INVALID_ARG;
+  if (!std::isfinite(s->temperature) || !(s->temperature > 0.0f)) return SPEC_ERR_INVALID_ARG;
+  if (s->top_k < 0) return SPEC_ERR_INVALID_ARG;
+  if (!(s->top_p > 0.0f && s->top_p <= 1.0f)) return SPEC_ERR_INVALID_ARG;
+  return SPEC_OK;
+}
+
+int check_sizes(int64_t B, int64_t k, int64_t V, bool need_k) {
+  if (B < 1 || V < 1) return SPEC_ERR_INVALID_ARG;
+  if (need_k && k < 1) return SPEC_ERR_INVALID_ARG;
+  if (B > (int64_t(1) << 24) || V > SPEC_MAX_V || (need_k && k > SPEC_MAX_K))
+    return SPEC_ERR_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+int check_workspace(void* ws, size_t bytes, const Layout& L) {
+  if (!ws || bytes < L.total || reinterpret_cast<uintptr_t>(ws) % 256) return SPEC_ERR_WORKSPACE;
+  return SPEC_OK;
+}
+
+bool grid_fits(int64_t blocks, int threads) { return blocks >= 1 && blocks * threads <= kMaxWorkItems; }
+
+float log2e_over(float T) { return float(1.4426950408889634 / double(T)); }
+
+template <typename T, bool VEC>
+void launch_partials(const Layout& L, const sv::RowMap& map, int64_t V, float a, sv::Partial* part,
+                     hipStream_t st) {
+  const dim3 grid(unsigned(L.rows * L.nchunks)), block(kRowThreads);
+  switch (L.vpt) {
+    case 8: hipLaunchKernelGGL((sv::k_row_partials<T, VEC, 8>), grid, block, 0, st, map, V, L.nchunks, a, part); break;
+    case 4: hipLaunchKernelGGL((sv::k_row_partials<T, VEC, 4>), grid, block, 0, st, map, V, L.nchunks, a, part); break;
+    case 2: hipLaunchKernelGGL((sv::k_row_partials<T, VEC, 2>), grid, block, 0, st, map, V, L.nchunks, a, part); break;
+    default: hipLaunchKernelGGL((sv::k_row_partials<T, VEC, 1>), grid, block, 0, st, map, V, L.nchunks, a, part); break;
+  }
+}
+
+template <typename T, bool VEC>
+void launch_greedy_partials(const Layout& L, const sv::RowMap& map, int64_t V, sv::GPartial* part,
+                            hipStream_t st) {
+  const dim3 grid(unsigned(L.rows * L.nchunks)), block(kRowThreads);
+  switch (L.vpt) {
+    case 8: hipLaunchKernelGGL((sv::k_greedy_partials<T, VEC, 8>), grid, block, 0, st, map, V, L.nchunks, part); break;
+    case 4: hipLaunchKernelGGL((sv::k_greedy_partials<T, VEC, 4>), grid, block, 0, st, map, V, L.nchunks, part); break;
+    case 2: hipLaunchKernelGGL((sv::k_greedy_partials<T, VEC, 2>), grid, block, 0, st, map, V, L.nchunks, part); break;
+    default: hipLaunchKernelGGL((sv::k_greedy_partials<T, VEC, 1>), grid, block, 0, st, map, V, L.nchunks, part); break;
+  }
+}
+
+template <typename T, bool VEC>
+void launch_probs(const Layout& L, const sv::RowMap& map, int64_t V, float a, const sv::RowStat* rs,
+                  float* probs, hipStream_t st) {
+  const dim3 grid(unsigned(L.rows * L.nchunks)), block(kRowThreads);
+  switch (L.vpt) {
+    case 8: hipLaunchKernelGGL((sv::k_probs<T, VEC, 8>), grid, block, 0, st, map, V, L.nchunks, a, rs, probs); break;
+    case 4: hipLaunchKernelGGL((sv::k_probs<T, VEC, 4>), grid, block, 0, st, map, V, L.nchunks, a, rs, probs); break;
+    case 2: hipLaunchKernelGGL((sv::k_probs<T, VEC, 2>), grid, block, 0, st, map, V, L.nchunks, a, rs, probs); break;
+    default: hipLaunchKernelGGL((sv::k_probs<T, VEC, 1>), grid, block, 0, st, map, V, L.nchunks, a, rs, probs); break;
+  }
+}
+
+template <typename T, bool VEC>
+void launch_filter(const Layout& L, const sv::RowMap& map, int64_t V, float a,
+                   const spec_sampling_t& s, sv::RowStat* rs, hipStream_t st) {
+  const dim3 grid(unsigned(L.rows)), block(kFilterThreads);
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((sv::k_filter_bf16_hist<VEC>), grid, block, 0, st, map, V, a, s.top_k,
+                       s.top_p, rs);
+  } else {
+    hipLaunchKernelGGL((sv::k_filter_bisect<T, VEC>), grid, block, 0, st, map, V, a, s.top_k,
+                       s.top_p, rs);
+  }
+}
+
+template <typename T, bool VEC>
+void launch_tail(int64_t B, const sv::TailArgs& args, hipStream_t st) {
+  hipLaunchKernelGGL((sv::k_tail<T, VEC>), dim3(unsigned(B)), dim3(kTailThreads), 0, st, args);
+}
+
+// Runs f<T, VEC>() for the dtype / alignment at hand.
+template <template <typename, bool> class F, typename... Args>
+void dispatch(int dtype, bool vec, Args&&... args) {
+  if (dtype == SPEC_DTYPE_BF16) {
+    if (vec) F<uint16_t, true>::run(args...);
+    else F<uint16_t, false>::run(args...);
+  } else {
+    if (vec) F<float, true>::run(args...);
+    else F<float, false>::run(args...);
+  }
+}
+
+template <typename T, bool VEC>
+struct StochasticRun {
+  static void run(const Layout& L, const sv::RowMap& map, int64_t B, int64_t V, float a,
+                  const spec_sampling_t& s, sv::TailArgs& args, char* ws, hipStream_t st) {
+    if (L.filtered) {
+      auto* rs = reinterpret_cast<sv::RowStat*>(ws + L.rowstat_off);
+      launch_filter<T, VEC>(L, map, V, a, s, rs, st);
+      args.rowstat = rs;
+      args.part = nullptr;
+    } else {
+      auto* part = reinterpret_cast<sv::Partial*>(ws + L.part_off);
+      launch_partials<T, VEC>(L, map, V, a, part, st);
+      args.rowstat = nullptr;
+      args.part = part;
+    }
+    args.nchunks = L.nchunks;
+    launch_tail<T, VEC>(B, args, st);
+  }
+};
+
+template <typename T, bool VEC>
+struct GreedyRun {
+  static void run(const Layout& L, const sv::RowMap& map, int64_t V, sv::GPartial* part, hipStream_t st) {
+    launch_greedy_partials<T, VEC>(L, map, V, part, st);
+  }
+};
+
+template <typename T, bool VEC>
+struct ProcessRun {
+  static void run(const Layout& L, const sv::RowMap& map, int64_t V, float a, const spec_sampling_t& s,
+                  spec_row_stats_t* row_stats, float* probs, char* ws, hipStream_t st) {
+    auto* rs = reinterpret_cast<sv::RowStat*>(ws + L.rowstat_off);
+    sv::Partial* part = nullptr;
+    if (L.filtered) {
+      launch_filter<T, VEC>(L, map, V, a, s, rs, st);
+    } else {
+      part = reinterpret_cast<sv::Partial*>(ws + L.part_off);
+      launch_partials<T, VEC>(L, map, V, a, part, st);
+    }
+    hipLaunchKernelGGL(sv::k_process_stats, dim3(unsigned((L.rows + 255) / 256)), dim3(256), 0, st,
+                       L.rows, L.nchunks, a, part, rs, row_stats);
+    if (probs) launch_probs<T, VEC>(L, map, V, a, rs, probs, st);
+  }
+};
+
+int finish_launch() {
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_workspace_size(int32_t op, int32_t B, int32_t k, int32_t V,
+                           const spec_sampling_t* sampling) {
+  if (op != SPEC_OP_STOCHASTIC && op != SPEC_OP_GREEDY && op != SPEC_OP_PROCESS) return 0;
+  if (check_sizes(B, k, V, op != SPEC_OP_PROCESS) != SPEC_OK) return 0;
+  spec_sampling_t plain = {1.0f, 0, 1.0f};
+  if (op != SPEC_OP_GREEDY) {
+    if (check_sampling(sampling) != SPEC_OK) return 0;
+  } else {
+    sampling = &plain;
+  }
+  return make_layout(op, B, k, V, sampling).total;
+}
+
+int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft, const int32_t* draft_tokens,
+                           const float* uniforms, int32_t B, int32_t k, int32_t V,
+                           const spec_sampling_t* sampling, int32_t* accepted_len,
+                           int32_t* out_tokens, float* accept_prob, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_sizes(B, k, V, true)) != SPEC_OK) return rc;
+  if ((rc = check_sampling(sampling)) != SPEC_OK) return rc;
+  if ((rc = check_logits(target, V)) != SPEC_OK) return rc;
+  if ((rc = check_logits(draft, V)) != SPEC_OK) return rc;
+  if (target.dtype != draft.dtype) return SPEC_ERR_INVALID_ARG;
+  if (!draft_tokens || !uniforms || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
+  const Layout L = make_layout(SPEC_OP_STOCHASTIC, B, k, V, sampling);
+  if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
+  if (!grid_fits(L.filtered ? L.rows : L.rows * L.nchunks,
+                 L.filtered ? kFilterThreads : kRowThreads) ||
+      !grid_fits(B, kTailThreads))
+    return SPEC_ERR_UNSUPPORTED;
+
+  sv::RowMap map{target.data, target.seq_stride, target.pos_stride, draft.data, draft.seq_stride,
+                 draft.pos_stride, 2 * k + 1, k + 1};
+  const float a = log2e_over(sampling->temperature);
+  sv::TailArgs args{};
+  args.map = map;
+  args.V = V;
+  args.k = k;
+  args.a = a;
+  args.tokens = draft_tokens;
+  args.u = uniforms;
+  args.accepted_len = accepted_len;
+  args.out_tokens = out_tokens;
+  args.accept_prob = accept_prob;
+  const bool vec = vec_ok(target) && vec_ok(draft);
+  (void)hipGetLastError();
+  dispatch<StochasticRun>(target.dtype, vec, L, map, int64_t(B), int64_t(V), a, *sampling, args,
+                          static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return finish_launch();
+}
+
+int spec_verify_greedy(spec_logits_t target, const int32_t* draft_tokens, int32_t B, int32_t k,
+                       int32_t V, int32_t* accepted_len, int32_t* out_tokens, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_sizes(B, k, V, true)) != SPEC_OK) return rc;
+  if ((rc = check_logits(target, V)) != SPEC_OK) return rc;
+  if (!draft_tokens || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
+  const spec_sampling_t plain = {1.0f, 0, 1.0f};
+  const Layout L = make_layout(SPEC_OP_GREEDY, B, k, V, &plain);
+  if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
+  if (!grid_fits(L.rows * L.nchunks, kRowThreads) || !grid_fits(B, 64)) return SPEC_ERR_UNSUPPORTED;
+  sv::RowMap map{target.data, target.seq_stride, target.pos_stride, target.data, target.seq_stride,
+                 target.pos_stride, k + 1, k + 1};
+  auto* part = reinterpret_cast<sv::GPartial*>(static_cast<char*>(workspace) + L.part_off);
+  auto st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  dispatch<GreedyRun>(target.dtype, vec_ok(target), L, map, int64_t(V), part, st);
+  hipLaunchKernelGGL(sv::k_greedy_tail, dim3(unsigned(B)), dim3(64), 0, st, int64_t(V), k,
+                     L.nchunks, draft_tokens, part, accepted_len, out_tokens);
+  return finish_launch();
+}
+
+int spec_logits_process(spec_logits_t logits, int32_t R, int32_t V, const spec_sampling_t* sampling,
+                        spec_row_stats_t* row_stats, float* probs, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_sizes(R, 1, V, false)) != SPEC_OK) return rc;
+  if ((rc = check_sampling(sampling)) != SPEC_OK) return rc;
+  logits.seq_stride = logits.pos_stride;  // row r lives at data + r * pos_stride
+  if ((rc = check_logits(logits, V)) != SPEC_OK) return rc;
+  const Layout L = make_layout(SPEC_OP_PROCESS, R, 1, V, sampling);
+  if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
+  if (!grid_fits(L.filtered ? L.rows : L.rows * L.nchunks,
+                 L.filtered ? kFilterThreads : kRowThreads))
+    return SPEC_ERR_UNSUPPORTED;
+  sv::RowMap map{logits.data, logits.pos_stride, 0, logits.data, logits.pos_stride, 0, 1, 1};
+  const float a = log2e_over(sampling->temperature);
+  auto st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  dispatch<ProcessRun>(logits.dtype, vec_ok(logits), L, map, int64_t(V), a, *sampling, row_stats,
+                       probs, static_cast<char*>(workspace), st);
+  // Leave the workspace zero-filled, as the contract promises.
+  const int64_t words = int64_t(L.total / 16);
+  hipLaunchKernelGGL(sv::k_clear, dim3(unsigned((words + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint4*>(workspace), words);
+  return finish_launch();
+}
+
+const char* spec_status_string(int status) {
+  switch (status) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_ERR_INVALID_ARG: return "SPEC_ERR_INVALID_ARG: invalid argument";
+    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED: dtype or size outside the supported limits";
+    case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case SPEC_ERR_HIP: return "SPEC_ERR_HIP: a HIP launch or runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,862 @@
+// sv_kernels.hpp -- HIP kernels (gfx950) of the speculative-decoding verify
+// step: row statistics (max, normaliser, top-k/top-p threshold), greedy
+// argmax, the per-sequence ratio test / first-rejection stop / residual
+// inverse-CDF draw, and dense probabilities.
+//
+// The rule implemented is the one in the encyclopedia entry "Speculative
+// decoding" (glopedia, 推测解码), section "Basic steps of proposal and
+// verification" (提议与核验的基本步骤); see include/specverify.h for the
+// readings taken where the entry is silent.
+//
+// Probability of token x in a row:  p(x) = [l_x >= thr] * 2^((l_x - m) a) / z
+// with m the row's largest finite logit, a = log2(e) / T, thr the filter
+// threshold (-inf without filters) and z the sum of 2^((l - m) a) over the
+// kept set.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specverify.h"
+#include "sv_device.hpp"
+
+namespace sv {
+
+// ---------------------------------------------------------------------------
+// Workspace records.
+struct RowStat {  // 32 bytes
+  float m;        // largest finite logit
+  float thr;      // kept set is {l >= thr}
+  double z;       // sum over the kept set of 2^((l - m) a)
+  int32_t valid;  // 0: NaN/+inf present or no finite logit
+  int32_t pad[3];
+};
+struct Partial {   // 16 bytes: one V-chunk of one row
+  float m;         // chunk max (-inf if the chunk holds no finite logit)
+  uint32_t flags;  // bit 0: NaN or +inf seen
+  double s;        // sum of 2^((l - m) a) over the chunk
+};
+struct GPartial {  // 16 bytes: greedy partial of one V-chunk
+  uint32_t key;    // order key of the chunk's largest finite logit (0 = none)
+  int32_t idx;     // its lowest index
+  uint32_t flags;  // bit 0: NaN or +inf seen
+  uint32_t pad;
+};
+constexpr uint32_t kFlagBad = 1u;
+
+// Flat row id -> row pointer.  A sequence holds `per_seq` rows: the first
+// `k1` are target rows 0..k1-1, the rest draft rows 0..per_seq-k1-1.
+struct RowMap {
+  const void* tgt;
+  int64_t t_seq, t_pos;
+  const void* drf;
+  int64_t d_seq, d_pos;
+  int32_t per_seq;
+  int32_t k1;
+  template <typename T>
+  __device__ __forceinline__ const T* row(int64_t r) const {
+    const int64_t b = r / per_seq;
+    const int64_t w = r - b * per_seq;
+    if (w < k1) return reinterpret_cast<const T*>(tgt) + b * t_seq + w * t_pos;
+    return reinterpret_cast<const T*>(drf) + b * d_seq + (w - k1) * d_pos;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Unfiltered rows: per (row, chunk) max and sum of 2^((l - m_c) a).  Each of
+// the 256 threads holds VPT groups of 8 consecutive elements in registers;
+// group g of the chunk starts at element chunk_lo + 8 g (coalesced 16-byte
+// loads: 1 load per group for bf16, 2 for fp32).
+template <typename T, bool VEC, int VPT>
+__global__ __launch_bounds__(256) void k_row_partials(RowMap map, int64_t V, int nchunks,
+                                                      float a, Partial* __restrict__ part) {
+  constexpr int NT = 256;
+  __shared__ float fslot[NT / kWave];
+  __shared__ double dslot[NT / kWave];
+  __shared__ uint32_t uslot[NT / kWave];
+  const int64_t bid = blockIdx.x;
+  const int64_t r = bid / nchunks;
+  const int c = (int)(bid - r * nchunks);
+  const T* row = map.row<T>(r);
+  const int64_t lo = (int64_t)c * (NT * VPT * 8);
+  const int64_t hi = min(V, lo + (int64_t)NT * VPT * 8);
+
+  float x[VPT][8];
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int64_t e = lo + ((int64_t)v * NT + threadIdx.x) * 8;
+    if (e < hi) {
+      load8<T, VEC>(row, e, hi, x[v]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[v][i] = -__builtin_inff();
+    }
+  }
+  float m = -__builtin_inff();
+  uint32_t bad = 0;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bad |= bad_logit(x[v][i]) ? 1u : 0u;
+      m = fmaxf(m, x[v][i]);
+    }
+  m = block_max<NT>(m, fslot);
+  bad = block_or<NT>(bad, uslot);
+  double s = 0.0;
+  if (!bad && m > -__builtin_inff()) {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = __builtin_amdgcn_exp2f((x[v][i] - m) * a);
+      s += (double)(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+    }
+  }
+  s = block_sum<NT>(s, dslot);
+  if (threadIdx.x == 0) {
+    Partial p;
+    p.m = m;
+    p.flags = bad ? kFlagBad : 0u;
+    p.s = s;
+    part[bid] = p;
+  }
+}
+
+// Merges the chunk partials of one row into a RowStat (unfiltered row).
+__device__ __forceinline__ RowStat merge_partials(const Partial* p, int nchunks, float a) {
+  RowStat st;
+  float m = -__builtin_inff();
+  uint32_t flags = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    m = fmaxf(m, p[c].m);
+    flags |= p[c].flags;
+  }
+  double z = 0.0;
+  if (m > -__builtin_inff()) {
+    for (int c = 0; c < nchunks; ++c)
+      if (p[c].m > -__builtin_inff()) z += p[c].s * exp2(((double)p[c].m - (double)m) * (double)a);
+  }
+  st.m = m;
+  st.thr = -__builtin_inff();
+  st.z = z;
+  st.valid = (!(flags & kFlagBad) && m > -__builtin_inff()) ? 1 : 0;
+  st.pad[0] = st.pad[1] = st.pad[2] = 0;
+  return st;
+}
+
+// ---------------------------------------------------------------------------
+// Greedy: per (row, chunk) largest finite logit (as an order key) and its
+// lowest index.
+__device__ __forceinline__ uint64_t pack_best(uint32_t key, int32_t idx) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, o, kWave);
+    uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), o, kWave);
+    uint64_t y = ((uint64_t)hi << 32) | lo;
+    x = y > x ? y : x;
+  }
+  return x;
+}
+
+template <typename T, bool VEC, int VPT>
+__global__ __launch_bounds__(256) void k_greedy_partials(RowMap map, int64_t V, int nchunks,
+                                                         GPartial* __restrict__ part) {
+  constexpr int NT = 256;
+  __shared__ uint64_t bslot[NT / kWave];
+  __shared__ uint32_t uslot[NT / kWave];
+  const int64_t bid = blockIdx.x;
+  const int64_t r = bid / nchunks;
+  const int c = (int)(bid - r * nchunks);
+  const T* row = map.row<T>(r);
+  const int64_t lo = (int64_t)c * (NT * VPT * 8);
+  const int64_t hi = min(V, lo + (int64_t)NT * VPT * 8);
+  uint64_t best = 0;
+  uint32_t bad = 0;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int64_t e = lo + ((int64_t)v * NT + threadIdx.x) * 8;
+    if (e < hi) {
+      float x[8];
+      load8<T, VEC>(row, e, hi, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool b = bad_logit(x[i]);
+        bad |= b ? 1u : 0u;
+        const uint32_t k = key_of(x[i]);
+        if (!b && k > kKeyNegInf && e + i < hi) {
+          const uint64_t cand = pack_best(k, (int32_t)(e + i));
+          best = cand > best ? cand : best;
+        }
+      }
+    }
+  }
+  best = wave_max_u64(best);
+  bad = wave_or(bad);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    bslot[w] = best;
+    uslot[w] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t bb = bslot[0];
+    uint32_t fl = uslot[0];
+    for (int i = 1; i < NT / kWave; ++i) {
+      bb = bslot[i] > bb ? bslot[i] : bb;
+      fl |= uslot[i];
+    }
+    GPartial g;
+    g.key = (uint32_t)(bb >> 32);
+    g.idx = (int32_t)(0xFFFFFFFFu - (uint32_t)bb);
+    g.flags = fl ? kFlagBad : 0u;
+    g.pad = 0;
+    part[bid] = g;
+  }
+}
+
+// One wave per sequence: merge each target row's greedy partials, compare
+// with the drafts, stop at the first mismatch, emit, clear the partials.
+__global__ __launch_bounds__(64) void k_greedy_tail(int64_t V, int k, int nchunks,
+                                                    const int32_t* __restrict__ tokens,
+                                                    GPartial* __restrict__ part,
+                                                    int32_t* __restrict__ accepted_len,
+                                                    int32_t* __restrict__ out_tokens) {
+  const int64_t b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int k1 = k + 1;
+  __shared__ int32_t best_idx[SPEC_MAX_K + 1];
+  bool ok = true;
+  for (int j = lane; j < k1; j += kWave) {
+    GPartial* p = part + (b * k1 + j) * (int64_t)nchunks;
+    uint64_t bb = 0;
+    uint32_t fl = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const uint64_t cand = pack_best(p[c].key, p[c].idx);
+      if (p[c].key != 0 && cand > bb) bb = cand;
+      fl |= p[c].flags;
+    }
+    for (int c = 0; c < nchunks; ++c) {
+      GPartial zero = {0u, 0, 0u, 0u};
+      p[c] = zero;
+    }
+    const uint32_t key = (uint32_t)(bb >> 32);
+    ok &= (fl == 0) && key != 0;
+    best_idx[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)bb);
+  }
+  int32_t tok = 0;
+  if (lane < k) {
+    tok = tokens[b * k + lane];
+    ok &= (tok >= 0 && (int64_t)tok < V);
+  }
+  const bool all_ok = __ballot(!ok) == 0;
+  __syncthreads();
+  int32_t* out = out_tokens + b * k1;
+  if (!all_ok) {
+    for (int j = lane; j < k1; j += kWave) out[j] = -1;
+    if (lane == 0) accepted_len[b] = -1;
+    return;
+  }
+  const uint64_t mism = __ballot(lane < k && tok != best_idx[lane < k ? lane : 0]);
+  const int n = mism ? (__ffsll((unsigned long long)mism) - 1) : k;
+  for (int j = lane; j < k1; j += kWave) {
+    int32_t v = -1;
+    if (j < n) v = tokens[b * k + j];
+    else if (j == n) v = best_idx[n];
+    out[j] = v;
+  }
+  if (lane == 0) accepted_len[b] = n;
+}
+
+// ---------------------------------------------------------------------------
+// Filtered rows, generic path: the top-k and top-p thresholds found by
+// bisection over the 32-bit order keys, each probe a pass over the row
+// (count of keys >= c for top-k, sum of 2^((l - m) a) over keys >= c for
+// top-p).  Used for fp32 rows and as the fallback of the bf16 histogram.
+template <typename T, bool VEC, int NT>
+__device__ void filter_row_bisect(const T* row, int64_t V, float a, int top_k, float top_p,
+                                  RowStat* out, double* dslot, uint32_t* uslot) {
+  const int64_t ngroups = (V + 7) / 8;
+  uint32_t bad = 0, mk = 0;
+  for (int64_t g = threadIdx.x; g < ngroups; g += NT) {
+    float x[8];
+    load8<T, VEC>(row, g * 8, V, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool b = bad_logit(x[i]);
+      bad |= b ? 1u : 0u;
+      const uint32_t k = key_of(x[i]);
+      if (!b && k > kKeyNegInf) mk = max(mk, k);
+    }
+  }
+  bad = block_or<NT>(bad, uslot);
+  mk = block_max_u32<NT>(mk, uslot);
+  if (bad || mk == 0) {
+    if (threadIdx.x == 0) {
+      RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
+      *out = st;
+    }
+    return;
+  }
+  const float m = value_of(mk);
+  auto count_ge = [&](uint32_t c) -> uint32_t {
+    uint32_t n = 0;
+    for (int64_t g = threadIdx.x; g < ngroups; g += NT) {
+      float x[8];
+      load8<T, VEC>(row, g * 8, V, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) n += (g * 8 + i < V && key_of(x[i]) >= c) ? 1u : 0u;
+    }
+    return block_sum<NT>(n, uslot);
+  };
+  auto mass_ge = [&](uint32_t c) -> double {
+    double s = 0.0;
+    for (int64_t g = threadIdx.x; g < ngroups; g += NT) {
+      float x[8];
+      load8<T, VEC>(row, g * 8, V, x);
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        e[i] = key_of(x[i]) >= c ? __builtin_amdgcn_exp2f((x[i] - m) * a) : 0.0f;
+      s += (double)(((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+    }
+    return block_sum<NT>(s, dslot);
+  };
+  const bool use_k = top_k > 0 && (int64_t)top_k < V;
+  const bool use_p = top_p < 1.0f;
+  uint32_t tk = 0;
+  if (use_k) {
+    uint32_t c = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = c | (1u << bit);
+      if (count_ge(cand) >= (uint32_t)top_k) c = cand;
+    }
+    tk = c;
+  }
+  const double zk = mass_ge(tk);
+  uint32_t thr_key = tk;
+  double z = zk;
+  if (use_p) {
+    const double target = (double)top_p * zk;
+    uint32_t c = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = c | (1u << bit);
+      if (mass_ge(max(cand, tk)) >= target) c = cand;
+    }
+    thr_key = max(c, tk);
+    z = mass_ge(thr_key);
+  }
+  if (threadIdx.x == 0) {
+    RowStat st;
+    st.m = m;
+    st.thr = (use_k || use_p) ? value_of(thr_key) : -__builtin_inff();
+    st.z = z;
+    st.valid = 1;
+    st.pad[0] = st.pad[1] = st.pad[2] = 0;
+    *out = st;
+  }
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(1024) void k_filter_bisect(RowMap map, int64_t V, float a, int top_k,
+                                                        float top_p, RowStat* __restrict__ stats) {
+  __shared__ double dslot[16];
+  __shared__ uint32_t uslot[16];
+  const int64_t r = blockIdx.x;
+  filter_row_bisect<T, VEC, 1024>(map.row<T>(r), V, a, top_k, top_p, stats + r, dslot, uslot);
+}
+
+// ---------------------------------------------------------------------------
+// Filtered bf16 rows: an exact 65536-bin count histogram of the 16-bit order
+// keys in LDS (two 16-bit counters per 32-bit word).  Equal bf16 values have
+// equal probabilities, so counts give the row's sorted value distribution
+// exactly: the max, the top-k threshold (by counts), the per-value masses
+// count * 2^((v - m) a), the top-p cut (by masses) and the normaliser all come
+// from the histogram after one streaming pass, with no per-element exp.
+// Overflow (>= 65536 equal values) is detected by the count total and falls
+// back to the bisection path.
+template <bool VEC>
+__global__ __launch_bounds__(1024) void k_filter_bf16_hist(RowMap map, int64_t V, float a,
+                                                           int top_k, float top_p,
+                                                           RowStat* __restrict__ stats) {
+  constexpr int NT = 1024;
+  __shared__ uint32_t hist[32768];
+  __shared__ uint32_t gcnt[1024];
+  __shared__ double gmass[1024];
+  __shared__ double gsuf[1025];
+  __shared__ double dslot[16];
+  __shared__ uint32_t uslot[16];
+  __shared__ uint32_t sh_key[2];
+  __shared__ double sh_z;
+  const int64_t r = blockIdx.x;
+  const uint16_t* row = map.row<uint16_t>(r);
+  const int tid = threadIdx.x;
+
+  // 1. clear
+  uint4* h4 = reinterpret_cast<uint4*>(hist);
+  for (int i = tid; i < 8192; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+
+  // 2. count: one atomic increment of a 16-bit counter per element
+  const int64_t ngroups = (V + 7) / 8;
+  auto count8 = [&](uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t k0 = key16_of_bits(w[i] & 0xFFFFu);
+      const uint32_t k1 = key16_of_bits(w[i] >> 16);
+      atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
+      atomicAdd(&hist[k1 >> 1], (k1 & 1u) ? 0x10000u : 1u);
+    }
+  };
+  int64_t g = tid;
+  if (VEC) {
+    for (; g + 3 * NT < ngroups && (g + 3 * NT + 1) * 8 <= V; g += 4 * NT) {
+      const uint4 v0 = load16(row + g * 8);
+      const uint4 v1 = load16(row + (g + NT) * 8);
+      const uint4 v2 = load16(row + (g + 2 * NT) * 8);
+      const uint4 v3 = load16(row + (g + 3 * NT) * 8);
+      count8(v0);
+      count8(v1);
+      count8(v2);
+      count8(v3);
+    }
+  }
+  for (; g < ngroups; g += NT) {
+    const int64_t e = g * 8;
+    if (VEC && e + 8 <= V) {
+      count8(load16(row + e));
+    } else {
+      for (int i = 0; i < 8 && e + i < V; ++i) {
+        const uint32_t k0 = key16_of_bits(row[e + i]);
+        atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. -0 and +0 are one value: move the count of key 0x7FFF (-0) to 0x8000.
+  if (tid == 0) {
+    const uint32_t w = hist[0x3FFF];
+    hist[0x3FFF] = w & 0xFFFFu;
+    hist[0x4000] += (w >> 16);
+  }
+  __syncthreads();
+
+  // 4. per 64-key group: count, bad keys, highest finite key
+  uint32_t cnt = 0, badc = 0, mk = 0;
+  {
+    const int grp = tid;
+#pragma unroll 4
+    for (int j = 0; j < 32; ++j) {
+      const int wi = grp * 32 + ((j + grp) & 31);
+      const uint32_t w = hist[wi];
+      const uint32_t c0 = w & 0xFFFFu, c1 = w >> 16;
+      const uint32_t k0 = (uint32_t)wi * 2u, k1 = k0 + 1u;
+      cnt += c0 + c1;
+      const bool b0 = k0 < 0x7Fu || k0 >= 0xFF80u, b1 = k1 < 0x7Fu || k1 >= 0xFF80u;
+      badc |= (b0 && c0) || (b1 && c1);
+      if (c0 && !b0 && k0 > 0x7Fu) mk = max(mk, k0);
+      if (c1 && !b1 && k1 > 0x7Fu) mk = max(mk, k1);
+    }
+    gcnt[grp] = cnt;
+  }
+  const uint32_t total = block_sum<NT>(cnt, uslot);
+  badc = block_or<NT>(badc, uslot);
+  mk = block_max_u32<NT>(mk, uslot);
+  if (badc || mk == 0) {
+    if (tid == 0) {
+      RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
+      stats[r] = st;
+    }
+    return;
+  }
+  if ((int64_t)total != V) {  // a 16-bit counter overflowed
+    __syncthreads();
+    filter_row_bisect<uint16_t, VEC, NT>(row, V, a, top_k, top_p, stats + r, dslot, uslot);
+    return;
+  }
+  const float m = value_of_key16(mk);
+  const uint16_t* c16 = reinterpret_cast<const uint16_t*>(hist);
+  const bool use_k = top_k > 0 && (int64_t)top_k < V;
+  const bool use_p = top_p < 1.0f;
+
+  // 5. top-k threshold key: the largest key whose suffix count reaches top_k
+  uint32_t tk = 0;
+  if (use_k) {
+    uint32_t tot;
+    const uint32_t suf = block_incl_suffix<NT>(cnt, uslot, &tot);
+    if (suf >= (uint32_t)top_k && suf - cnt < (uint32_t)top_k) {
+      uint32_t run = suf - cnt;
+      for (int i = 63; i >= 0; --i) {
+        run += c16[tid * 64 + i];
+        if (run >= (uint32_t)top_k) {
+          sh_key[0] = (uint32_t)(tid * 64 + i);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    tk = sh_key[0];
+  }
+
+  // 6. per-group masses over keys >= tk: sum of count * 2^((v - m) a)
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  for (int gi = 0; gi < 64; ++gi) {
+    const int grp = wv * 64 + gi;
+    double gm = 0.0;
+    if (gcnt[grp] != 0 && (uint32_t)(grp * 64 + 63) >= tk) {
+      const uint32_t key = (uint32_t)(grp * 64 + lane);
+      const uint32_t c = c16[key];
+      double e = 0.0;
+      if (c != 0 && key >= tk)
+        e = (double)c * (double)__builtin_amdgcn_exp2f((value_of_key16(key) - m) * a);
+      gm = wave_sum(e);
+    }
+    if (lane == 0) gmass[grp] = gm;
+  }
+  __syncthreads();
+  double ztot;
+  const double suf = block_incl_suffix<NT>(gmass[tid], dslot, &ztot);
+  gsuf[tid] = suf;
+  if (tid == 0) gsuf[1024] = 0.0;
+
+  uint32_t thr_key = tk;
+  double z = ztot;
+  if (use_p) {
+    const double target = (double)top_p * ztot;
+    __syncthreads();
+    // crossing group: the largest group whose suffix mass reaches target
+    const uint32_t cand = suf >= target ? (uint32_t)tid + 1u : 0u;
+    const uint32_t gp1 = block_max_u32<NT>(cand, uslot);
+    const int gp = (int)gp1 - 1;  // >= 0 since gsuf[0] = ztot >= target
+    if (wv == 0) {
+      const uint32_t key = (uint32_t)(gp * 64 + lane);
+      const uint32_t c = c16[key];
+      double e = 0.0;
+      if (c != 0 && key >= tk)
+        e = (double)c * (double)__builtin_amdgcn_exp2f((value_of_key16(key) - m) * a);
+      const double s = gsuf[gp + 1] + wave_incl_suffix(e);
+      const uint64_t hit = __ballot(s >= target);
+      int pick;
+      if (hit) {
+        pick = 63 - __clzll((long long)hit);
+      } else {  // rounding corner: take the lowest key with mass
+        const uint64_t nz = __ballot(e > 0.0);
+        pick = nz ? (__ffsll((unsigned long long)nz) - 1) : 0;
+      }
+      const double zs = __shfl(s, pick, kWave);
+      if (lane == 0) {
+        sh_key[1] = (uint32_t)(gp * 64 + pick);
+        sh_z = zs;
+      }
+    }
+    __syncthreads();
+    thr_key = max(tk, sh_key[1]);
+    z = sh_z;
+  }
+  if (tid == 0) {
+    RowStat st;
+    st.m = m;
+    st.thr = (use_k || use_p) ? value_of_key16(thr_key) : -__builtin_inff();
+    st.z = z;
+    st.valid = 1;
+    st.pad[0] = st.pad[1] = st.pad[2] = 0;
+    stats[r] = st;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-sequence tail of the stochastic verify (one workgroup of 512 threads
+// per sequence): row statistics, ratio test at every drafted position, first
+// rejection, then the residual max(0, p - q) at the rejected position (or the
+// bonus row's p) drawn by inverse CDF in ascending vocabulary order:
+// wave-contiguous segments of the row, 8 elements per lane per step, fp64
+// running sums (wave totals -> crossing wave -> crossing step -> crossing
+// lane -> crossing element, all from the same additions).
+struct TailArgs {
+  RowMap map;
+  int64_t V;
+  int32_t k;
+  float a;
+  const int32_t* tokens;
+  const float* u;
+  RowStat* rowstat;  // filtered rows (one per row), or nullptr
+  Partial* part;     // unfiltered rows (nchunks per row), or nullptr
+  int32_t nchunks;
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+  float* accept_prob;
+};
+
+__device__ __forceinline__ double prob_at(float l, const RowStat& s, float a) {
+  if (!(l >= s.thr)) return 0.0;
+  return exp2(((double)l - (double)s.m) * (double)a) / s.z;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(512) void k_tail(TailArgs A) {
+  constexpr int NT = 512;
+  constexpr int NW = NT / kWave;
+  __shared__ RowStat st[2 * SPEC_MAX_K + 1];
+  __shared__ double wtot[NW];
+  __shared__ int32_t sh_n, sh_valid, sh_emit;
+  const int64_t b = blockIdx.x;
+  const int k = A.k;
+  const int nr = 2 * k + 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  const int64_t V = A.V;
+  const float a = A.a;
+
+  // Row statistics of this sequence; the workspace records are cleared.
+  for (int t = tid; t < nr; t += NT) {
+    const int64_t rr = b * nr + t;
+    RowStat s;
+    if (A.rowstat) {
+      s = A.rowstat[rr];
+      RowStat zero = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
+      A.rowstat[rr] = zero;
+    } else {
+      Partial* p = A.part + rr * A.nchunks;
+      s = merge_partials(p, A.nchunks, a);
+      for (int c = 0; c < A.nchunks; ++c) {
+        Partial zero = {0.f, 0u, 0.0};
+        p[c] = zero;
+      }
+    }
+    st[t] = s;
+  }
+  __syncthreads();
+
+  // Ratio test (wave 0, lane j = position j) and first rejection.
+  if (w == 0) {
+    bool ok = true;
+    for (int t = lane; t < nr; t += kWave) ok &= st[t].valid != 0;
+    int32_t x = 0;
+    if (lane < k) {
+      x = A.tokens[b * k + lane];
+      ok &= x >= 0 && (int64_t)x < V;
+    }
+    const bool all_ok = __ballot(!ok) == 0;
+    bool acc = true;
+    if (lane < k) {
+      if (all_ok) {
+        const T* tr = A.map.row<T>(b * nr + lane);
+        const T* dr = A.map.row<T>(b * nr + k + 1 + lane);
+        const double p = prob_at(Elem<T>::load1(tr + x), st[lane], a);
+        const double q = prob_at(Elem<T>::load1(dr + x), st[k + 1 + lane], a);
+        const double alpha = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
+        acc = (double)A.u[b * (k + 1) + lane] < alpha;
+        if (A.accept_prob) A.accept_prob[b * k + lane] = (float)alpha;
+      } else if (A.accept_prob) {
+        A.accept_prob[b * k + lane] = __builtin_nanf("");
+      }
+    }
+    const uint64_t rej = __ballot(lane < k && !acc);
+    if (lane == 0) {
+      sh_valid = all_ok ? 1 : 0;
+      sh_n = rej ? (__ffsll((unsigned long long)rej) - 1) : k;
+    }
+  }
+  __syncthreads();
+  int32_t* out = A.out_tokens + b * (k + 1);
+  if (!sh_valid) {
+    for (int j = tid; j <= k; j += NT) out[j] = -1;
+    if (tid == 0) A.accepted_len[b] = -1;
+    return;
+  }
+  const int n = sh_n;
+
+  // Residual max(0, p_n - q_n) (n < k) or the bonus row's p_k (n = k).
+  const T* prow = A.map.row<T>(b * nr + n);
+  const bool has_q = n < k;
+  const T* qrow = has_q ? A.map.row<T>(b * nr + k + 1 + n) : prow;
+  const RowStat sp = st[n];
+  const RowStat sq = has_q ? st[k + 1 + n] : st[n];
+  const float izp = (float)(1.0 / sp.z), izq = (float)(1.0 / sq.z);
+  bool resid = has_q;
+  const int64_t nsteps = (V + 511) / 512;
+  const int64_t spw = (nsteps + NW - 1) / NW;
+  const int64_t s0 = (int64_t)w * spw;
+  const int64_t s1 = min(nsteps, s0 + spw);
+
+  auto lane_values = [&](int64_t s, float* r8) -> double {
+    const int64_t e = s * 512 + lane * 8;
+    float lp[8], lq[8];
+    load8<T, VEC>(prow, e, V, lp);
+    if (resid) load8<T, VEC>(qrow, e, V, lq);
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = lp[i] >= sp.thr ? __builtin_amdgcn_exp2f((lp[i] - sp.m) * a) * izp : 0.0f;
+      float r = p;
+      if (resid) {
+        const float q = lq[i] >= sq.thr ? __builtin_amdgcn_exp2f((lq[i] - sq.m) * a) * izq : 0.0f;
+        r = fmaxf(p - q, 0.0f);
+      }
+      r8[i] = r;
+      acc += (double)r;
+    }
+    return acc;
+  };
+
+  double S = 0.0;
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    double wt = 0.0;
+    for (int64_t s = s0; s < s1; ++s) {
+      float r8[8];
+      const double ls = lane_values(s, r8);
+      wt += __shfl(wave_incl_scan(ls), kWave - 1, kWave);
+    }
+    if (lane == 0) wtot[w] = wt;
+    __syncthreads();
+    S = 0.0;
+    for (int v = 0; v < NW; ++v) S += wtot[v];
+    if (S > 0.0 || !resid) break;
+    resid = false;  // a residual without mass falls back to p at that position
+    __syncthreads();
+  }
+  const double target = (double)A.u[b * (k + 1) + k] * S;
+  double cum = 0.0;
+  int wstar = -1;
+  for (int v = 0; v < NW; ++v) {
+    if (cum + wtot[v] > target) {
+      wstar = v;
+      break;
+    }
+    cum += wtot[v];
+  }
+  if (wstar < 0) {  // unreachable for u < 1; take the last wave with mass
+    cum = 0.0;
+    for (int v = 0; v < NW; ++v)
+      if (wtot[v] > 0.0) wstar = v;
+    for (int v = 0; v < wstar; ++v) cum += wtot[v];
+    if (wstar < 0) wstar = 0;
+  }
+  if (w == wstar) {
+    double wt = 0.0;
+    for (int64_t s = s0; s < s1; ++s) {
+      float r8[8];
+      const double ls = lane_values(s, r8);
+      const double inc = wave_incl_scan(ls);
+      const double stot = __shfl(inc, kWave - 1, kWave);
+      if (cum + (wt + stot) > target || s == s1 - 1) {
+        const uint64_t hit = __ballot(cum + (wt + inc) > target);
+        const uint64_t pos = __ballot(ls > 0.0);
+        int L;
+        if (hit) {
+          L = __ffsll((unsigned long long)hit) - 1;
+          if (!((pos >> L) & 1ull)) {  // rounding corner: nearest lane with mass
+            const uint64_t below = pos & ((2ull << L) - 1ull);
+            L = below ? 63 - __clzll((long long)below)
+                      : (pos ? __ffsll((unsigned long long)pos) - 1 : L);
+          }
+        } else {
+          L = pos ? 63 - __clzll((long long)pos) : 0;
+        }
+        const double excl = __shfl_up(inc, 1, kWave);
+        if (lane == L) {
+          const double base = cum + (wt + (lane > 0 ? excl : 0.0));
+          double run = 0.0;
+          int pick = -1, lastpos = -1;
+          for (int i = 0; i < 8; ++i) {
+            if (r8[i] > 0.0f) lastpos = i;
+            run += (double)r8[i];
+            if (pick < 0 && base + run > target) pick = i;
+          }
+          if (pick < 0 || !(r8[pick] > 0.0f)) pick = lastpos >= 0 ? lastpos : 0;
+          sh_emit = (int32_t)(s * 512 + lane * 8 + pick);
+        }
+        break;
+      }
+      wt += stot;
+    }
+  }
+  __syncthreads();
+  const int32_t emitted = sh_emit;
+  for (int j = tid; j <= k; j += NT) {
+    int32_t v = -1;
+    if (j < n) v = A.tokens[b * k + j];
+    else if (j == n) v = emitted;
+    out[j] = v;
+  }
+  if (tid == 0) A.accepted_len[b] = n;
+}
+
+// ---------------------------------------------------------------------------
+// Logits processing: merge (unfiltered) partials or copy (filtered) stats into
+// the caller's per-row records; keep a RowStat per row for the dense pass.
+__global__ __launch_bounds__(256) void k_process_stats(int64_t R, int nchunks, float a,
+                                                       Partial* __restrict__ part,
+                                                       RowStat* __restrict__ rowstat,
+                                                       spec_row_stats_t* __restrict__ out) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  RowStat s;
+  if (part) {
+    s = merge_partials(part + r * nchunks, nchunks, a);
+    rowstat[r] = s;
+  } else {
+    s = rowstat[r];
+  }
+  if (out) {
+    spec_row_stats_t o;
+    if (s.valid) {
+      o.max_logit = s.m;
+      o.threshold = s.thr;
+      o.log_norm = (float)log(s.z);
+      o.valid = 1;
+    } else {
+      o.max_logit = o.threshold = o.log_norm = __builtin_nanf("");
+      o.valid = 0;
+    }
+    out[r] = o;
+  }
+}
+
+template <typename T, bool VEC, int VPT>
+__global__ __launch_bounds__(256) void k_probs(RowMap map, int64_t V, int nchunks, float a,
+                                               const RowStat* __restrict__ rowstat,
+                                               float* __restrict__ probs) {
+  constexpr int NT = 256;
+  const int64_t bid = blockIdx.x;
+  const int64_t r = bid / nchunks;
+  const int c = (int)(bid - r * nchunks);
+  const T* row = map.row<T>(r);
+  const RowStat s = rowstat[r];
+  const float iz = s.valid ? (float)(1.0 / s.z) : __builtin_nanf("");
+  const int64_t lo = (int64_t)c * (NT * VPT * 8);
+  const int64_t hi = min(V, lo + (int64_t)NT * VPT * 8);
+  float* dst = probs + r * V;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int64_t e = lo + ((int64_t)v * NT + threadIdx.x) * 8;
+    if (e < hi) {
+      float x[8];
+      load8<T, VEC>(row, e, hi, x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (e + i < hi) {
+          float p = x[i] >= s.thr ? __builtin_amdgcn_exp2f((x[i] - s.m) * a) * iz : 0.0f;
+          if (!s.valid) p = __builtin_nanf("");
+          dst[e + i] = p;
+        }
+      }
+    }
+  }
+}
+
+// Clears `n` 16-byte words of workspace (used where a call's records are not
+// consumed by a per-sequence tail that clears them itself).
+__global__ __launch_bounds__(256) void k_clear(uint4* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+}  // namespace sv

@@ -1,0 +1,158 @@
+/*
+ * specverify.h -- C ABI of libspecverify, the speculative-decoding verify step
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one stated in the encyclopedia entry "Speculative
+ * decoding" (glopedia, 推测解码), section "Basic steps of proposal and
+ * verification" (提议与核验的基本步骤):
+ *   - a drafted token x at position j is accepted with probability
+ *     min(1, p(x)/q(x)), where p (target) and q (proposer) are the
+ *     conditional probabilities under the sampling settings in force;
+ *   - acceptance stops at the first rejected position, which is redrawn from
+ *     the normalised positive residual max(0, p - q);
+ *   - when all k candidates pass, one extra (bonus) token is drawn from the
+ *     target's next distribution;
+ *   - greedy decoding compares each draft with the target's most probable
+ *     token and replaces the first mismatch with it;
+ *   - temperature, top-k and nucleus (top-p) settings are applied in the same
+ *     way to p and q.
+ *
+ * Conventions (readings where the entry is silent):
+ *   - target logits hold k+1 rows per sequence; row k is the bonus row;
+ *   - uniforms are [B][k+1] floats in [0,1): column j < k is position j's
+ *     accept draw (accept iff u < alpha), column k the one draw for the
+ *     corrected or bonus token;
+ *   - sampling is an inverse CDF in ascending vocabulary order (the first
+ *     index whose running sum exceeds u * S);
+ *   - alpha = 1 when q(x) = 0 < p(x) and 0 when both are 0;
+ *   - a residual without mass falls back to p at that position;
+ *   - processing order: z = (l - max l) / T, then top-k (keep every logit >=
+ *     the top_k-th largest, duplicates counted), then top-p over the top-k
+ *     probabilities (keep the shortest descending prefix whose mass reaches
+ *     top_p; ties at the cut kept); a row's kept set is {l >= threshold};
+ *   - greedy ties go to the lowest index; greedy ignores temperature/filters.
+ *
+ * Memory: every array argument is a DEVICE pointer unless marked "host".  The
+ * caller owns all buffers; the library allocates nothing on these paths and
+ * keeps no pointer after a call returns.  A call only enqueues work on
+ * `stream` (a hipStream_t, NULL = the default stream) and never synchronises;
+ * outputs are valid once the stream reaches that point.
+ *
+ * Errors: the return value reports argument validation and launch failures
+ * (spec_status_t).  Data faults are reported per sequence with
+ * accepted_len[b] = -1 and out_tokens[b][*] = -1: a draft token outside
+ * [0, V), a NaN or +inf logit, or a row without any finite logit, in any row
+ * of that sequence.  -inf logits are allowed (vocabulary masking).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad setting, misaligned data */
+  SPEC_ERR_UNSUPPORTED = 2, /* dtype or size outside the supported limits */
+  SPEC_ERR_WORKSPACE = 3,   /* workspace missing, too small or misaligned */
+  SPEC_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} spec_status_t;
+
+typedef enum { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype_t;
+
+/* Limits: 1 <= k <= SPEC_MAX_K, 1 <= V <= SPEC_MAX_V, 1 <= B <= 2^24. */
+#define SPEC_MAX_K 64
+#define SPEC_MAX_V (1 << 24)
+
+/* A logits tensor in device memory.  Element (b, j, x) lives at
+ *   data[b * seq_stride + j * pos_stride + x]   (strides in elements).
+ * seq_stride 0 broadcasts one sequence to all B; pos_stride >= V.  data must
+ * be aligned to its element size; 16-byte aligned rows take the vector path. */
+typedef struct {
+  const void* data;
+  int32_t dtype; /* spec_dtype_t */
+  int32_t reserved;
+  int64_t seq_stride;
+  int64_t pos_stride;
+} spec_logits_t;
+
+/* Sampling settings (host struct), applied identically to target and draft. */
+typedef struct {
+  float temperature; /* finite, > 0 (greedy ignores it) */
+  int32_t top_k;     /* 0 = off, else keep the top_k largest (>= V is off) */
+  float top_p;       /* 1.0 = off, else in (0, 1) */
+} spec_sampling_t;
+
+/* Per-row result of spec_logits_process:
+ *   p(x) = (l_x >= threshold) ? exp((l_x - max_logit) / T - log_norm) : 0.
+ * valid = 0 marks a row with NaN/+inf or no finite logit (other fields NaN). */
+typedef struct {
+  float max_logit;
+  float threshold; /* -inf when no filter is active */
+  float log_norm;
+  int32_t valid;
+} spec_row_stats_t;
+
+typedef enum {
+  SPEC_OP_STOCHASTIC = 0,
+  SPEC_OP_GREEDY = 1,
+  SPEC_OP_PROCESS = 2
+} spec_op_t;
+
+/* Bytes of device workspace the given call needs (0 for invalid arguments).
+ * For SPEC_OP_PROCESS, B is the row count R and k is ignored.  The
+ * workspace must be zero-filled before its first use with this library and
+ * left untouched by the caller between calls; every call leaves it
+ * zero-filled when it completes.  Calls that share one workspace must be
+ * ordered on one stream. */
+size_t spec_workspace_size(int32_t op, int32_t B, int32_t k, int32_t V,
+                           const spec_sampling_t* sampling /* host */);
+
+/* Stochastic verify of B sequences with k drafted positions each.
+ *   target        [B][k+1][V] logits (row k = bonus row)
+ *   draft         [B][k][V] logits, same dtype as target
+ *   draft_tokens  [B][k] int32, drawn by the proposer from the processed q
+ *   uniforms      [B][k+1] float in [0,1)
+ *   sampling      host struct, applied to both target and draft
+ *   accepted_len  [B] int32 out: n = accepted draft count, or -1
+ *   out_tokens    [B][k+1] int32 out: drafts 0..n-1, then the corrected (n<k)
+ *                 or bonus (n=k) token, then -1 padding
+ *   accept_prob   [B][k] float out or NULL: alpha_j for every j < k (also past
+ *                 the first rejection); NaN for an invalid sequence
+ *   workspace     device scratch of spec_workspace_size(SPEC_OP_STOCHASTIC...)
+ *                 bytes, 256-byte aligned (see spec_workspace_size). */
+int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft,
+                           const int32_t* draft_tokens, const float* uniforms,
+                           int32_t B, int32_t k, int32_t V,
+                           const spec_sampling_t* sampling,
+                           int32_t* accepted_len, int32_t* out_tokens,
+                           float* accept_prob, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Greedy verify: a*_j = argmax_x target[b][j][x] (lowest index on ties);
+ * n = first j < k with draft_tokens[b][j] != a*_j, else k; out_tokens gets
+ * the n matching drafts, then a*_n, then -1 padding. */
+int spec_verify_greedy(spec_logits_t target, const int32_t* draft_tokens,
+                       int32_t B, int32_t k, int32_t V, int32_t* accepted_len,
+                       int32_t* out_tokens, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Logits processing of R rows (row r at data + r * pos_stride; seq_stride is
+ * ignored): per-row statistics and, if probs != NULL, the dense fp32
+ * probabilities [R][V] (row-major, stride V).  Either output may be NULL. */
+int spec_logits_process(spec_logits_t logits, int32_t R, int32_t V,
+                        const spec_sampling_t* sampling,
+                        spec_row_stats_t* row_stats, float* probs,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* spec_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECVERIFY_H */
