@@ -94,54 +94,107 @@ __device__ __forceinline__ float value_of_key16(uint32_t k) {
 }
 
 // ---------------------------------------------------------------------------
-// Wave-level reductions and scans (wave64).
-template <typename F>
-__device__ __forceinline__ F wave_sum(F x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
-  return x;
+// Wave-level scans and reductions (wave64) built from DPP row shifts inside
+// each 16-lane row and v_readlane fix-ups across the four rows: no LDS
+// round-trips, so serial chains of them stay cheap.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x, uint32_t fill) {
+  // lanes whose source lies outside their row receive `fill`
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)x, CTRL, 0xF, 0xF, false);
 }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x, float fill) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(x), __float_as_uint(fill)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x, double fill) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x), f = (uint64_t)__double_as_longlong(fill);
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)b, (uint32_t)f);
+  const uint32_t hi = dpp_u32<CTRL>((uint32_t)(b >> 32), (uint32_t)(f >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <int CTRL>
+struct Dpp {
+  __device__ static __forceinline__ uint32_t mov(uint32_t x, uint32_t f) { return dpp_u32<CTRL>(x, f); }
+  __device__ static __forceinline__ float mov(float x, float f) { return dpp_f32<CTRL>(x, f); }
+  __device__ static __forceinline__ double mov(double x, double f) { return dpp_f64<CTRL>(x, f); }
+};
+
+// Uniform-lane broadcast (the lane index must be wave-uniform).
+__device__ __forceinline__ uint32_t bcast(uint32_t x, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
+}
+__device__ __forceinline__ float bcast(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ double bcast(double x, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+struct OpAdd {
+  template <typename F>
+  __device__ __forceinline__ F operator()(F a, F b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+  __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); }
+};
+struct OpMin {
+  __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); }
+};
+struct OpOr {
+  __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; }
+};
+
+// Inclusive prefix scan: lane i gets op(x_0, ..., x_i).
+template <typename F, typename Op>
+__device__ __forceinline__ F wave_prefix(F x, F id, Op op) {
+  x = op(x, Dpp<0x111>::mov(x, id));  // row_shr:1
+  x = op(x, Dpp<0x112>::mov(x, id));  // row_shr:2
+  x = op(x, Dpp<0x114>::mov(x, id));  // row_shr:4
+  x = op(x, Dpp<0x118>::mov(x, id));  // row_shr:8
+  const F t0 = bcast(x, 15), t1 = bcast(x, 31), t2 = bcast(x, 47);
+  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  const F t01 = op(t0, t1);
+  const F t012 = op(t01, t2);
+  const F add = row == 0 ? id : (row == 1 ? t0 : (row == 2 ? t01 : t012));
+  return row == 0 ? x : op(add, x);
+}
+// Inclusive suffix scan: lane i gets op(x_i, ..., x_63).
+template <typename F, typename Op>
+__device__ __forceinline__ F wave_suffix(F x, F id, Op op) {
+  x = op(x, Dpp<0x101>::mov(x, id));  // row_shl:1
+  x = op(x, Dpp<0x102>::mov(x, id));  // row_shl:2
+  x = op(x, Dpp<0x104>::mov(x, id));  // row_shl:4
+  x = op(x, Dpp<0x108>::mov(x, id));  // row_shl:8
+  const F t1 = bcast(x, 16), t2 = bcast(x, 32), t3 = bcast(x, 48);
+  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  const F t23 = op(t2, t3);
+  const F t123 = op(t1, t23);
+  const F add = row == 3 ? id : (row == 2 ? t3 : (row == 1 ? t23 : t123));
+  return row == 3 ? x : op(x, add);
+}
+
+template <typename F>
+__device__ __forceinline__ F wave_incl_scan(F x) { return wave_prefix(x, F(0), OpAdd()); }
+template <typename F>
+__device__ __forceinline__ F wave_incl_suffix(F x) { return wave_suffix(x, F(0), OpAdd()); }
+template <typename F>
+__device__ __forceinline__ F wave_sum(F x) { return bcast(wave_prefix(x, F(0), OpAdd()), kWave - 1); }
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
-  return x;
+  return bcast(wave_prefix(x, -__builtin_inff(), OpMax()), kWave - 1);
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o, kWave));
-  return x;
+  return bcast(wave_prefix(x, 0u, OpMax()), kWave - 1);
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o, kWave));
-  return x;
+  return bcast(wave_prefix(x, 0xFFFFFFFFu, OpMin()), kWave - 1);
 }
 __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x |= (uint32_t)__shfl_xor((int)x, o, kWave);
-  return x;
-}
-// Inclusive prefix scan (lane i gets x_0 + ... + x_i).
-template <typename F>
-__device__ __forceinline__ F wave_incl_scan(F x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    F y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-// Inclusive suffix scan (lane i gets x_i + ... + x_63).
-template <typename F>
-__device__ __forceinline__ F wave_incl_suffix(F x) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    F y = __shfl_down(x, o, kWave);
-    if (lane + o < kWave) x += y;
-  }
-  return x;
+  return bcast(wave_prefix(x, 0u, OpOr()), kWave - 1);
 }
 
 // ---------------------------------------------------------------------------

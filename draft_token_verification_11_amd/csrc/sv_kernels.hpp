@@ -372,63 +372,62 @@ __global__ __launch_bounds__(1024) void k_filter_bisect(RowMap map, int64_t V, f
 // ---------------------------------------------------------------------------
 // Filtered bf16 rows: an exact 65536-bin count histogram of the 16-bit order
 // keys in LDS (two 16-bit counters per 32-bit word).  Equal bf16 values have
-// equal probabilities, so counts give the row's sorted value distribution
+// equal probabilities, so the counts give the row's sorted value distribution
 // exactly: the max, the top-k threshold (by counts), the per-value masses
 // count * 2^((v - m) a), the top-p cut (by masses) and the normaliser all come
 // from the histogram after one streaming pass, with no per-element exp.
 // Overflow (>= 65536 equal values) is detected by the count total and falls
 // back to the bisection path.
-template <bool VEC>
-__global__ __launch_bounds__(1024) void k_filter_bf16_hist(RowMap map, int64_t V, float a,
-                                                           int top_k, float top_p,
-                                                           RowStat* __restrict__ stats) {
-  constexpr int NT = 1024;
-  __shared__ uint32_t hist[32768];
-  __shared__ uint32_t gcnt[1024];
-  __shared__ double gmass[1024];
-  __shared__ double gsuf[1025];
-  __shared__ double dslot[16];
-  __shared__ uint32_t uslot[16];
-  __shared__ uint32_t sh_key[2];
-  __shared__ double sh_z;
-  const int64_t r = blockIdx.x;
-  const uint16_t* row = map.row<uint16_t>(r);
-  const int tid = threadIdx.x;
+struct HistScratch {
+  uint32_t gcnt[1024];   // count of group g (keys 64 g .. 64 g + 63)
+  uint16_t list[1024];   // non-empty groups, descending key order
+  double gmass[1024];    // mass of list entry i over keys >= the top-k key
+  uint32_t wcount[16];
+  double dslot[16];
+  uint32_t uslot[16];
+  uint32_t n_list, max_key, tk, tk_entry, tp;
+  int32_t state;         // 0 ok, 1 invalid row
+  double z;
+};
 
-  // 1. clear
+__device__ __forceinline__ void hist_clear(uint32_t* hist) {
   uint4* h4 = reinterpret_cast<uint4*>(hist);
-  for (int i = tid; i < 8192; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
-  __syncthreads();
+  for (int i = threadIdx.x; i < 8192; i += 1024) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+}
 
-  // 2. count: one atomic increment of a 16-bit counter per element
-  const int64_t ngroups = (V + 7) / 8;
-  auto count8 = [&](uint4 v) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ void hist_add8(uint32_t* hist, uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t k0 = key16_of_bits(w[i] & 0xFFFFu);
-      const uint32_t k1 = key16_of_bits(w[i] >> 16);
-      atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
-      atomicAdd(&hist[k1 >> 1], (k1 & 1u) ? 0x10000u : 1u);
-    }
-  };
-  int64_t g = tid;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t k0 = key16_of_bits(w[i] & 0xFFFFu);
+    const uint32_t k1 = key16_of_bits(w[i] >> 16);
+    atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
+    atomicAdd(&hist[k1 >> 1], (k1 & 1u) ? 0x10000u : 1u);
+  }
+}
+
+// Streams one bf16 row into the (cleared) histogram.
+template <bool VEC>
+__device__ __forceinline__ void hist_count_row(uint32_t* hist, const uint16_t* row, int64_t V) {
+  constexpr int NT = 1024;
+  const int64_t ngroups = (V + 7) / 8;
+  int64_t g = threadIdx.x;
   if (VEC) {
-    for (; g + 3 * NT < ngroups && (g + 3 * NT + 1) * 8 <= V; g += 4 * NT) {
+    for (; (g + 3 * NT + 1) * 8 <= V; g += 4 * NT) {
       const uint4 v0 = load16(row + g * 8);
       const uint4 v1 = load16(row + (g + NT) * 8);
       const uint4 v2 = load16(row + (g + 2 * NT) * 8);
       const uint4 v3 = load16(row + (g + 3 * NT) * 8);
-      count8(v0);
-      count8(v1);
-      count8(v2);
-      count8(v3);
+      hist_add8(hist, v0);
+      hist_add8(hist, v1);
+      hist_add8(hist, v2);
+      hist_add8(hist, v3);
     }
   }
   for (; g < ngroups; g += NT) {
     const int64_t e = g * 8;
     if (VEC && e + 8 <= V) {
-      count8(load16(row + e));
+      hist_add8(hist, load16(row + e));
     } else {
       for (int i = 0; i < 8 && e + i < V; ++i) {
         const uint32_t k0 = key16_of_bits(row[e + i]);
@@ -436,9 +435,27 @@ __global__ __launch_bounds__(1024) void k_filter_bf16_hist(RowMap map, int64_t V
       }
     }
   }
-  __syncthreads();
+}
 
-  // 3. -0 and +0 are one value: move the count of key 0x7FFF (-0) to 0x8000.
+// Mass of key `key` (count c) relative to the max logit m.
+__device__ __forceinline__ double key_mass(uint32_t key, uint32_t c, float m, float a) {
+  return c ? (double)c * (double)__builtin_amdgcn_exp2f((value_of_key16(key) - m) * a) : 0.0;
+}
+
+// Row statistics from a filled histogram (all 1024 threads).  Returns 0 on
+// success (RowStat written), 1 for an invalid row (written), 2 on counter
+// overflow (nothing written: the caller takes the bisection path).
+__device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a, int top_k,
+                              float top_p, RowStat* out) {
+  constexpr int NT = 1024;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const uint16_t* c16 = reinterpret_cast<const uint16_t*>(hist);
+  const bool use_k = top_k > 0 && (int64_t)top_k < V;
+  const bool use_p = top_p < 1.0f;
+
+  // -0 and +0 are one value: move the count of key 0x7FFF (-0) to 0x8000.
   if (tid == 0) {
     const uint32_t w = hist[0x3FFF];
     hist[0x3FFF] = w & 0xFFFFu;
@@ -446,127 +463,176 @@ __global__ __launch_bounds__(1024) void k_filter_bf16_hist(RowMap map, int64_t V
   }
   __syncthreads();
 
-  // 4. per 64-key group: count, bad keys, highest finite key
-  uint32_t cnt = 0, badc = 0, mk = 0;
-  {
-    const int grp = tid;
-#pragma unroll 4
-    for (int j = 0; j < 32; ++j) {
-      const int wi = grp * 32 + ((j + grp) & 31);
-      const uint32_t w = hist[wi];
-      const uint32_t c0 = w & 0xFFFFu, c1 = w >> 16;
-      const uint32_t k0 = (uint32_t)wi * 2u, k1 = k0 + 1u;
-      cnt += c0 + c1;
-      const bool b0 = k0 < 0x7Fu || k0 >= 0xFF80u, b1 = k1 < 0x7Fu || k1 >= 0xFF80u;
-      badc |= (b0 && c0) || (b1 && c1);
-      if (c0 && !b0 && k0 > 0x7Fu) mk = max(mk, k0);
-      if (c1 && !b1 && k1 > 0x7Fu) mk = max(mk, k1);
-    }
-    gcnt[grp] = cnt;
+  // S1: thread t counts group t (8 rotated 16-byte LDS reads).
+  const uint4* h4 = reinterpret_cast<const uint4*>(hist);
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4 w = h4[tid * 8 + ((j + tid) & 7)];
+    cnt += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) + (w.z & 0xFFFFu) +
+           (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
   }
-  const uint32_t total = block_sum<NT>(cnt, uslot);
-  badc = block_or<NT>(badc, uslot);
-  mk = block_max_u32<NT>(mk, uslot);
-  if (badc || mk == 0) {
+  S.gcnt[tid] = cnt;
+  // keys < 0x7F are negative NaNs, keys >= 0xFF80 are +inf and positive NaNs
+  uint32_t bad = (tid == 0 || tid >= 1022) ? cnt : 0u;
+  if (tid == 1) bad = cnt - c16[0x7F];
+  const uint32_t total = block_sum<NT>(cnt, S.uslot);
+  bad = block_or<NT>(bad, S.uslot);
+  if (bad) {
     if (tid == 0) {
       RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
-      stats[r] = st;
+      *out = st;
     }
-    return;
+    return 1;
   }
-  if ((int64_t)total != V) {  // a 16-bit counter overflowed
-    __syncthreads();
-    filter_row_bisect<uint16_t, VEC, NT>(row, V, a, top_k, top_p, stats + r, dslot, uslot);
-    return;
-  }
-  const float m = value_of_key16(mk);
-  const uint16_t* c16 = reinterpret_cast<const uint16_t*>(hist);
-  const bool use_k = top_k > 0 && (int64_t)top_k < V;
-  const bool use_p = top_p < 1.0f;
+  if ((int64_t)total != V) return 2;
 
-  // 5. top-k threshold key: the largest key whose suffix count reaches top_k
-  uint32_t tk = 0;
-  if (use_k) {
-    uint32_t tot;
-    const uint32_t suf = block_incl_suffix<NT>(cnt, uslot, &tot);
-    if (suf >= (uint32_t)top_k && suf - cnt < (uint32_t)top_k) {
-      uint32_t run = suf - cnt;
-      for (int i = 63; i >= 0; --i) {
-        run += c16[tid * 64 + i];
-        if (run >= (uint32_t)top_k) {
-          sh_key[0] = (uint32_t)(tid * 64 + i);
-          break;
-        }
-      }
-    }
+  // S2: non-empty groups in descending key order (thread t looks at group 1023 - t).
+  {
+    const int g = 1023 - tid;
+    const bool ne = S.gcnt[g] != 0;
+    const uint64_t bal = __ballot(ne);
+    const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) S.wcount[wv] = (uint32_t)__popcll(bal);
     __syncthreads();
-    tk = sh_key[0];
-  }
-
-  // 6. per-group masses over keys >= tk: sum of count * 2^((v - m) a)
-  const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
-  for (int gi = 0; gi < 64; ++gi) {
-    const int grp = wv * 64 + gi;
-    double gm = 0.0;
-    if (gcnt[grp] != 0 && (uint32_t)(grp * 64 + 63) >= tk) {
-      const uint32_t key = (uint32_t)(grp * 64 + lane);
-      const uint32_t c = c16[key];
-      double e = 0.0;
-      if (c != 0 && key >= tk)
-        e = (double)c * (double)__builtin_amdgcn_exp2f((value_of_key16(key) - m) * a);
-      gm = wave_sum(e);
+    uint32_t off = 0;
+    for (int v = 0; v < wv; ++v) off += S.wcount[v];
+    if (ne) S.list[off + before] = (uint16_t)g;
+    if (tid == NT - 1) {
+      uint32_t n = 0;
+      for (int v = 0; v < 16; ++v) n += S.wcount[v];
+      S.n_list = n;
     }
-    if (lane == 0) gmass[grp] = gm;
   }
   __syncthreads();
-  double ztot;
-  const double suf = block_incl_suffix<NT>(gmass[tid], dslot, &ztot);
-  gsuf[tid] = suf;
-  if (tid == 0) gsuf[1024] = 0.0;
+  const uint32_t nl = S.n_list;
 
-  uint32_t thr_key = tk;
-  double z = ztot;
-  if (use_p) {
-    const double target = (double)top_p * ztot;
-    __syncthreads();
-    // crossing group: the largest group whose suffix mass reaches target
-    const uint32_t cand = suf >= target ? (uint32_t)tid + 1u : 0u;
-    const uint32_t gp1 = block_max_u32<NT>(cand, uslot);
-    const int gp = (int)gp1 - 1;  // >= 0 since gsuf[0] = ztot >= target
-    if (wv == 0) {
-      const uint32_t key = (uint32_t)(gp * 64 + lane);
-      const uint32_t c = c16[key];
-      double e = 0.0;
-      if (c != 0 && key >= tk)
-        e = (double)c * (double)__builtin_amdgcn_exp2f((value_of_key16(key) - m) * a);
-      const double s = gsuf[gp + 1] + wave_incl_suffix(e);
-      const uint64_t hit = __ballot(s >= target);
-      int pick;
-      if (hit) {
-        pick = 63 - __clzll((long long)hit);
-      } else {  // rounding corner: take the lowest key with mass
-        const uint64_t nz = __ballot(e > 0.0);
-        pick = nz ? (__ffsll((unsigned long long)nz) - 1) : 0;
-      }
-      const double zs = __shfl(s, pick, kWave);
-      if (lane == 0) {
-        sh_key[1] = (uint32_t)(gp * 64 + pick);
-        sh_z = zs;
+  // Wave 0: max finite key, then the top-k key by exact counts.
+  if (wv == 0) {
+    const uint32_t g0 = S.list[0];
+    const uint32_t key = g0 * 64 + lane;
+    const uint64_t nz = __ballot(c16[key] != 0 && key > 0x7Fu);
+    if (lane == 0) {
+      S.state = nz ? 0 : 1;  // only -inf in the row
+      S.max_key = nz ? g0 * 64 + (63 - __clzll((long long)nz)) : 0u;
+      S.tk = 0;
+      S.tk_entry = nl - 1;
+    }
+    if (use_k && nz) {
+      uint32_t carry = 0;
+      for (uint32_t base = 0; base < nl; base += kWave) {
+        const uint32_t x = (base + lane < nl) ? S.gcnt[S.list[base + lane]] : 0u;
+        const uint32_t inc = wave_incl_scan(x) + carry;
+        const uint64_t hit = __ballot(base + lane < nl && inc >= (uint32_t)top_k);
+        if (hit) {
+          const int L = __ffsll((unsigned long long)hit) - 1;
+          const uint32_t before = bcast(inc - x, L);
+          const uint32_t g = S.list[base + L];
+          // within the group: suffix counts over keys, descending
+          const uint32_t c = c16[g * 64 + lane];
+          const uint32_t suf = wave_incl_suffix(c) + before;
+          const uint64_t ok = __ballot(suf >= (uint32_t)top_k);
+          if (lane == 0) {
+            S.tk = g * 64 + (63 - __clzll((long long)ok));
+            S.tk_entry = base + L;
+          }
+          break;
+        }
+        carry = bcast(inc, kWave - 1);
       }
     }
-    __syncthreads();
-    thr_key = max(tk, sh_key[1]);
-    z = sh_z;
   }
-  if (tid == 0) {
-    RowStat st;
-    st.m = m;
-    st.thr = (use_k || use_p) ? value_of_key16(thr_key) : -__builtin_inff();
-    st.z = z;
-    st.valid = 1;
-    st.pad[0] = st.pad[1] = st.pad[2] = 0;
-    stats[r] = st;
+  __syncthreads();
+  if (S.state) {
+    if (tid == 0) {
+      RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
+      *out = st;
+    }
+    return 1;
+  }
+  const float m = value_of_key16(S.max_key);
+  const uint32_t tk = S.tk;
+  const uint32_t last = S.tk_entry;  // entries after it lie below the top-k key
+
+  // S3: masses of the list entries (one wave per entry, lane = key).
+  for (uint32_t i = wv; i < nl; i += 16) {
+    double s = 0.0;
+    if (i <= last) {
+      const uint32_t key = (uint32_t)S.list[i] * 64 + lane;
+      const double e = key >= tk ? key_mass(key, c16[key], m, a) : 0.0;
+      s = wave_sum(e);
+    }
+    if (lane == 0) S.gmass[i] = s;
+  }
+  __syncthreads();
+
+  // S4 (wave 0): cumulative mass from the top; normaliser and top-p cut.
+  if (wv == 0) {
+    double carry = 0.0;
+    for (uint32_t base = 0; base < nl; base += kWave) {
+      const double x = (base + lane < nl) ? S.gmass[base + lane] : 0.0;
+      carry = bcast(wave_incl_scan(x) + carry, kWave - 1);
+    }
+    const double zk = carry;
+    uint32_t thr_key = tk;
+    double z = zk;
+    if (use_p) {
+      const double target = (double)top_p * zk;
+      double c2 = 0.0;
+      for (uint32_t base = 0; base < nl; base += kWave) {
+        const double x = (base + lane < nl) ? S.gmass[base + lane] : 0.0;
+        const double inc = wave_incl_scan(x) + c2;
+        const uint64_t hit = __ballot(base + lane < nl && inc >= target);
+        if (hit || base + kWave >= nl) {
+          int L = hit ? __ffsll((unsigned long long)hit) - 1 : (int)(nl - 1 - base);
+          const double before = bcast(inc - x, L);
+          const uint32_t g = S.list[base + L];
+          const uint32_t key = g * 64 + lane;
+          const double e = key >= tk ? key_mass(key, c16[key], m, a) : 0.0;
+          const double suf = wave_incl_suffix(e) + before;
+          const uint64_t ok = __ballot(suf >= target);
+          int pick;
+          if (ok) {
+            pick = 63 - __clzll((long long)ok);
+          } else {  // rounding corner: the lowest key with mass in the group
+            const uint64_t nzm = __ballot(e > 0.0);
+            pick = nzm ? __ffsll((unsigned long long)nzm) - 1 : 0;
+          }
+          thr_key = max(tk, g * 64 + (uint32_t)pick);
+          z = bcast(suf, pick);
+          break;
+        }
+        c2 = bcast(inc, kWave - 1);
+      }
+    }
+    if (lane == 0) {
+      RowStat st;
+      st.m = m;
+      st.thr = (use_k || use_p) ? value_of_key16(thr_key) : -__builtin_inff();
+      st.z = z;
+      st.valid = 1;
+      st.pad[0] = st.pad[1] = st.pad[2] = 0;
+      *out = st;
+    }
+  }
+  return 0;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(1024) void k_filter_bf16_hist(RowMap map, int64_t V, float a,
+                                                           int top_k, float top_p,
+                                                           RowStat* __restrict__ stats) {
+  __shared__ uint32_t hist[32768];
+  __shared__ HistScratch S;
+  const int64_t r = blockIdx.x;
+  const uint16_t* row = map.row<uint16_t>(r);
+  hist_clear(hist);
+  __syncthreads();
+  hist_count_row<VEC>(hist, row, V);
+  __syncthreads();
+  if (hist_row_stats(hist, S, V, a, top_k, top_p, stats + r) == 2) {
+    __syncthreads();
+    filter_row_bisect<uint16_t, VEC, 1024>(row, V, a, top_k, top_p, stats + r, S.dslot, S.uslot);
   }
 }
 
@@ -712,7 +778,7 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
     for (int64_t s = s0; s < s1; ++s) {
       float r8[8];
       const double ls = lane_values(s, r8);
-      wt += __shfl(wave_incl_scan(ls), kWave - 1, kWave);
+      wt += bcast(wave_incl_scan(ls), kWave - 1);
     }
     if (lane == 0) wtot[w] = wt;
     __syncthreads();
@@ -745,7 +811,7 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
       float r8[8];
       const double ls = lane_values(s, r8);
       const double inc = wave_incl_scan(ls);
-      const double stot = __shfl(inc, kWave - 1, kWave);
+      const double stot = bcast(inc, kWave - 1);
       if (cum + (wt + stot) > target || s == s1 - 1) {
         const uint64_t hit = __ballot(cum + (wt + inc) > target);
         const uint64_t pos = __ballot(ls > 0.0);
@@ -760,9 +826,9 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
         } else {
           L = pos ? 63 - __clzll((long long)pos) : 0;
         }
-        const double excl = __shfl_up(inc, 1, kWave);
+        const double excl = L > 0 ? bcast(inc, L - 1) : 0.0;
         if (lane == L) {
-          const double base = cum + (wt + (lane > 0 ? excl : 0.0));
+          const double base = cum + (wt + excl);
           double run = 0.0;
           int pick = -1, lastpos = -1;
           for (int i = 0; i < 8; ++i) {
