@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="0 = min(16, host cores)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--print-source-hash", action="store_true")
     return ap.parse_args()
 
 
@@ -47,7 +50,7 @@ def draft_tokens_on_gpu(sv, torch, draft, draft_u, T, top_k, top_p, chunk_rows=5
     library's logits_process gives q, an inverse CDF (torch cumsum +
     searchsorted) with the seeded uniforms picks the token."""
     B, k, V = draft.shape
-    rows = draft.reshape(B * k, V)
+    rows = draft.contiguous().reshape(B * k, V)
     u = torch.from_numpy(draft_u.reshape(-1)).to(draft.device, torch.float64)
     out = torch.empty(B * k, dtype=torch.int64, device=draft.device)
     for lo in range(0, B * k, chunk_rows):
@@ -59,6 +62,54 @@ def draft_tokens_on_gpu(sv, torch, draft, draft_u, T, top_k, top_p, chunk_rows=5
         out[lo:hi] = idx.clamp_(max=V - 1)
         del q, c
     return out.view(B, k).to(torch.int32)
+
+
+KERNEL_SOURCES = ["draft_token_verification_11_amd/csrc/sv_kernels.hpp",
+                  "draft_token_verification_11_amd/csrc/sv_device.hpp",
+                  "draft_token_verification_11_amd/csrc/sv_abi.hip"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg, kernel):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of
+    known size), or None when no summary exists for this workload or the
+    kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_workload%d.md" % cfg)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device copy of a known size (1 GiB read + 1 GiB written), for
+    scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    x = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 copies of %d bytes" % n)
 
 
 def cpu_baseline(cfg, budget_s, threads):
@@ -102,6 +153,12 @@ def cpu_baseline(cfg, budget_s, threads):
 
 def main():
     args = parse()
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -127,15 +184,21 @@ def main():
 
     sets = []
     for s in range(nsets):
-        # set s holds sequences s*B .. s*B+B-1 of the same seeded recipe
+        # set s holds sequences s*B .. s*B+B-1 of the same seeded recipe, in one
+        # [B][2k+1][V] tensor: rows 0..k the target, rows k+1..2k the draft
         t0 = time.perf_counter()
         w = workloads.generate(cfg, seqs=np.arange(s * c.B, (s + 1) * c.B), threads=host_threads)
-        tgt, drf, uni = up(w.target), up(w.draft), torch.from_numpy(w.uniforms).to(dev)
+        tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        big = torch.empty((c.B, 2 * c.k + 1, c.V), dtype=tdt, device=dev)
+        big[:, : c.k + 1] = up(w.target)
+        big[:, c.k + 1:] = up(w.draft)
+        uni = torch.from_numpy(w.uniforms).to(dev)
         draft_u = w.draft_u
         del w
+        tgt, drf = big[:, : c.k + 1], big[:, c.k + 1:]
         toks = draft_tokens_on_gpu(sv, torch, drf, draft_u, c.temperature, c.top_k, c.top_p)
         torch.cuda.synchronize()
-        sets.append((tgt, drf, uni, toks))
+        sets.append((tgt, drf, uni, toks, big))
         log("  set %d ready in %.1f s" % (s, time.perf_counter() - t0))
 
     ws = torch.zeros(sv.workspace_size(sv.SPEC_OP_STOCHASTIC, c.B, c.k, c.V, c.temperature,
@@ -145,7 +208,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(i):
-        tgt, drf, uni, toks = sets[i % len(sets)]
+        tgt, drf, uni, toks, _ = sets[i % len(sets)]
         sv.verify_stochastic(tgt, drf, toks, uni, temperature=c.temperature, top_k=c.top_k,
                              top_p=c.top_p, out=(acc, out, None), workspace=ws, stream=stream)
 
@@ -175,13 +238,42 @@ def main():
     positions = c.B * c.k
     value = positions / (ms / 1e3)
 
+    # The dominant kernel -- the per-row statistics pass over every target
+    # and draft row -- timed alone: the same kernel on the same rows, launched
+    # through spec_logits_process (statistics only, no dense output).
+    proc_ws = torch.zeros(sv.workspace_size(sv.SPEC_OP_PROCESS, c.B * (2 * c.k + 1), 0, c.V,
+                                            c.temperature, c.top_k, c.top_p),
+                          dtype=torch.uint8, device=dev)
+
+    def row_pass(i):
+        big = sets[i % len(sets)][4]
+        sv.logits_process(big.view(-1, c.V), temperature=c.temperature, top_k=c.top_k,
+                          top_p=c.top_p, return_probs=False, workspace=proc_ws, stream=stream)
+
+    for i in range(args.warmup):
+        row_pass(i)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        row_pass(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_rows = ev0.elapsed_time(ev1) / args.steps
+
     a1_bytes = c.B * (2 * c.k + 1) * c.V * esize
     a8_bytes = np.mean([resid_rows[i % len(sets)] for i in range(args.steps)]) * c.V * esize
     alg_bytes = a1_bytes + a8_bytes
-    achieved = alg_bytes / (ms / 1e3) / 1e9
-    log("ms/step %.4f (wall %.4f), positions/s %.4g, algorithmic GB/s %.1f (%.1f%% of %g), "
-        "mean accepted %.3f" % (ms, wall * 1e3 / args.steps, value, achieved,
-                                100 * achieved / PEAK_HBM_GBPS, PEAK_HBM_GBPS, mean_acc))
+    achieved_call = alg_bytes / (ms / 1e3) / 1e9
+    achieved = a1_bytes / (ms_rows / 1e3) / 1e9
+    kernel = ("k_filter_bf16_persistent (exact bf16 key histogram, top-k/top-p)"
+              if c.dtype == "bf16" and (c.top_k or c.top_p < 1.0) else
+              "k_filter_bisect (fp32 top-k/top-p)" if (c.top_k or c.top_p < 1.0) else
+              "k_row_partials (split-V max / sum of exponentials)")
+    traffic = measured_traffic(cfg, kernel)
+    log("ms/step %.4f (wall %.4f), positions/s %.4g, whole call %.1f GB/s (%.1f%% of %g); "
+        "row pass alone %.4f ms = %.1f GB/s (%.1f%%); mean accepted %.3f"
+        % (ms, wall * 1e3 / args.steps, value, achieved_call, 100 * achieved_call / PEAK_HBM_GBPS,
+           PEAK_HBM_GBPS, ms_rows, achieved, 100 * achieved / PEAK_HBM_GBPS, mean_acc))
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -206,9 +298,11 @@ def main():
                    "temperature": c.temperature, "top_k": c.top_k, "top_p": c.top_p,
                    "input_sets": len(sets), "mean_accepted": mean_acc},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
-                     "kernel": "whole spec_verify_stochastic call",
-                     "algorithmic_bytes": alg_bytes},
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "kernel": kernel, "kernel_ms": ms_rows,
+                     "algorithmic_bytes_per_launch": a1_bytes,
+                     "whole_call": {"achieved": achieved_call, "frac": achieved_call / PEAK_HBM_GBPS,
+                                    "algorithmic_bytes": alg_bytes}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -106,6 +106,22 @@ bool grid_fits(int64_t blocks, int threads) { return blocks >= 1 && blocks * thr
 
 float log2e_over(float T) { return float(1.4426950408889634 / double(T)); }
 
+// Workgroups of the persistent filter: one per CU, a multiple of 8 (one
+// range of rows per XCD), no more than needed.
+int persistent_grid(int64_t rows) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  int64_t g = cus;
+  if (rows < g) g = rows;
+  g = (g + 7) / 8 * 8;
+  return int(g);
+}
+
+constexpr int kPrefetch = 4;  // 16-byte vectors per thread prefetched for the next row
+
 template <typename T, bool VEC>
 void launch_partials(const Layout& L, const sv::RowMap& map, int64_t V, float a, sv::Partial* part,
                      hipStream_t st) {
@@ -147,8 +163,14 @@ void launch_filter(const Layout& L, const sv::RowMap& map, int64_t V, float a,
                    const spec_sampling_t& s, sv::RowStat* rs, hipStream_t st) {
   const dim3 grid(unsigned(L.rows)), block(kFilterThreads);
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((sv::k_filter_bf16_hist<VEC>), grid, block, 0, st, map, V, a, s.top_k,
-                       s.top_p, rs);
+    if (VEC) {
+      sv::FilterArgs F{map, V, L.rows, a, s.top_k, s.top_p, rs};
+      hipLaunchKernelGGL((sv::k_filter_bf16_persistent<true, kPrefetch>),
+                         dim3(persistent_grid(L.rows)), block, 0, st, F);
+    } else {
+      hipLaunchKernelGGL((sv::k_filter_bf16_hist<VEC>), grid, block, 0, st, map, V, a, s.top_k,
+                         s.top_p, rs);
+    }
   } else {
     hipLaunchKernelGGL((sv::k_filter_bisect<T, VEC>), grid, block, 0, st, map, V, a, s.top_k,
                        s.top_p, rs);

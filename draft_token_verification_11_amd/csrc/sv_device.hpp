@@ -64,6 +64,43 @@ __device__ __forceinline__ void load8(const T* row, int64_t e, int64_t V, float*
   }
 }
 
+// Raw form of load8: the 8 elements as 16-byte words (1 for bf16, 2 for
+// fp32), missing elements filled with -inf bits, unpacked later by unpack8.
+template <typename T>
+struct Raw8 {
+  uint4 v[8 / Elem<T>::kPerVec];
+};
+template <typename T, bool VEC>
+__device__ __forceinline__ void load8_raw(const T* row, int64_t e, int64_t V, Raw8<T>& out) {
+  constexpr int P = Elem<T>::kPerVec;
+  if (VEC && e + 8 <= V) {
+#pragma unroll
+    for (int h = 0; h < 8 / P; ++h) out.v[h] = load16(row + e + h * P);
+  } else if constexpr (sizeof(T) == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (e + 2 * i < V) ? (uint32_t)row[e + 2 * i] : 0xFF80u;
+      const uint32_t hi = (e + 2 * i + 1 < V) ? (uint32_t)row[e + 2 * i + 1] : 0xFF80u;
+      w[i] = lo | (hi << 16);
+    }
+    out.v[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = (e + i < V) ? __float_as_uint(((const float*)row)[e + i]) : 0xFF800000u;
+    out.v[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    out.v[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void unpack8(const Raw8<T>& r, float* out) {
+  constexpr int P = Elem<T>::kPerVec;
+#pragma unroll
+  for (int h = 0; h < 8 / P; ++h) Elem<T>::unpack(r.v[h], out + h * P);
+}
+
 // ---------------------------------------------------------------------------
 // Order-preserving keys: key(a) < key(b) iff a < b for non-NaN floats, with
 // -0 mapped to +0 so that equal values share one key.
@@ -198,15 +235,25 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t x) {
 }
 
 // ---------------------------------------------------------------------------
+// Workgroup barrier that orders LDS only: unlike __syncthreads() it does not
+// wait for outstanding global loads, so a prefetch issued before it stays in
+// flight across it.
+__device__ __forceinline__ void block_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------------------
 // Block-level reductions through a small LDS array of one slot per wave.
 // Every thread of the block must call them; all threads get the result.
 template <int NT, typename F>
 __device__ __forceinline__ F block_sum(F x, F* slots) {
   constexpr int NW = NT / kWave;
   x = wave_sum(x);
-  __syncthreads();
+  block_sync_lds();
   if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
-  __syncthreads();
+  block_sync_lds();
   F r = slots[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r += slots[w];
@@ -216,9 +263,9 @@ template <int NT>
 __device__ __forceinline__ float block_max(float x, float* slots) {
   constexpr int NW = NT / kWave;
   x = wave_max(x);
-  __syncthreads();
+  block_sync_lds();
   if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
-  __syncthreads();
+  block_sync_lds();
   float r = slots[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r = fmaxf(r, slots[w]);
@@ -228,9 +275,9 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t* slots) {
   constexpr int NW = NT / kWave;
   x = wave_max_u32(x);
-  __syncthreads();
+  block_sync_lds();
   if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
-  __syncthreads();
+  block_sync_lds();
   uint32_t r = slots[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r = max(r, slots[w]);
@@ -240,9 +287,9 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_min_u32(uint32_t x, uint32_t* slots) {
   constexpr int NW = NT / kWave;
   x = wave_min_u32(x);
-  __syncthreads();
+  block_sync_lds();
   if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
-  __syncthreads();
+  block_sync_lds();
   uint32_t r = slots[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r = min(r, slots[w]);
@@ -252,9 +299,9 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_or(uint32_t x, uint32_t* slots) {
   constexpr int NW = NT / kWave;
   x = wave_or(x);
-  __syncthreads();
+  block_sync_lds();
   if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
-  __syncthreads();
+  block_sync_lds();
   uint32_t r = slots[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) r |= slots[w];
@@ -268,9 +315,9 @@ __device__ __forceinline__ F block_incl_suffix(F x, F* slots, F* total) {
   constexpr int NW = NT / kWave;
   const int w = threadIdx.x / kWave;
   F s = wave_incl_suffix(x);
-  __syncthreads();
+  block_sync_lds();
   if ((threadIdx.x & (kWave - 1)) == 0) slots[w] = s;  // wave total
-  __syncthreads();
+  block_sync_lds();
   F above = F(0);
   F all = F(0);
 #pragma unroll

@@ -461,7 +461,7 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
     hist[0x3FFF] = w & 0xFFFFu;
     hist[0x4000] += (w >> 16);
   }
-  __syncthreads();
+  block_sync_lds();
 
   // S1: thread t counts group t (8 rotated 16-byte LDS reads).
   const uint4* h4 = reinterpret_cast<const uint4*>(hist);
@@ -494,7 +494,7 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
     const uint64_t bal = __ballot(ne);
     const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) S.wcount[wv] = (uint32_t)__popcll(bal);
-    __syncthreads();
+    block_sync_lds();
     uint32_t off = 0;
     for (int v = 0; v < wv; ++v) off += S.wcount[v];
     if (ne) S.list[off + before] = (uint16_t)g;
@@ -504,7 +504,7 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
       S.n_list = n;
     }
   }
-  __syncthreads();
+  block_sync_lds();
   const uint32_t nl = S.n_list;
 
   // Wave 0: max finite key, then the top-k key by exact counts.
@@ -542,7 +542,7 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
       }
     }
   }
-  __syncthreads();
+  block_sync_lds();
   if (S.state) {
     if (tid == 0) {
       RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
@@ -564,7 +564,7 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
     }
     if (lane == 0) S.gmass[i] = s;
   }
-  __syncthreads();
+  block_sync_lds();
 
   // S4 (wave 0): cumulative mass from the top; normaliser and top-p cut.
   if (wv == 0) {
@@ -637,8 +637,8 @@ __global__ __launch_bounds__(1024) void k_filter_bf16_hist(RowMap map, int64_t V
 }
 
 // ---------------------------------------------------------------------------
-// Per-sequence tail of the stochastic verify (one workgroup of 512 threads
-// per sequence): row statistics, ratio test at every drafted position, first
+// Per-sequence tail of the stochastic verify, run by one workgroup of NT
+// threads: row statistics, ratio test at every drafted position, first
 // rejection, then the residual max(0, p - q) at the rejected position (or the
 // bonus row's p) drawn by inverse CDF in ascending vocabulary order:
 // wave-contiguous segments of the row, 8 elements per lane per step, fp64
@@ -659,19 +659,20 @@ struct TailArgs {
   float* accept_prob;
 };
 
+struct TailScratch {
+  RowStat st[2 * SPEC_MAX_K + 1];
+  double wtot[16];
+  int32_t n, valid, emit;
+};
+
 __device__ __forceinline__ double prob_at(float l, const RowStat& s, float a) {
   if (!(l >= s.thr)) return 0.0;
   return exp2(((double)l - (double)s.m) * (double)a) / s.z;
 }
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(512) void k_tail(TailArgs A) {
-  constexpr int NT = 512;
+template <typename T, bool VEC, int NT>
+__device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   constexpr int NW = NT / kWave;
-  __shared__ RowStat st[2 * SPEC_MAX_K + 1];
-  __shared__ double wtot[NW];
-  __shared__ int32_t sh_n, sh_valid, sh_emit;
-  const int64_t b = blockIdx.x;
   const int k = A.k;
   const int nr = 2 * k + 1;
   const int tid = threadIdx.x;
@@ -696,14 +697,14 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
         p[c] = zero;
       }
     }
-    st[t] = s;
+    TS.st[t] = s;
   }
-  __syncthreads();
+  block_sync_lds();
 
   // Ratio test (wave 0, lane j = position j) and first rejection.
   if (w == 0) {
     bool ok = true;
-    for (int t = lane; t < nr; t += kWave) ok &= st[t].valid != 0;
+    for (int t = lane; t < nr; t += kWave) ok &= TS.st[t].valid != 0;
     int32_t x = 0;
     if (lane < k) {
       x = A.tokens[b * k + lane];
@@ -715,8 +716,8 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
       if (all_ok) {
         const T* tr = A.map.row<T>(b * nr + lane);
         const T* dr = A.map.row<T>(b * nr + k + 1 + lane);
-        const double p = prob_at(Elem<T>::load1(tr + x), st[lane], a);
-        const double q = prob_at(Elem<T>::load1(dr + x), st[k + 1 + lane], a);
+        const double p = prob_at(Elem<T>::load1(tr + x), TS.st[lane], a);
+        const double q = prob_at(Elem<T>::load1(dr + x), TS.st[k + 1 + lane], a);
         const double alpha = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
         acc = (double)A.u[b * (k + 1) + lane] < alpha;
         if (A.accept_prob) A.accept_prob[b * k + lane] = (float)alpha;
@@ -726,25 +727,25 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
     }
     const uint64_t rej = __ballot(lane < k && !acc);
     if (lane == 0) {
-      sh_valid = all_ok ? 1 : 0;
-      sh_n = rej ? (__ffsll((unsigned long long)rej) - 1) : k;
+      TS.valid = all_ok ? 1 : 0;
+      TS.n = rej ? (__ffsll((unsigned long long)rej) - 1) : k;
     }
   }
-  __syncthreads();
+  block_sync_lds();
   int32_t* out = A.out_tokens + b * (k + 1);
-  if (!sh_valid) {
+  if (!TS.valid) {
     for (int j = tid; j <= k; j += NT) out[j] = -1;
     if (tid == 0) A.accepted_len[b] = -1;
     return;
   }
-  const int n = sh_n;
+  const int n = TS.n;
 
   // Residual max(0, p_n - q_n) (n < k) or the bonus row's p_k (n = k).
   const T* prow = A.map.row<T>(b * nr + n);
   const bool has_q = n < k;
   const T* qrow = has_q ? A.map.row<T>(b * nr + k + 1 + n) : prow;
-  const RowStat sp = st[n];
-  const RowStat sq = has_q ? st[k + 1 + n] : st[n];
+  const RowStat sp = TS.st[n];
+  const RowStat sq = has_q ? TS.st[k + 1 + n] : TS.st[n];
   const float izp = (float)(1.0 / sp.z), izq = (float)(1.0 / sq.z);
   bool resid = has_q;
   const int64_t nsteps = (V + 511) / 512;
@@ -752,11 +753,10 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
   const int64_t s0 = (int64_t)w * spw;
   const int64_t s1 = min(nsteps, s0 + spw);
 
-  auto lane_values = [&](int64_t s, float* r8) -> double {
-    const int64_t e = s * 512 + lane * 8;
-    float lp[8], lq[8];
-    load8<T, VEC>(prow, e, V, lp);
-    if (resid) load8<T, VEC>(qrow, e, V, lq);
+  // Residual (or p) of the 8 elements of lane `lane` in step s; returns their
+  // sum (fp64, in element order, the same additions the crossing search
+  // repeats).
+  auto residual8 = [&](const float* lp, const float* lq, float* r8) -> double {
     double acc = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -771,81 +771,110 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
     }
     return acc;
   };
+  // U steps per batch: all their loads are issued before any is used.
+  constexpr int U = sizeof(T) == 2 ? 4 : 2;
+  auto load_batch = [&](int64_t s, Raw8<T>* rp, Raw8<T>* rq) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = (s + u) * 512 + lane * 8;
+      load8_raw<T, VEC>(prow, e, V, rp[u]);
+      if (resid) load8_raw<T, VEC>(qrow, e, V, rq[u]);
+    }
+  };
+  auto step_values = [&](const Raw8<T>& rp, const Raw8<T>& rq, float* r8) -> double {
+    float lp[8], lq[8];
+    unpack8<T>(rp, lp);
+    if (resid) unpack8<T>(rq, lq);
+    return residual8(lp, lq, r8);
+  };
 
   double S = 0.0;
   for (int attempt = 0; attempt < 2; ++attempt) {
     double wt = 0.0;
-    for (int64_t s = s0; s < s1; ++s) {
-      float r8[8];
-      const double ls = lane_values(s, r8);
-      wt += bcast(wave_incl_scan(ls), kWave - 1);
+    for (int64_t s = s0; s < s1; s += U) {
+      Raw8<T> rp[U], rq[U];
+      load_batch(s, rp, rq);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float r8[8];
+        const double ls = step_values(rp[u], rq[u], r8);
+        if (s + u < s1) wt += bcast(wave_incl_scan(ls), kWave - 1);
+      }
     }
-    if (lane == 0) wtot[w] = wt;
-    __syncthreads();
+    if (lane == 0) TS.wtot[w] = wt;
+    block_sync_lds();
     S = 0.0;
-    for (int v = 0; v < NW; ++v) S += wtot[v];
+    for (int v = 0; v < NW; ++v) S += TS.wtot[v];
     if (S > 0.0 || !resid) break;
     resid = false;  // a residual without mass falls back to p at that position
-    __syncthreads();
+    block_sync_lds();
   }
   const double target = (double)A.u[b * (k + 1) + k] * S;
   double cum = 0.0;
   int wstar = -1;
   for (int v = 0; v < NW; ++v) {
-    if (cum + wtot[v] > target) {
+    if (cum + TS.wtot[v] > target) {
       wstar = v;
       break;
     }
-    cum += wtot[v];
+    cum += TS.wtot[v];
   }
   if (wstar < 0) {  // unreachable for u < 1; take the last wave with mass
     cum = 0.0;
     for (int v = 0; v < NW; ++v)
-      if (wtot[v] > 0.0) wstar = v;
-    for (int v = 0; v < wstar; ++v) cum += wtot[v];
+      if (TS.wtot[v] > 0.0) wstar = v;
     if (wstar < 0) wstar = 0;
+    for (int v = 0; v < wstar; ++v) cum += TS.wtot[v];
   }
   if (w == wstar) {
     double wt = 0.0;
-    for (int64_t s = s0; s < s1; ++s) {
-      float r8[8];
-      const double ls = lane_values(s, r8);
-      const double inc = wave_incl_scan(ls);
-      const double stot = bcast(inc, kWave - 1);
-      if (cum + (wt + stot) > target || s == s1 - 1) {
-        const uint64_t hit = __ballot(cum + (wt + inc) > target);
-        const uint64_t pos = __ballot(ls > 0.0);
-        int L;
-        if (hit) {
-          L = __ffsll((unsigned long long)hit) - 1;
-          if (!((pos >> L) & 1ull)) {  // rounding corner: nearest lane with mass
-            const uint64_t below = pos & ((2ull << L) - 1ull);
-            L = below ? 63 - __clzll((long long)below)
-                      : (pos ? __ffsll((unsigned long long)pos) - 1 : L);
+    bool done = false;
+    for (int64_t s = s0; s < s1 && !done; s += U) {
+      Raw8<T> rp[U], rq[U];
+      load_batch(s, rp, rq);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (done || s + u >= s1) continue;
+        float r8[8];
+        const double ls = step_values(rp[u], rq[u], r8);
+        const double inc = wave_incl_scan(ls);
+        const double stot = bcast(inc, kWave - 1);
+        if (cum + (wt + stot) > target || s + u == s1 - 1) {
+          const uint64_t hit = __ballot(cum + (wt + inc) > target);
+          const uint64_t pos = __ballot(ls > 0.0);
+          int L;
+          if (hit) {
+            L = __ffsll((unsigned long long)hit) - 1;
+            if (!((pos >> L) & 1ull)) {  // rounding corner: nearest lane with mass
+              const uint64_t below = pos & ((2ull << L) - 1ull);
+              L = below ? 63 - __clzll((long long)below)
+                        : (pos ? __ffsll((unsigned long long)pos) - 1 : L);
+            }
+          } else {
+            L = pos ? 63 - __clzll((long long)pos) : 0;
           }
-        } else {
-          L = pos ? 63 - __clzll((long long)pos) : 0;
-        }
-        const double excl = L > 0 ? bcast(inc, L - 1) : 0.0;
-        if (lane == L) {
-          const double base = cum + (wt + excl);
-          double run = 0.0;
-          int pick = -1, lastpos = -1;
-          for (int i = 0; i < 8; ++i) {
-            if (r8[i] > 0.0f) lastpos = i;
-            run += (double)r8[i];
-            if (pick < 0 && base + run > target) pick = i;
+          const double excl = L > 0 ? bcast(inc, L - 1) : 0.0;
+          if (lane == L) {
+            const double base = cum + (wt + excl);
+            double run = 0.0;
+            int pick = -1, lastpos = -1;
+            for (int i = 0; i < 8; ++i) {
+              if (r8[i] > 0.0f) lastpos = i;
+              run += (double)r8[i];
+              if (pick < 0 && base + run > target) pick = i;
+            }
+            if (pick < 0 || !(r8[pick] > 0.0f)) pick = lastpos >= 0 ? lastpos : 0;
+            TS.emit = (int32_t)((s + u) * 512 + lane * 8 + pick);
           }
-          if (pick < 0 || !(r8[pick] > 0.0f)) pick = lastpos >= 0 ? lastpos : 0;
-          sh_emit = (int32_t)(s * 512 + lane * 8 + pick);
+          done = true;
+          continue;
         }
-        break;
+        wt += stot;
       }
-      wt += stot;
     }
   }
-  __syncthreads();
-  const int32_t emitted = sh_emit;
+  block_sync_lds();
+  const int32_t emitted = TS.emit;
   for (int j = tid; j <= k; j += NT) {
     int32_t v = -1;
     if (j < n) v = A.tokens[b * k + j];
@@ -853,6 +882,119 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
     out[j] = v;
   }
   if (tid == 0) A.accepted_len[b] = n;
+}
+
+// Out-of-line entry point of the bisection fallback, so that its registers do
+// not burden the persistent kernel's streaming loop.
+template <typename T, bool VEC, int NT>
+__device__ __noinline__ void filter_row_bisect_call(const T* row, int64_t V, float a, int top_k,
+                                                   float top_p, RowStat* out, double* dslot,
+                                                   uint32_t* uslot) {
+  filter_row_bisect<T, VEC, NT>(row, V, a, top_k, top_p, out, dslot, uslot);
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(512) void k_tail(TailArgs A) {
+  __shared__ TailScratch TS;
+  seq_tail<T, VEC, 512>(A, blockIdx.x, TS);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent bf16 filter: one 1024-thread workgroup per CU walks its rows
+// (XCD-aware: the workgroups of XCD x take the rows of one contiguous range,
+// so a sequence's rows are read by one XCD close together in time).  While a
+// row's histogram is scanned, the first PF vectors per thread of the next row
+// are already loading (the scan's barriers order LDS only, so they do not
+// wait for those loads).
+struct FilterArgs {
+  RowMap map;
+  int64_t V;
+  int64_t R;
+  float a;
+  int32_t top_k;
+  float top_p;
+  RowStat* stats;
+};
+
+template <bool VEC, int PF>
+__global__ __launch_bounds__(1024) void k_filter_bf16_persistent(FilterArgs F) {
+  constexpr int NT = 1024;
+  __shared__ uint32_t hist[32768];
+  __shared__ HistScratch S;
+  const int tid = threadIdx.x;
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per_xcd = nwg >> 3;  // nwg is a multiple of 8
+  const int64_t rx = (F.R + 7) / 8;
+  const int64_t r_lo = (int64_t)xcd * rx, r_hi = min(F.R, r_lo + rx);
+  const int64_t V = F.V;
+  const int64_t nfull = VEC ? V / 8 : 0;  // full 16-byte groups
+
+  uint4 pf[PF];
+  auto prefetch = [&](int64_t r) {
+    if (r < r_hi) {
+      const uint16_t* row = F.map.template row<uint16_t>(r);
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int64_t g = tid + (int64_t)j * NT;
+        if (g < nfull) pf[j] = load16(row + g * 8);
+      }
+    }
+  };
+  int64_t r = r_lo + slot;
+  prefetch(r);
+  for (; r < r_hi; r += per_xcd) {
+    const uint16_t* row = F.map.template row<uint16_t>(r);
+    hist_clear(hist);
+    block_sync_lds();
+    // count: the prefetched groups, then the rest of the row
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int64_t g = tid + (int64_t)j * NT;
+      if (g < nfull) {
+        hist_add8(hist, pf[j]);
+      } else {
+        for (int i = 0; i < 8 && g * 8 + i < V; ++i) {
+          const uint32_t k0 = key16_of_bits(row[g * 8 + i]);
+          atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
+        }
+      }
+    }
+    {
+      const int64_t ngroups = (V + 7) / 8;
+      int64_t g = tid + (int64_t)PF * NT;
+      if (VEC) {
+        for (; g + 3 * NT < nfull; g += 4 * NT) {
+          const uint4 v0 = load16(row + g * 8);
+          const uint4 v1 = load16(row + (g + NT) * 8);
+          const uint4 v2 = load16(row + (g + 2 * NT) * 8);
+          const uint4 v3 = load16(row + (g + 3 * NT) * 8);
+          hist_add8(hist, v0);
+          hist_add8(hist, v1);
+          hist_add8(hist, v2);
+          hist_add8(hist, v3);
+        }
+      }
+      for (; g < ngroups; g += NT) {
+        if (g < nfull) {
+          hist_add8(hist, load16(row + g * 8));
+        } else {
+          for (int i = 0; i < 8 && g * 8 + i < V; ++i) {
+            const uint32_t k0 = key16_of_bits(row[g * 8 + i]);
+            atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
+          }
+        }
+      }
+    }
+    block_sync_lds();
+    prefetch(r + per_xcd);  // lands while this row's histogram is scanned
+    if (hist_row_stats(hist, S, V, F.a, F.top_k, F.top_p, F.stats + r) == 2) {
+      block_sync_lds();
+      filter_row_bisect_call<uint16_t, VEC, NT>(row, V, F.a, F.top_k, F.top_p, F.stats + r,
+                                                 S.dslot, S.uslot);
+    }
+    block_sync_lds();
+  }
 }
 
 // ---------------------------------------------------------------------------
