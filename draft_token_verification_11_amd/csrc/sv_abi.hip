@@ -120,7 +120,7 @@ int persistent_grid(int64_t rows) {
   return int(g);
 }
 
-constexpr int kPrefetch = 4;  // 16-byte vectors per thread prefetched for the next row
+constexpr int kPrefetch = 1;  // 16-byte vectors per thread prefetched for the next row
 
 template <typename T, bool VEC>
 void launch_partials(const Layout& L, const sv::RowMap& map, int64_t V, float a, sv::Partial* part,

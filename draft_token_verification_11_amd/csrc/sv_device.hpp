@@ -120,15 +120,19 @@ __device__ __forceinline__ bool bad_logit(float f) {
   return __builtin_isnan(f) || f == __builtin_inff();
 }
 
-// 16-bit keys of bf16 patterns (the upper half of key_of for the widened
-// value, except that -0 keeps its own key 0x7FFF).
+// 16-bit order keys of bf16 patterns: 0x8000 + magnitude for positive
+// values, 0x8000 - magnitude for negative ones, so -0 and +0 share key 0x8000.
+// -inf is 0x0080, +inf 0xFF80; keys below 0x0080 or from 0xFF80 up are NaN/+inf.
 __device__ __forceinline__ uint32_t key16_of_bits(uint32_t h) {
-  return (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+  const uint32_t mag = h & 0x7FFFu;
+  return (h & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
 }
 __device__ __forceinline__ float value_of_key16(uint32_t k) {
-  uint32_t h = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+  const uint32_t h = k >= 0x8000u ? k - 0x8000u : (0x8000u | (0x8000u - k));
   return __uint_as_float(h << 16);
 }
+constexpr uint32_t kKey16NegInf = 0x0080u;
+constexpr uint32_t kKey16PosInf = 0xFF80u;
 
 // ---------------------------------------------------------------------------
 // Wave-level scans and reductions (wave64) built from DPP row shifts inside

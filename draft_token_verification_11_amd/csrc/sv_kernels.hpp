@@ -379,15 +379,13 @@ __global__ __launch_bounds__(1024) void k_filter_bisect(RowMap map, int64_t V, f
 // Overflow (>= 65536 equal values) is detected by the count total and falls
 // back to the bisection path.
 struct HistScratch {
-  uint32_t gcnt[1024];   // count of group g (keys 64 g .. 64 g + 63)
-  uint16_t list[1024];   // non-empty groups, descending key order
-  double gmass[1024];    // mass of list entry i over keys >= the top-k key
-  uint32_t wcount[16];
+  uint16_t list[1024];   // non-empty 64-key groups, descending key order
+  uint32_t lcnt[1024];   // count of list entry i
+  float gmass[1024];     // mass of list entry i relative to the reference value
+  uint32_t wcount[16], wtot[16], wbad[16];
   double dslot[16];
   uint32_t uslot[16];
-  uint32_t n_list, max_key, tk, tk_entry, tp;
-  int32_t state;         // 0 ok, 1 invalid row
-  double z;
+  uint32_t tk, tk_entry;
 };
 
 __device__ __forceinline__ void hist_clear(uint32_t* hist) {
@@ -395,14 +393,17 @@ __device__ __forceinline__ void hist_clear(uint32_t* hist) {
   for (int i = threadIdx.x; i < 8192; i += 1024) h4[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
+__device__ __forceinline__ void hist_add1(uint32_t* hist, uint32_t bits) {
+  const uint32_t k = key16_of_bits(bits);
+  atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u);
+}
+
 __device__ __forceinline__ void hist_add8(uint32_t* hist, uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t k0 = key16_of_bits(w[i] & 0xFFFFu);
-    const uint32_t k1 = key16_of_bits(w[i] >> 16);
-    atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
-    atomicAdd(&hist[k1 >> 1], (k1 & 1u) ? 0x10000u : 1u);
+    hist_add1(hist, w[i] & 0xFFFFu);
+    hist_add1(hist, w[i] >> 16);
   }
 }
 
@@ -429,166 +430,158 @@ __device__ __forceinline__ void hist_count_row(uint32_t* hist, const uint16_t* r
     if (VEC && e + 8 <= V) {
       hist_add8(hist, load16(row + e));
     } else {
-      for (int i = 0; i < 8 && e + i < V; ++i) {
-        const uint32_t k0 = key16_of_bits(row[e + i]);
-        atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
-      }
+      for (int i = 0; i < 8 && e + i < V; ++i) hist_add1(hist, row[e + i]);
     }
   }
 }
 
-// Mass of key `key` (count c) relative to the max logit m.
-__device__ __forceinline__ double key_mass(uint32_t key, uint32_t c, float m, float a) {
-  return c ? (double)c * (double)__builtin_amdgcn_exp2f((value_of_key16(key) - m) * a) : 0.0;
+// Mass of `key` (count c) relative to the max logit m.
+__device__ __forceinline__ float key_mass(uint32_t key, uint32_t c, float m, float a) {
+  return c ? (float)c * __builtin_amdgcn_exp2f((value_of_key16(key) - m) * a) : 0.0f;
 }
 
 // Row statistics from a filled histogram (all 1024 threads).  Returns 0 on
 // success (RowStat written), 1 for an invalid row (written), 2 on counter
-// overflow (nothing written: the caller takes the bisection path).
+// overflow (nothing written: the caller takes the bisection path).  Leaves
+// the histogram all zero when it returns 0 or 1.
 __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a, int top_k,
                               float top_p, RowStat* out) {
   constexpr int NT = 1024;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
-  const uint16_t* c16 = reinterpret_cast<const uint16_t*>(hist);
+  uint16_t* c16 = reinterpret_cast<uint16_t*>(hist);
   const bool use_k = top_k > 0 && (int64_t)top_k < V;
   const bool use_p = top_p < 1.0f;
 
-  // -0 and +0 are one value: move the count of key 0x7FFF (-0) to 0x8000.
-  if (tid == 0) {
-    const uint32_t w = hist[0x3FFF];
-    hist[0x3FFF] = w & 0xFFFFu;
-    hist[0x4000] += (w >> 16);
+  // Counts of group g = 1023 - tid (8 rotated 16-byte reads), validity,
+  // total, and the compacted list of non-empty groups in descending order.
+  const int g = 1023 - tid;
+  uint32_t cnt = 0;
+  {
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 w = h4[g * 8 + ((j + g) & 7)];
+      cnt += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) + (w.z & 0xFFFFu) +
+             (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
+    }
+  }
+  // groups 0, 1 hold keys below -inf (negative NaNs), 1022, 1023 +inf and NaNs
+  const bool bad = cnt != 0 && (g <= 1 || g >= 1022);
+  const uint64_t ne = __ballot(cnt != 0);
+  const uint32_t wsum = wave_sum(cnt);
+  const uint64_t wbad = __ballot(bad);
+  if (lane == 0) {
+    S.wcount[wv] = (uint32_t)__popcll(ne);
+    S.wtot[wv] = wsum;
+    S.wbad[wv] = wbad ? 1u : 0u;
+  }
+  block_sync_lds();
+  uint32_t total = 0, anybad = 0, off = 0, nl = 0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    total += S.wtot[v];
+    anybad |= S.wbad[v];
+    off += v < wv ? S.wcount[v] : 0u;
+    nl += S.wcount[v];
+  }
+  if (cnt != 0) {
+    const uint32_t pos = off + (uint32_t)__popcll(ne & ((1ull << lane) - 1ull));
+    S.list[pos] = (uint16_t)g;
+    S.lcnt[pos] = cnt;
   }
   block_sync_lds();
 
-  // S1: thread t counts group t (8 rotated 16-byte LDS reads).
-  const uint4* h4 = reinterpret_cast<const uint4*>(hist);
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint4 w = h4[tid * 8 + ((j + tid) & 7)];
-    cnt += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) + (w.z & 0xFFFFu) +
-           (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
-  }
-  S.gcnt[tid] = cnt;
-  // keys < 0x7F are negative NaNs, keys >= 0xFF80 are +inf and positive NaNs
-  uint32_t bad = (tid == 0 || tid >= 1022) ? cnt : 0u;
-  if (tid == 1) bad = cnt - c16[0x7F];
-  const uint32_t total = block_sum<NT>(cnt, S.uslot);
-  bad = block_or<NT>(bad, S.uslot);
-  if (bad) {
+  auto clear_listed = [&]() {  // zero the groups that hold counts
+    uint4* h4 = reinterpret_cast<uint4*>(hist);
+    for (uint32_t i = tid >> 3; i < nl; i += NT / 8) h4[(uint32_t)S.list[i] * 8 + (tid & 7)] = make_uint4(0u, 0u, 0u, 0u);
+  };
+  if (anybad) {
     if (tid == 0) {
       RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
       *out = st;
     }
+    clear_listed();
     return 1;
   }
-  if ((int64_t)total != V) return 2;
+  if ((int64_t)total != V) return 2;  // a 16-bit counter overflowed
 
-  // S2: non-empty groups in descending key order (thread t looks at group 1023 - t).
-  {
-    const int g = 1023 - tid;
-    const bool ne = S.gcnt[g] != 0;
-    const uint64_t bal = __ballot(ne);
-    const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) S.wcount[wv] = (uint32_t)__popcll(bal);
-    block_sync_lds();
-    uint32_t off = 0;
-    for (int v = 0; v < wv; ++v) off += S.wcount[v];
-    if (ne) S.list[off + before] = (uint16_t)g;
-    if (tid == NT - 1) {
-      uint32_t n = 0;
-      for (int v = 0; v < 16; ++v) n += S.wcount[v];
-      S.n_list = n;
+  // Every wave finds the max finite key in the highest non-empty group.
+  const uint32_t g0 = S.list[0];
+  const uint64_t nzmax = __ballot(c16[g0 * 64 + lane] != 0 && g0 * 64 + lane > kKey16NegInf);
+  if (!nzmax) {  // no finite logit (only -inf)
+    if (tid == 0) {
+      RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
+      *out = st;
     }
+    block_sync_lds();
+    clear_listed();
+    return 1;
   }
-  block_sync_lds();
-  const uint32_t nl = S.n_list;
-
-  // Wave 0: max finite key, then the top-k key by exact counts.
-  if (wv == 0) {
-    const uint32_t g0 = S.list[0];
-    const uint32_t key = g0 * 64 + lane;
-    const uint64_t nz = __ballot(c16[key] != 0 && key > 0x7Fu);
+  const uint32_t max_key = g0 * 64 + (63 - __clzll((long long)nzmax));
+  const float m = value_of_key16(max_key);
+  // Wave 0, with top-k: the top-k key by exact counts.
+  if (use_k && wv == 0) {
     if (lane == 0) {
-      S.state = nz ? 0 : 1;  // only -inf in the row
-      S.max_key = nz ? g0 * 64 + (63 - __clzll((long long)nz)) : 0u;
       S.tk = 0;
       S.tk_entry = nl - 1;
     }
-    if (use_k && nz) {
-      uint32_t carry = 0;
-      for (uint32_t base = 0; base < nl; base += kWave) {
-        const uint32_t x = (base + lane < nl) ? S.gcnt[S.list[base + lane]] : 0u;
-        const uint32_t inc = wave_incl_scan(x) + carry;
-        const uint64_t hit = __ballot(base + lane < nl && inc >= (uint32_t)top_k);
-        if (hit) {
-          const int L = __ffsll((unsigned long long)hit) - 1;
-          const uint32_t before = bcast(inc - x, L);
-          const uint32_t g = S.list[base + L];
-          // within the group: suffix counts over keys, descending
-          const uint32_t c = c16[g * 64 + lane];
-          const uint32_t suf = wave_incl_suffix(c) + before;
-          const uint64_t ok = __ballot(suf >= (uint32_t)top_k);
-          if (lane == 0) {
-            S.tk = g * 64 + (63 - __clzll((long long)ok));
-            S.tk_entry = base + L;
-          }
-          break;
+    uint32_t carry = 0;
+    for (uint32_t base = 0; base < nl; base += kWave) {
+      const uint32_t x = (base + lane < nl) ? S.lcnt[base + lane] : 0u;
+      const uint32_t inc = wave_incl_scan(x) + carry;
+      const uint64_t hit = __ballot(base + lane < nl && inc >= (uint32_t)top_k);
+      if (hit) {
+        const int L = __ffsll((unsigned long long)hit) - 1;
+        const uint32_t before = bcast(inc - x, L);
+        const uint32_t gk = S.list[base + L];
+        const uint32_t c = c16[gk * 64 + lane];
+        const uint32_t suf = wave_incl_suffix(c) + before;
+        const uint64_t ok = __ballot(suf >= (uint32_t)top_k);
+        if (lane == 0) {
+          S.tk = gk * 64 + (63 - __clzll((long long)ok));
+          S.tk_entry = base + L;
         }
-        carry = bcast(inc, kWave - 1);
+        break;
       }
+      carry = bcast(inc, kWave - 1);
     }
   }
-  block_sync_lds();
-  if (S.state) {
-    if (tid == 0) {
-      RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
-      *out = st;
-    }
-    return 1;
-  }
-  const float m = value_of_key16(S.max_key);
-  const uint32_t tk = S.tk;
-  const uint32_t last = S.tk_entry;  // entries after it lie below the top-k key
+  if (use_k) block_sync_lds();
+  const uint32_t tk = use_k ? S.tk : 0u;
+  const uint32_t last = use_k ? S.tk_entry : nl - 1;  // entries after it lie below tk
 
-  // S3: masses of the list entries (one wave per entry, lane = key).
-  for (uint32_t i = wv; i < nl; i += 16) {
-    double s = 0.0;
-    if (i <= last) {
-      const uint32_t key = (uint32_t)S.list[i] * 64 + lane;
-      const double e = key >= tk ? key_mass(key, c16[key], m, a) : 0.0;
-      s = wave_sum(e);
-    }
+  // Group masses over keys >= tk (one wave per list entry, lane = key).
+  for (uint32_t i = wv; i <= last; i += 16) {
+    const uint32_t key = (uint32_t)S.list[i] * 64 + lane;
+    const float e = key >= tk ? key_mass(key, c16[key], m, a) : 0.0f;
+    const float s = wave_sum(e);
     if (lane == 0) S.gmass[i] = s;
   }
   block_sync_lds();
 
-  // S4 (wave 0): cumulative mass from the top; normaliser and top-p cut.
+  // Wave 0: normaliser, then the top-p cut by cumulative mass from the top.
   if (wv == 0) {
-    double carry = 0.0;
-    for (uint32_t base = 0; base < nl; base += kWave) {
-      const double x = (base + lane < nl) ? S.gmass[base + lane] : 0.0;
-      carry = bcast(wave_incl_scan(x) + carry, kWave - 1);
-    }
-    const double zk = carry;
+    double part = 0.0;
+    for (uint32_t i = lane; i <= last; i += kWave) part += (double)S.gmass[i];
+    const double zk = wave_sum(part);
     uint32_t thr_key = tk;
     double z = zk;
     if (use_p) {
       const double target = (double)top_p * zk;
-      double c2 = 0.0;
-      for (uint32_t base = 0; base < nl; base += kWave) {
-        const double x = (base + lane < nl) ? S.gmass[base + lane] : 0.0;
-        const double inc = wave_incl_scan(x) + c2;
-        const uint64_t hit = __ballot(base + lane < nl && inc >= target);
-        if (hit || base + kWave >= nl) {
-          int L = hit ? __ffsll((unsigned long long)hit) - 1 : (int)(nl - 1 - base);
+      double carry = 0.0;
+      for (uint32_t base = 0; base <= last; base += kWave) {
+        const bool in = base + lane <= last;
+        const double x = in ? (double)S.gmass[base + lane] : 0.0;
+        const double inc = wave_incl_scan(x) + carry;
+        const uint64_t hit = __ballot(in && inc >= target);
+        if (hit || base + kWave > last) {
+          const int L = hit ? __ffsll((unsigned long long)hit) - 1 : (int)(last - base);
           const double before = bcast(inc - x, L);
-          const uint32_t g = S.list[base + L];
-          const uint32_t key = g * 64 + lane;
-          const double e = key >= tk ? key_mass(key, c16[key], m, a) : 0.0;
+          const uint32_t gc = S.list[base + L];
+          const uint32_t key = gc * 64 + lane;
+          const double e = key >= tk ? (double)key_mass(key, c16[key], m, a) : 0.0;
           const double suf = wave_incl_suffix(e) + before;
           const uint64_t ok = __ballot(suf >= target);
           int pick;
@@ -598,11 +591,11 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
             const uint64_t nzm = __ballot(e > 0.0);
             pick = nzm ? __ffsll((unsigned long long)nzm) - 1 : 0;
           }
-          thr_key = max(tk, g * 64 + (uint32_t)pick);
+          thr_key = max(tk, gc * 64 + (uint32_t)pick);
           z = bcast(suf, pick);
           break;
         }
-        c2 = bcast(inc, kWave - 1);
+        carry = bcast(inc, kWave - 1);
       }
     }
     if (lane == 0) {
@@ -615,6 +608,8 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
       *out = st;
     }
   }
+  block_sync_lds();
+  clear_listed();
   return 0;
 }
 
@@ -943,9 +938,9 @@ __global__ __launch_bounds__(1024) void k_filter_bf16_persistent(FilterArgs F) {
   };
   int64_t r = r_lo + slot;
   prefetch(r);
+  hist_clear(hist);  // afterwards each row's scan leaves the histogram zero
   for (; r < r_hi; r += per_xcd) {
     const uint16_t* row = F.map.template row<uint16_t>(r);
-    hist_clear(hist);
     block_sync_lds();
     // count: the prefetched groups, then the rest of the row
 #pragma unroll
@@ -954,10 +949,7 @@ __global__ __launch_bounds__(1024) void k_filter_bf16_persistent(FilterArgs F) {
       if (g < nfull) {
         hist_add8(hist, pf[j]);
       } else {
-        for (int i = 0; i < 8 && g * 8 + i < V; ++i) {
-          const uint32_t k0 = key16_of_bits(row[g * 8 + i]);
-          atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
-        }
+        for (int i = 0; i < 8 && g * 8 + i < V; ++i) hist_add1(hist, row[g * 8 + i]);
       }
     }
     {
@@ -979,10 +971,7 @@ __global__ __launch_bounds__(1024) void k_filter_bf16_persistent(FilterArgs F) {
         if (g < nfull) {
           hist_add8(hist, load16(row + g * 8));
         } else {
-          for (int i = 0; i < 8 && g * 8 + i < V; ++i) {
-            const uint32_t k0 = key16_of_bits(row[g * 8 + i]);
-            atomicAdd(&hist[k0 >> 1], (k0 & 1u) ? 0x10000u : 1u);
-          }
+          for (int i = 0; i < 8 && g * 8 + i < V; ++i) hist_add1(hist, row[g * 8 + i]);
         }
       }
     }
@@ -992,8 +981,9 @@ __global__ __launch_bounds__(1024) void k_filter_bf16_persistent(FilterArgs F) {
       block_sync_lds();
       filter_row_bisect_call<uint16_t, VEC, NT>(row, V, F.a, F.top_k, F.top_p, F.stats + r,
                                                  S.dslot, S.uslot);
+      block_sync_lds();
+      hist_clear(hist);
     }
-    block_sync_lds();
   }
 }
 
