@@ -121,6 +121,7 @@ int persistent_grid(int64_t rows) {
 }
 
 constexpr int kPrefetch = 1;  // 16-byte vectors per thread prefetched for the next row
+constexpr int kLoadDepth = 8;  // 16-byte loads in flight per thread in the row stream
 
 template <typename T, bool VEC>
 void launch_partials(const Layout& L, const sv::RowMap& map, int64_t V, float a, sv::Partial* part,
@@ -165,7 +166,7 @@ void launch_filter(const Layout& L, const sv::RowMap& map, int64_t V, float a,
   if constexpr (sizeof(T) == 2) {
     if (VEC) {
       sv::FilterArgs F{map, V, L.rows, a, s.top_k, s.top_p, rs};
-      hipLaunchKernelGGL((sv::k_filter_bf16_persistent<true, kPrefetch>),
+      hipLaunchKernelGGL((sv::k_filter_bf16_persistent<true, kPrefetch, kLoadDepth>),
                          dim3(persistent_grid(L.rows)), block, 0, st, F);
     } else {
       hipLaunchKernelGGL((sv::k_filter_bf16_hist<VEC>), grid, block, 0, st, map, V, a, s.top_k,

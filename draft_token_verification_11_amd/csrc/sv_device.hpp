@@ -120,19 +120,19 @@ __device__ __forceinline__ bool bad_logit(float f) {
   return __builtin_isnan(f) || f == __builtin_inff();
 }
 
-// 16-bit order keys of bf16 patterns: 0x8000 + magnitude for positive
-// values, 0x8000 - magnitude for negative ones, so -0 and +0 share key 0x8000.
-// -inf is 0x0080, +inf 0xFF80; keys below 0x0080 or from 0xFF80 up are NaN/+inf.
-__device__ __forceinline__ uint32_t key16_of_bits(uint32_t h) {
-  const uint32_t mag = h & 0x7FFFu;
-  return (h & 0x8000u) ? 0x8000u - mag : 0x8000u + mag;
+// 16-bit order keys of bf16 patterns: negative patterns h map to 0xFFFF - h,
+// non-negative ones to 0x8000 + h, so key order is value order (-0 at key
+// 0x7FFF sits next to +0 at 0x8000; callers fold the two).  -inf is key
+// 0x007F, +inf 0xFF80; keys below 0x007F or from 0xFF80 up are NaN/+inf.
+__device__ __forceinline__ uint32_t raw_of_key16(uint32_t k) {
+  return k >= 0x8000u ? k - 0x8000u : 0xFFFFu - k;
 }
 __device__ __forceinline__ float value_of_key16(uint32_t k) {
-  const uint32_t h = k >= 0x8000u ? k - 0x8000u : (0x8000u | (0x8000u - k));
-  return __uint_as_float(h << 16);
+  return __uint_as_float(raw_of_key16(k) << 16);
 }
-constexpr uint32_t kKey16NegInf = 0x0080u;
-constexpr uint32_t kKey16PosInf = 0xFF80u;
+constexpr uint32_t kKey16NegInf = 0x007Fu;
+constexpr uint32_t kKey16NegZero = 0x7FFFu;
+constexpr uint32_t kKey16PosZero = 0x8000u;
 
 // ---------------------------------------------------------------------------
 // Wave-level scans and reductions (wave64) built from DPP row shifts inside

@@ -393,17 +393,18 @@ __device__ __forceinline__ void hist_clear(uint32_t* hist) {
   for (int i = threadIdx.x; i < 8192; i += 1024) h4[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-__device__ __forceinline__ void hist_add1(uint32_t* hist, uint32_t bits) {
-  const uint32_t k = key16_of_bits(bits);
-  atomicAdd(&hist[k >> 1], (k & 1u) ? 0x10000u : 1u);
+// The histogram counts raw bf16 patterns (code c: 16-bit half c & 1 of word
+// c >> 1); the scan reads it in key order through raw_of_key16.
+__device__ __forceinline__ void hist_add1(uint32_t* hist, uint32_t code) {
+  atomicAdd(&hist[code >> 1], 1u + (code & 1u) * 0xFFFFu);
 }
 
 __device__ __forceinline__ void hist_add8(uint32_t* hist, uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    hist_add1(hist, w[i] & 0xFFFFu);
-    hist_add1(hist, w[i] >> 16);
+    atomicAdd(&hist[(w[i] & 0xFFFFu) >> 1], 1u + (w[i] & 1u) * 0xFFFFu);
+    atomicAdd(&hist[w[i] >> 17], 1u + ((w[i] >> 16) & 1u) * 0xFFFFu);
   }
 }
 
@@ -454,21 +455,29 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
   const bool use_k = top_k > 0 && (int64_t)top_k < V;
   const bool use_p = top_p < 1.0f;
 
-  // Counts of group g = 1023 - tid (8 rotated 16-byte reads), validity,
-  // total, and the compacted list of non-empty groups in descending order.
+  // Counts of key group g = 1023 - tid (keys 64 g .. 64 g + 63; 8 rotated
+  // 16-byte reads of its raw group), validity, total, and the compacted list
+  // of non-empty groups in descending order.  -0 (key 0x7FFF, last of group
+  // 511) is counted with +0 (key 0x8000, first of group 512).
   const int g = 1023 - tid;
+  const uint32_t rg = g >= 512 ? (uint32_t)g - 512u : 1023u - (uint32_t)g;
   uint32_t cnt = 0;
   {
     const uint4* h4 = reinterpret_cast<const uint4*>(hist);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint4 w = h4[g * 8 + ((j + g) & 7)];
+      const uint4 w = h4[rg * 8 + ((j + rg) & 7)];
       cnt += (w.x & 0xFFFFu) + (w.x >> 16) + (w.y & 0xFFFFu) + (w.y >> 16) + (w.z & 0xFFFFu) +
              (w.z >> 16) + (w.w & 0xFFFFu) + (w.w >> 16);
     }
+    const uint32_t neg0 = c16[0x8000];
+    if (g == 511) cnt -= neg0;
+    if (g == 512) cnt += neg0;
   }
-  // groups 0, 1 hold keys below -inf (negative NaNs), 1022, 1023 +inf and NaNs
-  const bool bad = cnt != 0 && (g <= 1 || g >= 1022);
+  // keys below 0x7F (groups 0 and 1 but for its last key, -inf) are negative
+  // NaNs; groups 1022 and 1023 hold +inf and positive NaNs
+  const bool bad = (cnt != 0 && (g == 0 || g >= 1022)) ||
+                   (g == 1 && cnt != c16[raw_of_key16(kKey16NegInf)]);
   const uint64_t ne = __ballot(cnt != 0);
   const uint32_t wsum = wave_sum(cnt);
   const uint64_t wbad = __ballot(bad);
@@ -493,9 +502,20 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
   }
   block_sync_lds();
 
+  // count of key `key` (with -0 folded into +0)
+  auto kcount = [&](uint32_t key) -> uint32_t {
+    if (key == kKey16NegZero) return 0u;
+    const uint32_t c = c16[raw_of_key16(key)];
+    return key == kKey16PosZero ? c + c16[0x8000] : c;
+  };
   auto clear_listed = [&]() {  // zero the groups that hold counts
     uint4* h4 = reinterpret_cast<uint4*>(hist);
-    for (uint32_t i = tid >> 3; i < nl; i += NT / 8) h4[(uint32_t)S.list[i] * 8 + (tid & 7)] = make_uint4(0u, 0u, 0u, 0u);
+    for (uint32_t i = tid >> 3; i < nl; i += NT / 8) {
+      const uint32_t gl = S.list[i];
+      const uint32_t rgl = gl >= 512 ? gl - 512u : 1023u - gl;
+      h4[rgl * 8 + (tid & 7)] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (tid == 0) c16[0x8000] = 0;  // -0 (its group may not be listed)
   };
   if (anybad) {
     if (tid == 0) {
@@ -509,7 +529,7 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
 
   // Every wave finds the max finite key in the highest non-empty group.
   const uint32_t g0 = S.list[0];
-  const uint64_t nzmax = __ballot(c16[g0 * 64 + lane] != 0 && g0 * 64 + lane > kKey16NegInf);
+  const uint64_t nzmax = __ballot(kcount(g0 * 64 + lane) != 0 && g0 * 64 + lane > kKey16NegInf);
   if (!nzmax) {  // no finite logit (only -inf)
     if (tid == 0) {
       RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
@@ -536,7 +556,7 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
         const int L = __ffsll((unsigned long long)hit) - 1;
         const uint32_t before = bcast(inc - x, L);
         const uint32_t gk = S.list[base + L];
-        const uint32_t c = c16[gk * 64 + lane];
+        const uint32_t c = kcount(gk * 64 + lane);
         const uint32_t suf = wave_incl_suffix(c) + before;
         const uint64_t ok = __ballot(suf >= (uint32_t)top_k);
         if (lane == 0) {
@@ -552,20 +572,26 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
   const uint32_t tk = use_k ? S.tk : 0u;
   const uint32_t last = use_k ? S.tk_entry : nl - 1;  // entries after it lie below tk
 
-  // Group masses over keys >= tk (one wave per list entry, lane = key).
+  // Masses over keys >= tk: every lane accumulates its keys of the list
+  // entries its wave visits (one wave per entry, lane = key) for the
+  // normaliser; the first kTop entries also get their group totals, which
+  // is where the top-p cut lies for any sensible top_p (deeper entries are
+  // summed on demand below).
+  constexpr uint32_t kTop = 32;
+  float acc = 0.0f;
   for (uint32_t i = wv; i <= last; i += 16) {
     const uint32_t key = (uint32_t)S.list[i] * 64 + lane;
-    const float e = key >= tk ? key_mass(key, c16[key], m, a) : 0.0f;
-    const float s = wave_sum(e);
-    if (lane == 0) S.gmass[i] = s;
+    const float e = key >= tk ? key_mass(key, kcount(key), m, a) : 0.0f;
+    acc += e;
+    if (i < kTop) {
+      const float gs = wave_sum(e);
+      if (lane == 0) S.gmass[i] = gs;
+    }
   }
-  block_sync_lds();
+  const double zk = block_sum<NT>((double)acc, S.dslot);
 
-  // Wave 0: normaliser, then the top-p cut by cumulative mass from the top.
+  // Wave 0: the top-p cut by cumulative mass from the top.
   if (wv == 0) {
-    double part = 0.0;
-    for (uint32_t i = lane; i <= last; i += kWave) part += (double)S.gmass[i];
-    const double zk = wave_sum(part);
     uint32_t thr_key = tk;
     double z = zk;
     if (use_p) {
@@ -573,15 +599,36 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
       double carry = 0.0;
       for (uint32_t base = 0; base <= last; base += kWave) {
         const bool in = base + lane <= last;
-        const double x = in ? (double)S.gmass[base + lane] : 0.0;
+        double x = 0.0;
+        if (base < kTop) {
+          x = (in && base + lane < kTop) ? (double)S.gmass[base + lane] : 0.0;
+        }
         const double inc = wave_incl_scan(x) + carry;
-        const uint64_t hit = __ballot(in && inc >= target);
-        if (hit || base + kWave > last) {
-          const int L = hit ? __ffsll((unsigned long long)hit) - 1 : (int)(last - base);
-          const double before = bcast(inc - x, L);
+        // entries from kTop on: their totals are computed one by one
+        uint64_t hit = __ballot(in && base + lane < kTop && inc >= target);
+        int L = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
+        double before = L >= 0 ? bcast(inc - x, L) : 0.0;
+        if (L < 0 && base + kWave >= kTop) {
+          double run = bcast(inc, kWave - 1);
+          for (uint32_t i = max(base, kTop); i <= last; ++i) {
+            const uint32_t key = (uint32_t)S.list[i] * 64 + lane;
+            const double gm = wave_sum(key >= tk ? (double)key_mass(key, kcount(key), m, a) : 0.0);
+            if (run + gm >= target || i == last) {
+              L = (int)(i - base);
+              before = run;
+              break;
+            }
+            run += gm;
+          }
+        }
+        if (L >= 0 || base + kWave > last) {
+          if (L < 0) {  // rounding corner: the last entry
+            L = (int)(last - base);
+            before = bcast(inc - x, L);
+          }
           const uint32_t gc = S.list[base + L];
           const uint32_t key = gc * 64 + lane;
-          const double e = key >= tk ? (double)key_mass(key, c16[key], m, a) : 0.0;
+          const double e = key >= tk ? (double)key_mass(key, kcount(key), m, a) : 0.0;
           const double suf = wave_incl_suffix(e) + before;
           const uint64_t ok = __ballot(suf >= target);
           int pick;
@@ -749,10 +796,10 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   const int64_t s1 = min(nsteps, s0 + spw);
 
   // Residual (or p) of the 8 elements of lane `lane` in step s; returns their
-  // sum (fp64, in element order, the same additions the crossing search
-  // repeats).
+  // sum (fp32 in element order -- the same additions the crossing search
+  // repeats -- widened to fp64).
   auto residual8 = [&](const float* lp, const float* lq, float* r8) -> double {
-    double acc = 0.0;
+    float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float p = lp[i] >= sp.thr ? __builtin_amdgcn_exp2f((lp[i] - sp.m) * a) * izp : 0.0f;
@@ -762,9 +809,9 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
         r = fmaxf(p - q, 0.0f);
       }
       r8[i] = r;
-      acc += (double)r;
+      acc += r;
     }
-    return acc;
+    return (double)acc;
   };
   // U steps per batch: all their loads are issued before any is used.
   constexpr int U = sizeof(T) == 2 ? 4 : 2;
@@ -851,12 +898,12 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
           const double excl = L > 0 ? bcast(inc, L - 1) : 0.0;
           if (lane == L) {
             const double base = cum + (wt + excl);
-            double run = 0.0;
+            float run = 0.0f;
             int pick = -1, lastpos = -1;
             for (int i = 0; i < 8; ++i) {
               if (r8[i] > 0.0f) lastpos = i;
-              run += (double)r8[i];
-              if (pick < 0 && base + run > target) pick = i;
+              run += r8[i];
+              if (pick < 0 && base + (double)run > target) pick = i;
             }
             if (pick < 0 || !(r8[pick] > 0.0f)) pick = lastpos >= 0 ? lastpos : 0;
             TS.emit = (int32_t)((s + u) * 512 + lane * 8 + pick);
@@ -911,7 +958,7 @@ struct FilterArgs {
   RowStat* stats;
 };
 
-template <bool VEC, int PF>
+template <bool VEC, int PF, int D>
 __global__ __launch_bounds__(1024) void k_filter_bf16_persistent(FilterArgs F) {
   constexpr int NT = 1024;
   __shared__ uint32_t hist[32768];
@@ -956,15 +1003,13 @@ __global__ __launch_bounds__(1024) void k_filter_bf16_persistent(FilterArgs F) {
       const int64_t ngroups = (V + 7) / 8;
       int64_t g = tid + (int64_t)PF * NT;
       if (VEC) {
-        for (; g + 3 * NT < nfull; g += 4 * NT) {
-          const uint4 v0 = load16(row + g * 8);
-          const uint4 v1 = load16(row + (g + NT) * 8);
-          const uint4 v2 = load16(row + (g + 2 * NT) * 8);
-          const uint4 v3 = load16(row + (g + 3 * NT) * 8);
-          hist_add8(hist, v0);
-          hist_add8(hist, v1);
-          hist_add8(hist, v2);
-          hist_add8(hist, v3);
+        // D 16-byte loads in flight per thread
+        for (; g + (D - 1) * NT < nfull; g += D * NT) {
+          uint4 v[D];
+#pragma unroll
+          for (int d = 0; d < D; ++d) v[d] = load16(row + (g + (int64_t)d * NT) * 8);
+#pragma unroll
+          for (int d = 0; d < D; ++d) hist_add8(hist, v[d]);
         }
       }
       for (; g < ngroups; g += NT) {
