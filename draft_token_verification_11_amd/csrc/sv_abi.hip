@@ -120,7 +120,7 @@ int persistent_grid(int64_t rows) {
   return int(g);
 }
 
-constexpr int kPrefetch = 1;  // 16-byte vectors per thread prefetched for the next row
+constexpr int kPrefetch = 2;  // 16-byte vectors per thread prefetched for the next row
 constexpr int kLoadDepth = 8;  // 16-byte loads in flight per thread in the row stream
 
 template <typename T, bool VEC>
