@@ -228,8 +228,7 @@ __global__ __launch_bounds__(64) void k_greedy_tail(int64_t V, int k, int nchunk
   const int64_t b = blockIdx.x;
   const int lane = threadIdx.x;
   const int k1 = k + 1;
-  __shared__ int32_t best_idx[SPEC_MAX_K + 1];
-  bool ok = true;
+  __shared__ int32_t best_idx[SPEC_MAX_K + 1];  // -1 for an invalid row
   for (int j = lane; j < k1; j += kWave) {
     GPartial* p = part + (b * k1 + j) * (int64_t)nchunks;
     uint64_t bb = 0;
@@ -244,24 +243,27 @@ __global__ __launch_bounds__(64) void k_greedy_tail(int64_t V, int k, int nchunk
       p[c] = zero;
     }
     const uint32_t key = (uint32_t)(bb >> 32);
-    ok &= (fl == 0) && key != 0;
-    best_idx[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)bb);
+    best_idx[j] = (fl == 0 && key != 0) ? (int32_t)(0xFFFFFFFFu - (uint32_t)bb) : -1;
   }
-  int32_t tok = 0;
-  if (lane < k) {
-    tok = tokens[b * k + lane];
-    ok &= (tok >= 0 && (int64_t)tok < V);
-  }
-  const bool all_ok = __ballot(!ok) == 0;
   __syncthreads();
+  // Positions in order up to the first mismatch; only what the walk consults
+  // can make the sequence invalid.
+  bool formed = false, match = false;
+  if (lane < k) {
+    const int32_t tok = tokens[b * k + lane];
+    formed = best_idx[lane] >= 0 && tok >= 0 && (int64_t)tok < V;
+    match = formed && tok == best_idx[lane];
+  }
+  const uint64_t stop = __ballot(lane < k && !match);
+  const uint64_t ill = __ballot(lane < k && !formed);
+  const int n = stop ? (__ffsll((unsigned long long)stop) - 1) : k;
+  const bool valid = n < k ? !((ill >> n) & 1ull) : best_idx[k] >= 0;
   int32_t* out = out_tokens + b * k1;
-  if (!all_ok) {
+  if (!valid) {
     for (int j = lane; j < k1; j += kWave) out[j] = -1;
     if (lane == 0) accepted_len[b] = -1;
     return;
   }
-  const uint64_t mism = __ballot(lane < k && tok != best_idx[lane < k ? lane : 0]);
-  const int n = mism ? (__ffsll((unsigned long long)mism) - 1) : k;
   for (int j = lane; j < k1; j += kWave) {
     int32_t v = -1;
     if (j < n) v = tokens[b * k + j];
@@ -743,34 +745,34 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   }
   block_sync_lds();
 
-  // Ratio test (wave 0, lane j = position j) and first rejection.
+  // Ratio test (wave 0, lane j = position j).  Positions are walked in
+  // order and the first rejection stops the walk: the sequence is invalid
+  // only if an ill-formed position (invalid row or token out of range) comes
+  // before it, or every position passes and the bonus row is invalid.
   if (w == 0) {
-    bool ok = true;
-    for (int t = lane; t < nr; t += kWave) ok &= TS.st[t].valid != 0;
-    int32_t x = 0;
+    bool formed = false, acc = false;
     if (lane < k) {
-      x = A.tokens[b * k + lane];
-      ok &= x >= 0 && (int64_t)x < V;
-    }
-    const bool all_ok = __ballot(!ok) == 0;
-    bool acc = true;
-    if (lane < k) {
-      if (all_ok) {
+      const int32_t x = A.tokens[b * k + lane];
+      formed = TS.st[lane].valid != 0 && TS.st[k + 1 + lane].valid != 0 && x >= 0 &&
+               (int64_t)x < V;
+      float alpha_out = __builtin_nanf("");
+      if (formed) {
         const T* tr = A.map.row<T>(b * nr + lane);
         const T* dr = A.map.row<T>(b * nr + k + 1 + lane);
         const double p = prob_at(Elem<T>::load1(tr + x), TS.st[lane], a);
         const double q = prob_at(Elem<T>::load1(dr + x), TS.st[k + 1 + lane], a);
         const double alpha = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
         acc = (double)A.u[b * (k + 1) + lane] < alpha;
-        if (A.accept_prob) A.accept_prob[b * k + lane] = (float)alpha;
-      } else if (A.accept_prob) {
-        A.accept_prob[b * k + lane] = __builtin_nanf("");
+        alpha_out = (float)alpha;
       }
+      if (A.accept_prob) A.accept_prob[b * k + lane] = alpha_out;
     }
-    const uint64_t rej = __ballot(lane < k && !acc);
+    const uint64_t stop = __ballot(lane < k && !acc);
+    const uint64_t ill = __ballot(lane < k && !formed);
     if (lane == 0) {
-      TS.valid = all_ok ? 1 : 0;
-      TS.n = rej ? (__ffsll((unsigned long long)rej) - 1) : k;
+      const int n = stop ? (__ffsll((unsigned long long)stop) - 1) : k;
+      TS.n = n;
+      TS.valid = (n < k ? !((ill >> n) & 1ull) : TS.st[k].valid != 0) ? 1 : 0;
     }
   }
   block_sync_lds();

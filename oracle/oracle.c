@@ -38,8 +38,16 @@
  *      renormalised over the top-k set, keeps the shortest descending prefix
  *      whose mass reaches top_p, ties at the cut kept;
  *   R12 -inf logits have probability 0; NaN, +inf or a row without a finite
- *      logit make the row, and its sequence, invalid (accepted length -1);
- *   R13 everything is computed in double precision on exactly decoded inputs.
+ *      logit make the row invalid, and a position is ill-formed when one of
+ *      its rows (target and, stochastic, draft) is invalid or its draft token
+ *      lies outside [0, V).  Positions are examined in order and the first
+ *      rejection ends the walk, so a sequence is invalid (accepted length -1)
+ *      only when an ill-formed position comes before any rejection, or every
+ *      candidate passes and the bonus row is invalid; rows past the stop are
+ *      never consulted;
+ *   R13 everything is computed in double precision on exactly decoded inputs;
+ *   R14 alpha is reported for every position, past the stop too, and is NaN
+ *      at an ill-formed position.
  */
 #include "oracle.h"
 
@@ -281,46 +289,45 @@ int orc_verify_stochastic(const void* target, long long t_seq, long long t_pos,
   }
 
   for (int b = 0; b < B; b++) {
-    int valid = 1;
     for (int j = 0; j <= k; j++) {
       decode_row(target, dtype, b * t_seq + j * t_pos, V, l);
       pres[j] = process_logits(l, V, temperature, top_k, top_p,
                                P + (size_t)j * V, scratch);
-      valid &= pres[j].valid;
     }
     for (int j = 0; j < k; j++) {
       decode_row(draft, dtype, b * d_seq + j * d_pos, V, l);
       qres[j] = process_logits(l, V, temperature, top_k, top_p,
                                Q + (size_t)j * V, scratch);
-      valid &= qres[j].valid;
     }
+    /* R14: the ratio test's alpha at every well-formed position. */
     for (int j = 0; j < k; j++) {
       int x = tokens[(size_t)b * k + j];
-      if (x < 0 || x >= V) valid = 0;
-    }
-    int* out = out_tokens + (size_t)b * (k + 1);
-    if (!valid) {
-      accepted_len[b] = -1;
-      for (int j = 0; j <= k; j++) out[j] = -1;
-      if (accept_prob)
-        for (int j = 0; j < k; j++) accept_prob[(size_t)b * k + j] = NAN;
-      if (flags) flags[b] = 0;
-      continue;
-    }
-
-    /* Ratio test at every position; decisions stop at the first rejection. */
-    for (int j = 0; j < k; j++) {
-      int x = tokens[(size_t)b * k + j];
-      alpha[j] = acceptance_probability(P[(size_t)j * V + x], Q[(size_t)j * V + x]);
+      int formed = pres[j].valid && qres[j].valid && x >= 0 && x < V;
+      alpha[j] = formed ? acceptance_probability(P[(size_t)j * V + x],
+                                                 Q[(size_t)j * V + x])
+                        : NAN;
       if (accept_prob) accept_prob[(size_t)b * k + j] = alpha[j];
     }
+    /* Positions in order; the first rejection stops the walk (R12). */
     const float* ub = u + (size_t)b * (k + 1);
-    int n = k;
+    int n = k, valid = 1;
     for (int j = 0; j < k; j++) {
+      if (isnan(alpha[j])) {
+        valid = 0;
+        break;
+      }
       if (!((double)ub[j] < alpha[j])) {
         n = j;
         break;
       }
+    }
+    if (valid && n == k && !pres[k].valid) valid = 0;
+    int* out = out_tokens + (size_t)b * (k + 1);
+    if (!valid) {
+      accepted_len[b] = -1;
+      for (int j = 0; j <= k; j++) out[j] = -1;
+      if (flags) flags[b] = 0;
+      continue;
     }
 
     /* Correction: residual max(0, p - q) at the rejected position, or the
@@ -381,28 +388,30 @@ int orc_verify_greedy(const void* target, long long t_seq, long long t_pos,
     return -1;
   }
   for (int b = 0; b < B; b++) {
-    int valid = 1;
     for (int j = 0; j <= k; j++) {
       decode_row(target, dtype, b * t_seq + j * t_pos, V, l);
       best[j] = first_argmax(l, V);
-      if (best[j] < 0) valid = 0;
     }
+    /* Positions in order up to the first mismatch (R12). */
+    int n = k, valid = 1;
     for (int j = 0; j < k; j++) {
       int x = tokens[(size_t)b * k + j];
-      if (x < 0 || x >= V) valid = 0;
+      if (best[j] < 0 || x < 0 || x >= V) {
+        valid = 0;
+        break;
+      }
+      if (x != best[j]) {
+        n = j;
+        break;
+      }
     }
+    if (valid && n == k && best[k] < 0) valid = 0;
     int* out = out_tokens + (size_t)b * (k + 1);
     if (!valid) {
       accepted_len[b] = -1;
       for (int j = 0; j <= k; j++) out[j] = -1;
       continue;
     }
-    int n = k;
-    for (int j = 0; j < k; j++)
-      if (tokens[(size_t)b * k + j] != best[j]) {
-        n = j;
-        break;
-      }
     accepted_len[b] = n;
     for (int j = 0; j < n; j++) out[j] = tokens[(size_t)b * k + j];
     out[n] = best[n];

@@ -53,8 +53,12 @@ def compare_stochastic(ref, acc, out, ap, rows=None, fp32=True, label=""):
            ref["accept_prob"][mism[:1]]))
     valid = ref["accepted_len"] >= 0
     assert np.array_equal(g_acc[~valid], ref["accepted_len"][~valid])
-    a_ref = ref["accept_prob"][valid]
-    a_gpu = g_ap[valid].astype(np.float64)
+    # alpha is reported at every position and is NaN exactly where the
+    # position is ill-formed
+    nan_ref = np.isnan(ref["accept_prob"])
+    assert np.array_equal(np.isnan(g_ap), nan_ref), label
+    a_ref = ref["accept_prob"][~nan_ref]
+    a_gpu = g_ap[~nan_ref].astype(np.float64)
     # alpha = min(1, p/q) is a probability: 1e-6 absolute for fp32 inputs
     # (plus the fp32 rounding of the reported value), 2e-3 relative for bf16.
     if fp32:

@@ -333,28 +333,61 @@ def pin_bf16_decode(orc):
 
 # ---------------------------------------------------------------------------
 def pin_invalid_inputs(orc):
-    """NaN, +inf, rows without a finite logit and out-of-range draft tokens
-    mark the sequence invalid (accepted length -1); -inf is a mask."""
+    """NaN, +inf and rows without a finite logit make a row invalid, a draft
+    token outside [0, V) makes its position ill-formed, and -inf is only a
+    mask.  The walk over positions stops at the first rejection (the pages'
+    first-rejection stop), so only what it consults before stopping can make
+    the sequence invalid (accepted length -1)."""
     rs = np.random.default_rng(17)
-    B, k, V = 6, 2, 16
+    B, k, V = 10, 2, 16
     t = rs.normal(0, 1, (B, k + 1, V)).astype(np.float32)
     d = (t[:, :k] + rs.normal(0, 1, (B, k, V))).astype(np.float32)
-    toks = np.zeros((B, k), np.int32)
-    t[0, 1, 3] = np.nan
-    t[1, 2, 0] = np.inf
-    d[2, 0, :] = -np.inf
-    toks[3, 1] = V
-    toks[4, 0] = -1
-    t[5, 0, :8] = -np.inf  # masking only: still valid
-    u = np.full((B, k + 1), 0.5, np.float32)
+    # accept every consulted position (u = 0 and p(x) > 0 at the argmax) ...
+    toks = np.argmax(t[:, :k], axis=2).astype(np.int32)
+    u = np.zeros((B, k + 1), np.float32)
+    u[:, k] = 0.5
+    # ... except where a rejection at position 0 is forced: x masked in p
+    reject0 = [1, 3, 7, 9]
+    for b in reject0:
+        t[b, 0, 0] = -np.inf
+        toks[b, 0] = 0
+    t[0, 1, 3] = np.nan          # consulted (position 0 passes): invalid
+    t[1, 1, 3] = np.nan          # past the stop: valid, n = 0
+    d[2, 0, :] = -np.inf         # draft row without a finite logit: invalid
+    toks[3, 1] = V               # out of range past the stop: valid
+    toks[4, 0] = -1              # out of range at position 0: invalid
+    t[5, 0, 8:] = -np.inf        # masking only: valid
+    toks[5, 0] = np.argmax(t[5, 0])
+    t[6, k, 2] = np.inf          # bonus row consulted (all pass): invalid
+    t[7, k, 2] = np.inf          # bonus row not consulted: valid
+    d[8, 1, 5] = np.inf          # draft row at a consulted position: invalid
+    d[9, 1, 5] = np.nan          # draft row past the stop: valid
     r = orc.verify_stochastic(t, d, toks, u)
-    assert list(r["accepted_len"][:5]) == [-1] * 5
-    assert (r["out_tokens"][:5] == -1).all()
-    assert r["accepted_len"][5] >= 0
+    expect = [-1, 0, -1, 0, -1, k, -1, 0, -1, 0]
+    assert list(r["accepted_len"]) == expect, list(r["accepted_len"])
+    for b in range(B):
+        if expect[b] < 0:
+            assert (r["out_tokens"][b] == -1).all()
+        else:
+            n = expect[b]
+            assert 0 <= r["out_tokens"][b, n] < V and (r["out_tokens"][b, n + 1:] == -1).all()
+    # alpha is reported at every position, NaN exactly where it is ill-formed
+    ap = r["accept_prob"]
+    ill = np.zeros((B, k), bool)
+    ill[0, 1] = ill[1, 1] = ill[2, 0] = ill[3, 1] = ill[4, 0] = ill[8, 1] = ill[9, 1] = True
+    assert np.array_equal(np.isnan(ap), ill)
+    assert (ap[reject0, 0] == 0).all()
+    # a rejected position resamples from the residual, which here holds the
+    # positive part of p - q over the unmasked tokens
+    assert r["out_tokens"][1, 0] != 0
+    # greedy walks the same way: mismatch at 0 where the token is not the argmax
     acc, out = orc.verify_greedy(t, toks)
-    assert acc[0] == -1 and acc[1] == -1 and acc[3] == -1 and acc[4] == -1
+    assert list(acc) == [-1, 0, k, 0, -1, k, -1, 0, k, 0], list(acc)
+    assert out[2, k] == np.argmax(t[2, k]) and out[1, 0] == np.argmax(t[1, 0])
     ok, p, _ = orc.process_row(t[5, 0])
-    assert ok and (p[:8] == 0).all() and abs(p.sum() - 1) < 1e-12
+    assert ok and (p[8:] == 0).all() and abs(p.sum() - 1) < 1e-12
+    ok, _, _ = orc.process_row(t[0, 1])
+    assert not ok
 
 
 # ---------------------------------------------------------------------------

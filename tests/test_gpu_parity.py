@@ -251,24 +251,39 @@ def test_unaligned_strides_and_broadcast(dtype):
 @pytest.mark.parametrize("V", [777, 1024])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_masks_and_invalid_rows(dtype, V):
+    """Invalid rows and tokens count only where the walk over positions
+    consults them: before the first rejection, and the bonus row when every
+    position passes."""
     rs = np.random.default_rng(8)
     B, k = 12, 3
     for T, top_k, top_p in [(1.0, 0, 1.0), (1.0, 10, 0.8)]:
         t, d, toks, u = _random_case(rs, B, k, V, dtype, T, top_k, top_p, mask_frac=0.5)
+        tf = workloads.bf16_bits_to_f32(t) if dtype == "bf16" else t
         nan = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
         pinf = np.uint16(0x7F80) if dtype == "bf16" else np.float32(np.inf)
         ninf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
-        t[0, 1, 5] = nan
-        d[1, 2, 9] = pinf
-        t[2, 3, :] = ninf          # bonus row without a finite logit
+        # sequences 0..7 pass every position they reach (token = argmax, u = 0)
+        toks[:8] = np.argmax(tf[:8, :k], axis=2)
+        u[:8, :k] = 0.0
+        t[0, 1, 5] = nan           # consulted target row
+        d[1, 2, 9] = pinf          # consulted draft row
+        t[2, k, :] = ninf          # bonus row without a finite logit, all passed
         toks[3, 1] = V             # token out of range
         toks[4, 0] = -7
-        d[5, 0, 100] = nan         # NaN in a row past ... still invalidates the sequence
+        d[5, 0, 100] = nan
+        # sequences 6, 7 reject position 0 (its token masked in p); what lies
+        # past the stop is never consulted
+        for b in (6, 7):
+            t[b, 0, 0] = ninf
+            toks[b, 0] = 0
+        t[6, 2, 4] = nan
+        toks[7, 2] = V
+        t[7, k, :] = ninf
         acc, out, ap = gpu_stochastic(t, d, toks, u, T, top_k, top_p)
         ref = oracle.verify_stochastic(t, d, toks, u, T, top_k, top_p)
-        assert list(acc[:6]) == [-1] * 6
+        assert list(ref["accepted_len"][:8]) == [-1] * 6 + [0, 0]
+        assert list(acc[:8]) == [-1] * 6 + [0, 0]
         assert (out[:6] == -1).all()
-        assert np.isnan(ap[:6]).all()
         compare_stochastic(ref, acc, out, ap, fp32=(dtype == "f32"), label="masks " + dtype)
         gacc, gout = sv.verify_greedy(to_dev(t), torch.from_numpy(toks).to(DEV))
         torch.cuda.synchronize()

@@ -30,6 +30,10 @@ MUTATIONS = {
     "max logit ignored in the exponent": ("if (l[i] >= thr) z += exp((l[i] - m) / T);",
                                           "if (l[i] >= thr) z += exp((l[i] - m + 0.25) / T);", 1),
     "q = 0 rejects a token p supports": ("return p > 0.0 ? 1.0 : 0.0;", "return 0.0;", 1),
+    "bonus row consulted after a rejection": ("if (valid && n == k && !pres[k].valid) valid = 0;",
+                                              "if (!pres[k].valid) valid = 0;", 1),
+    "ill-formed position past the stop invalidates": ("if (isnan(alpha[j])) {\n        valid = 0;\n        break;\n      }\n      if (!((double)ub[j] < alpha[j])) {\n        n = j;\n        break;\n      }",
+                                                      "if (isnan(alpha[j])) {\n        valid = 0;\n        break;\n      }\n      if (!((double)ub[j] < alpha[j]) && n == k) {\n        n = j;\n      }", 1),
 }
 
 FAST_PINS = [p for p in pins.ALL_PINS if p is not pins.pin_chi_square]
