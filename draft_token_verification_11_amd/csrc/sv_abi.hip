@@ -22,7 +22,7 @@ struct Layout {
   int vpt = 1;       // 8-element groups per thread in split-V kernels
   int nchunks = 1;   // V-chunks per row
   int64_t rows = 0;  // rows processed
-  size_t rowstat_off = 0, part_off = 0, total = 0;
+  size_t rowstat_off = 0, part_off = 0, queue_off = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -60,6 +60,10 @@ Layout make_layout(int op, int64_t B, int64_t k, int64_t V, const spec_sampling_
   if (need_part) {
     L.part_off = off;
     off = align256(off + size_t(L.rows) * size_t(L.nchunks) * 16);
+  }
+  if (op == SPEC_OP_STOCHASTIC) {  // sequence queue of the whole-sequence kernel
+    L.queue_off = off;
+    off = align256(off + 2 * sizeof(uint32_t));
   }
   L.total = off < 256 ? 256 : off;
   return L;
@@ -106,19 +110,28 @@ bool grid_fits(int64_t blocks, int threads) { return blocks >= 1 && blocks * thr
 
 float log2e_over(float T) { return float(1.4426950408889634 / double(T)); }
 
-// Workgroups of the persistent filter: one per CU, a multiple of 8 (one
-// range of rows per XCD), no more than needed.
-int persistent_grid(int64_t rows) {
+int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
-  int64_t g = cus;
+  return cus;
+}
+
+// Workgroups of the persistent filter: one per CU, a multiple of 8 (one
+// range of rows per XCD), no more than needed.
+int persistent_grid(int64_t rows) {
+  int64_t g = device_cus();
   if (rows < g) g = rows;
   g = (g + 7) / 8 * 8;
   return int(g);
 }
+
+// The whole-sequence kernel (rows read in walk order, nothing past the stop)
+// pays off once every CU has several sequences to take from the queue;
+// smaller batches spread their rows over the chip instead.
+constexpr int kSeqPerCu = 2;
 
 constexpr int kPrefetch = 2;  // 16-byte vectors per thread prefetched for the next row
 constexpr int kLoadDepth = 8;  // 16-byte loads in flight per thread in the row stream
@@ -199,6 +212,17 @@ template <typename T, bool VEC>
 struct StochasticRun {
   static void run(const Layout& L, const sv::RowMap& map, int64_t B, int64_t V, float a,
                   const spec_sampling_t& s, sv::TailArgs& args, char* ws, hipStream_t st) {
+    if constexpr (sizeof(T) == 2 && VEC) {
+      const int cus = device_cus();
+      if (B >= int64_t(kSeqPerCu) * cus) {
+        sv::SeqArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
+                      args.accepted_len, args.out_tokens, args.accept_prob,
+                      reinterpret_cast<uint32_t*>(ws + L.queue_off)};
+        hipLaunchKernelGGL((sv::k_verify_seq_bf16<kPrefetch, kLoadDepth>), dim3(unsigned(cus)),
+                           dim3(kFilterThreads), 0, st, A);
+        return;
+      }
+    }
     if (L.filtered) {
       auto* rs = reinterpret_cast<sv::RowStat*>(ws + L.rowstat_off);
       launch_filter<T, VEC>(L, map, V, a, s, rs, st);

@@ -44,6 +44,16 @@ struct Elem<uint16_t> {
   }
 };
 
+// 2^x for a double x <= 0 (or moderately positive), to about 1e-7 relative:
+// the integer part exactly through ldexp, the fraction in [0, 1) through the
+// hardware single-precision exp2.  Needs no double-precision polynomial
+// constants (which a long-lived kernel would otherwise keep in registers).
+__device__ __forceinline__ double exp2_d(double x) {
+  if (!(x > -1100.0)) return 0.0;
+  const double n = __builtin_floor(x);
+  return __builtin_ldexp((double)__builtin_amdgcn_exp2f((float)(x - n)), (int)n);
+}
+
 __device__ __forceinline__ uint4 load16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
@@ -190,6 +200,15 @@ struct OpOr {
   __device__ __forceinline__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; }
 };
 
+// threadIdx.x passed through an empty asm statement: what a helper derives
+// from it is recomputed where it is used instead of being hoisted out of a
+// caller's loop and held in a register for the whole kernel.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Inclusive prefix scan: lane i gets op(x_0, ..., x_i).
 template <typename F, typename Op>
 __device__ __forceinline__ F wave_prefix(F x, F id, Op op) {
@@ -198,7 +217,7 @@ __device__ __forceinline__ F wave_prefix(F x, F id, Op op) {
   x = op(x, Dpp<0x114>::mov(x, id));  // row_shr:4
   x = op(x, Dpp<0x118>::mov(x, id));  // row_shr:8
   const F t0 = bcast(x, 15), t1 = bcast(x, 31), t2 = bcast(x, 47);
-  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  const int row = (opaque_tid() & (kWave - 1)) >> 4;
   const F t01 = op(t0, t1);
   const F t012 = op(t01, t2);
   const F add = row == 0 ? id : (row == 1 ? t0 : (row == 2 ? t01 : t012));
@@ -212,7 +231,7 @@ __device__ __forceinline__ F wave_suffix(F x, F id, Op op) {
   x = op(x, Dpp<0x104>::mov(x, id));  // row_shl:4
   x = op(x, Dpp<0x108>::mov(x, id));  // row_shl:8
   const F t1 = bcast(x, 16), t2 = bcast(x, 32), t3 = bcast(x, 48);
-  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  const int row = (opaque_tid() & (kWave - 1)) >> 4;
   const F t23 = op(t2, t3);
   const F t123 = op(t1, t23);
   const F add = row == 3 ? id : (row == 2 ? t3 : (row == 1 ? t23 : t123));
@@ -256,7 +275,7 @@ __device__ __forceinline__ F block_sum(F x, F* slots) {
   constexpr int NW = NT / kWave;
   x = wave_sum(x);
   block_sync_lds();
-  if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
+  if (const int t = opaque_tid(); (t & (kWave - 1)) == 0) slots[t / kWave] = x;
   block_sync_lds();
   F r = slots[0];
 #pragma unroll
@@ -268,7 +287,7 @@ __device__ __forceinline__ float block_max(float x, float* slots) {
   constexpr int NW = NT / kWave;
   x = wave_max(x);
   block_sync_lds();
-  if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
+  if (const int t = opaque_tid(); (t & (kWave - 1)) == 0) slots[t / kWave] = x;
   block_sync_lds();
   float r = slots[0];
 #pragma unroll
@@ -280,7 +299,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t* slots) {
   constexpr int NW = NT / kWave;
   x = wave_max_u32(x);
   block_sync_lds();
-  if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
+  if (const int t = opaque_tid(); (t & (kWave - 1)) == 0) slots[t / kWave] = x;
   block_sync_lds();
   uint32_t r = slots[0];
 #pragma unroll
@@ -292,7 +311,7 @@ __device__ __forceinline__ uint32_t block_min_u32(uint32_t x, uint32_t* slots) {
   constexpr int NW = NT / kWave;
   x = wave_min_u32(x);
   block_sync_lds();
-  if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
+  if (const int t = opaque_tid(); (t & (kWave - 1)) == 0) slots[t / kWave] = x;
   block_sync_lds();
   uint32_t r = slots[0];
 #pragma unroll
@@ -304,7 +323,7 @@ __device__ __forceinline__ uint32_t block_or(uint32_t x, uint32_t* slots) {
   constexpr int NW = NT / kWave;
   x = wave_or(x);
   block_sync_lds();
-  if ((threadIdx.x & (kWave - 1)) == 0) slots[threadIdx.x / kWave] = x;
+  if (const int t = opaque_tid(); (t & (kWave - 1)) == 0) slots[t / kWave] = x;
   block_sync_lds();
   uint32_t r = slots[0];
 #pragma unroll
@@ -317,10 +336,11 @@ __device__ __forceinline__ uint32_t block_or(uint32_t x, uint32_t* slots) {
 template <int NT, typename F>
 __device__ __forceinline__ F block_incl_suffix(F x, F* slots, F* total) {
   constexpr int NW = NT / kWave;
-  const int w = threadIdx.x / kWave;
+  const int t = opaque_tid();
+  const int w = t / kWave;
   F s = wave_incl_suffix(x);
   block_sync_lds();
-  if ((threadIdx.x & (kWave - 1)) == 0) slots[w] = s;  // wave total
+  if ((t & (kWave - 1)) == 0) slots[w] = s;  // wave total
   block_sync_lds();
   F above = F(0);
   F all = F(0);

@@ -43,6 +43,7 @@ struct GPartial {  // 16 bytes: greedy partial of one V-chunk
   uint32_t pad;
 };
 constexpr uint32_t kFlagBad = 1u;
+constexpr int kDrawChunks = 16;  // chunk sums kept per wave by the residual draw
 
 // Flat row id -> row pointer.  A sequence holds `per_seq` rows: the first
 // `k1` are target rows 0..k1-1, the rest draft rows 0..per_seq-k1-1.
@@ -135,7 +136,7 @@ __device__ __forceinline__ RowStat merge_partials(const Partial* p, int nchunks,
   double z = 0.0;
   if (m > -__builtin_inff()) {
     for (int c = 0; c < nchunks; ++c)
-      if (p[c].m > -__builtin_inff()) z += p[c].s * exp2(((double)p[c].m - (double)m) * (double)a);
+      if (p[c].m > -__builtin_inff()) z += p[c].s * exp2_d(((double)p[c].m - (double)m) * (double)a);
   }
   st.m = m;
   st.thr = -__builtin_inff();
@@ -388,11 +389,12 @@ struct HistScratch {
   double dslot[16];
   uint32_t uslot[16];
   uint32_t tk, tk_entry;
+  RowStat res;  // the row's statistics, as also written to the caller's record
 };
 
 __device__ __forceinline__ void hist_clear(uint32_t* hist) {
   uint4* h4 = reinterpret_cast<uint4*>(hist);
-  for (int i = threadIdx.x; i < 8192; i += 1024) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = opaque_tid(); i < 8192; i += 1024) h4[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // The histogram counts raw bf16 patterns (code c: 16-bit half c & 1 of word
@@ -444,13 +446,18 @@ __device__ __forceinline__ float key_mass(uint32_t key, uint32_t c, float m, flo
 }
 
 // Row statistics from a filled histogram (all 1024 threads).  Returns 0 on
-// success (RowStat written), 1 for an invalid row (written), 2 on counter
-// overflow (nothing written: the caller takes the bisection path).  Leaves
-// the histogram all zero when it returns 0 or 1.
-__device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a, int top_k,
+// success (RowStat written to S.res and, if given, *out), 1 for an invalid
+// row (written), 2 on counter overflow (nothing written: the caller takes the
+// bisection path).  Leaves the histogram all zero when it returns 0 or 1;
+// S.res can be read by every thread on return.
+__device__ __forceinline__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a, int top_k,
                               float top_p, RowStat* out) {
   constexpr int NT = 1024;
-  const int tid = threadIdx.x;
+  // The thread index is made opaque here so that the addresses derived from
+  // it are recomputed for each row instead of being kept live (in registers
+  // the streaming loop needs) across a persistent kernel's row loop.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   uint16_t* c16 = reinterpret_cast<uint16_t*>(hist);
@@ -522,8 +529,10 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
   if (anybad) {
     if (tid == 0) {
       RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
-      *out = st;
+      S.res = st;
+      if (out) *out = st;
     }
+    block_sync_lds();
     clear_listed();
     return 1;
   }
@@ -535,7 +544,8 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
   if (!nzmax) {  // no finite logit (only -inf)
     if (tid == 0) {
       RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
-      *out = st;
+      S.res = st;
+      if (out) *out = st;
     }
     block_sync_lds();
     clear_listed();
@@ -654,7 +664,8 @@ __device__ int hist_row_stats(uint32_t* hist, HistScratch& S, int64_t V, float a
       st.z = z;
       st.valid = 1;
       st.pad[0] = st.pad[1] = st.pad[2] = 0;
-      *out = st;
+      S.res = st;
+      if (out) *out = st;
     }
   }
   block_sync_lds();
@@ -705,18 +716,229 @@ struct TailArgs {
 
 struct TailScratch {
   RowStat st[2 * SPEC_MAX_K + 1];
-  double wtot[16];
+  double csum[8 * kDrawChunks];  // residual-draw chunk sums (512 threads)
   int32_t n, valid, emit;
 };
 
 __device__ __forceinline__ double prob_at(float l, const RowStat& s, float a) {
   if (!(l >= s.thr)) return 0.0;
-  return exp2(((double)l - (double)s.m) * (double)a) / s.z;
+  return exp2_d(((double)l - (double)s.m) * (double)a) / s.z;
+}
+
+// Inverse-CDF draw in ascending vocabulary order from the normalised residual
+// max(0, p - q) of two processed rows, or from p alone (has_q false, or a
+// residual without mass).  All NT threads take part; every thread returns the
+// drawn index.  csum ([NT / 64][kDrawChunks] doubles) and emit_slot are LDS
+// scratch.
+struct DrawStats {  // what the draw needs of a processed row
+  float m, thr;
+  double z;
+};
+
+__device__ __forceinline__ DrawStats draw_stats(const RowStat& s) { return {s.m, s.thr, s.z}; }
+
+// Offset c with p = 2^(l a - c) for a row's processed probabilities:
+// c = m a + log2(z), log2(z) taken as exponent plus log2 of the mantissa
+// (hardware single-precision log2 on [1, 2)).
+__device__ __forceinline__ float prob_offset(float m, double z, float a) {
+  int e = 0;
+  const double f = __builtin_frexp(z, &e);  // z = f 2^e, f in [0.5, 1)
+  return (float)((double)m * (double)a + (double)(e - 1) +
+                 (double)__builtin_amdgcn_logf((float)(2.0 * f)));
+}
+
+template <typename T, bool VEC, int NT>
+__device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const DrawStats sp,
+                                 const DrawStats sq, float a, int64_t V, float u, double* csum,
+                                 int32_t* emit_slot) {
+  constexpr int NW = NT / kWave;
+  constexpr int E = NW * kDrawChunks / kWave;  // chunk entries per lane in the prefix
+  static_assert(E * kWave == NW * kDrawChunks, "chunk table must fill whole lanes");
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & (kWave - 1);
+  const int w = tid / kWave;
+  const float cp = prob_offset(sp.m, sp.z, a), cq = prob_offset(sq.m, sq.z, a);
+  bool resid = has_q;
+  const int64_t nsteps = (V + 511) / 512;
+  const int64_t spw = (nsteps + NW - 1) / NW;
+  const int64_t s0 = (int64_t)w * spw;
+  const int64_t s1 = min(nsteps, s0 + spw);
+  // Each wave's span is cut into at most kDrawChunks chunks of cs steps whose
+  // sums are kept (csum[w][c], zero past the wave's last chunk), so the
+  // crossing is located from the table and one chunk is read again.
+  const int64_t cs = (spw + kDrawChunks - 1) / kDrawChunks;
+
+  // Residual (or p) of the 8 elements of lane `lane` in step s; returns their
+  // sum (fp32 in element order -- the same additions the crossing search
+  // repeats -- widened to fp64).
+  auto residual8 = [&](const float* lp, const float* lq, float* r8) -> double {
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p =
+          lp[i] >= sp.thr ? __builtin_amdgcn_exp2f(__builtin_fmaf(lp[i], a, -cp)) : 0.0f;
+      float r = p;
+      if (resid) {
+        const float q =
+            lq[i] >= sq.thr ? __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i], a, -cq)) : 0.0f;
+        r = fmaxf(p - q, 0.0f);
+      }
+      r8[i] = r;
+      acc += r;
+    }
+    return (double)acc;
+  };
+  // U steps per batch: all their loads are issued before any is used.
+  constexpr int U = sizeof(T) == 2 ? 4 : 2;
+  auto load_batch = [&](int64_t s, Raw8<T>* rp, Raw8<T>* rq) {
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+      const int64_t e = (s + v) * 512 + lane * 8;
+      load8_raw<T, VEC>(prow, e, V, rp[v]);
+      if (resid) load8_raw<T, VEC>(qrow, e, V, rq[v]);
+    }
+  };
+  auto step_values = [&](const Raw8<T>& rp, const Raw8<T>& rq, float* r8) -> double {
+    float lp[8], lq[8];
+    unpack8<T>(rp, lp);
+    if (resid) unpack8<T>(rq, lq);
+    return residual8(lp, lq, r8);
+  };
+
+  // Pass 1: chunk sums; then every wave forms the same prefix over the
+  // table (chunk order = vocabulary order) and locates the crossing.
+  double S = 0.0, inc = 0.0, lsum = 0.0;
+  double ent[E];
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    if (lane < kDrawChunks) csum[w * kDrawChunks + lane] = 0.0;
+    double cacc = 0.0;
+    int ci = 0;
+    int64_t cend = s0 + cs;
+    for (int64_t s = s0; s < s1; s += U) {
+      Raw8<T> rp[U], rq[U];
+      load_batch(s, rp, rq);
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        float r8[8];
+        const double ls = step_values(rp[v], rq[v], r8);
+        if (s + v < s1) {
+          cacc += bcast(wave_incl_scan(ls), kWave - 1);
+          if (s + v + 1 == cend || s + v + 1 == s1) {
+            if (lane == 0) csum[w * kDrawChunks + ci] = cacc;
+            ++ci;
+            cacc = 0.0;
+            cend += cs;
+          }
+        }
+      }
+    }
+    block_sync_lds();
+    lsum = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      ent[e] = csum[lane * E + e];
+      lsum += ent[e];
+    }
+    inc = wave_incl_scan(lsum);
+    S = bcast(inc, kWave - 1);
+    if (S > 0.0 || !resid) break;
+    resid = false;  // a residual without mass falls back to p at that position
+    block_sync_lds();
+  }
+  const double target = (double)u * S;
+  // the first table entry whose running sum exceeds the target; if rounding
+  // leaves none, the last entry with mass
+  int gstar = -1;
+  double cum = 0.0;
+  {
+    const uint64_t hit = __ballot(inc > target);
+    int L;
+    bool crossed = hit != 0;
+    if (crossed) {
+      L = __ffsll((unsigned long long)hit) - 1;
+    } else {
+      const uint64_t pos = __ballot(lsum > 0.0);
+      L = pos ? 63 - __clzll((long long)pos) : 0;
+    }
+    double base = bcast(inc - lsum, L);
+    int epick = -1, elast = 0;
+    double run = base, before = base, before_last = base;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const double x = bcast(ent[e], L);
+      if (x > 0.0) {
+        elast = e;
+        before_last = run;
+      }
+      if (epick < 0 && crossed && run + x > target) {
+        epick = e;
+        before = run;
+      }
+      run += x;
+    }
+    if (epick < 0) {
+      epick = elast;
+      before = before_last;
+    }
+    gstar = L * E + epick;
+    cum = before;
+  }
+  const int wstar = gstar / kDrawChunks, cstar = gstar % kDrawChunks;
+  if (w == wstar) {
+    const int64_t c0 = s0 + (int64_t)cstar * cs, c1 = min(s1, c0 + cs);
+    double wt = 0.0;
+    bool done = false;
+    for (int64_t s = c0; s < c1 && !done; s += U) {
+      Raw8<T> rp[U], rq[U];
+      load_batch(s, rp, rq);
+#pragma unroll
+      for (int v = 0; v < U; ++v) {
+        if (done || s + v >= c1) continue;
+        float r8[8];
+        const double ls = step_values(rp[v], rq[v], r8);
+        const double sinc = wave_incl_scan(ls);
+        const double stot = bcast(sinc, kWave - 1);
+        if (cum + (wt + stot) > target || s + v == c1 - 1) {
+          const uint64_t hit = __ballot(cum + (wt + sinc) > target);
+          const uint64_t pos = __ballot(ls > 0.0);
+          int L;
+          if (hit) {
+            L = __ffsll((unsigned long long)hit) - 1;
+            if (!((pos >> L) & 1ull)) {  // rounding corner: nearest lane with mass
+              const uint64_t below = pos & ((2ull << L) - 1ull);
+              L = below ? 63 - __clzll((long long)below)
+                        : (pos ? __ffsll((unsigned long long)pos) - 1 : L);
+            }
+          } else {
+            L = pos ? 63 - __clzll((long long)pos) : 0;
+          }
+          const double excl = L > 0 ? bcast(sinc, L - 1) : 0.0;
+          if (lane == L) {
+            const double base = cum + (wt + excl);
+            float run = 0.0f;
+            int pick = -1, lastpos = -1;
+            for (int i = 0; i < 8; ++i) {
+              if (r8[i] > 0.0f) lastpos = i;
+              run += r8[i];
+              if (pick < 0 && base + (double)run > target) pick = i;
+            }
+            if (pick < 0 || !(r8[pick] > 0.0f)) pick = lastpos >= 0 ? lastpos : 0;
+            *emit_slot = (int32_t)((s + v) * 512 + lane * 8 + pick);
+          }
+          done = true;
+          continue;
+        }
+        wt += stot;
+      }
+    }
+  }
+  block_sync_lds();
+  return *emit_slot;
 }
 
 template <typename T, bool VEC, int NT>
 __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
-  constexpr int NW = NT / kWave;
   const int k = A.k;
   const int nr = 2 * k + 1;
   const int tid = threadIdx.x;
@@ -785,140 +1007,13 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   const int n = TS.n;
 
   // Residual max(0, p_n - q_n) (n < k) or the bonus row's p_k (n = k).
-  const T* prow = A.map.row<T>(b * nr + n);
   const bool has_q = n < k;
+  const T* prow = A.map.row<T>(b * nr + n);
   const T* qrow = has_q ? A.map.row<T>(b * nr + k + 1 + n) : prow;
-  const RowStat sp = TS.st[n];
-  const RowStat sq = has_q ? TS.st[k + 1 + n] : TS.st[n];
-  const float izp = (float)(1.0 / sp.z), izq = (float)(1.0 / sq.z);
-  bool resid = has_q;
-  const int64_t nsteps = (V + 511) / 512;
-  const int64_t spw = (nsteps + NW - 1) / NW;
-  const int64_t s0 = (int64_t)w * spw;
-  const int64_t s1 = min(nsteps, s0 + spw);
-
-  // Residual (or p) of the 8 elements of lane `lane` in step s; returns their
-  // sum (fp32 in element order -- the same additions the crossing search
-  // repeats -- widened to fp64).
-  auto residual8 = [&](const float* lp, const float* lq, float* r8) -> double {
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = lp[i] >= sp.thr ? __builtin_amdgcn_exp2f((lp[i] - sp.m) * a) * izp : 0.0f;
-      float r = p;
-      if (resid) {
-        const float q = lq[i] >= sq.thr ? __builtin_amdgcn_exp2f((lq[i] - sq.m) * a) * izq : 0.0f;
-        r = fmaxf(p - q, 0.0f);
-      }
-      r8[i] = r;
-      acc += r;
-    }
-    return (double)acc;
-  };
-  // U steps per batch: all their loads are issued before any is used.
-  constexpr int U = sizeof(T) == 2 ? 4 : 2;
-  auto load_batch = [&](int64_t s, Raw8<T>* rp, Raw8<T>* rq) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t e = (s + u) * 512 + lane * 8;
-      load8_raw<T, VEC>(prow, e, V, rp[u]);
-      if (resid) load8_raw<T, VEC>(qrow, e, V, rq[u]);
-    }
-  };
-  auto step_values = [&](const Raw8<T>& rp, const Raw8<T>& rq, float* r8) -> double {
-    float lp[8], lq[8];
-    unpack8<T>(rp, lp);
-    if (resid) unpack8<T>(rq, lq);
-    return residual8(lp, lq, r8);
-  };
-
-  double S = 0.0;
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    double wt = 0.0;
-    for (int64_t s = s0; s < s1; s += U) {
-      Raw8<T> rp[U], rq[U];
-      load_batch(s, rp, rq);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        float r8[8];
-        const double ls = step_values(rp[u], rq[u], r8);
-        if (s + u < s1) wt += bcast(wave_incl_scan(ls), kWave - 1);
-      }
-    }
-    if (lane == 0) TS.wtot[w] = wt;
-    block_sync_lds();
-    S = 0.0;
-    for (int v = 0; v < NW; ++v) S += TS.wtot[v];
-    if (S > 0.0 || !resid) break;
-    resid = false;  // a residual without mass falls back to p at that position
-    block_sync_lds();
-  }
-  const double target = (double)A.u[b * (k + 1) + k] * S;
-  double cum = 0.0;
-  int wstar = -1;
-  for (int v = 0; v < NW; ++v) {
-    if (cum + TS.wtot[v] > target) {
-      wstar = v;
-      break;
-    }
-    cum += TS.wtot[v];
-  }
-  if (wstar < 0) {  // unreachable for u < 1; take the last wave with mass
-    cum = 0.0;
-    for (int v = 0; v < NW; ++v)
-      if (TS.wtot[v] > 0.0) wstar = v;
-    if (wstar < 0) wstar = 0;
-    for (int v = 0; v < wstar; ++v) cum += TS.wtot[v];
-  }
-  if (w == wstar) {
-    double wt = 0.0;
-    bool done = false;
-    for (int64_t s = s0; s < s1 && !done; s += U) {
-      Raw8<T> rp[U], rq[U];
-      load_batch(s, rp, rq);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (done || s + u >= s1) continue;
-        float r8[8];
-        const double ls = step_values(rp[u], rq[u], r8);
-        const double inc = wave_incl_scan(ls);
-        const double stot = bcast(inc, kWave - 1);
-        if (cum + (wt + stot) > target || s + u == s1 - 1) {
-          const uint64_t hit = __ballot(cum + (wt + inc) > target);
-          const uint64_t pos = __ballot(ls > 0.0);
-          int L;
-          if (hit) {
-            L = __ffsll((unsigned long long)hit) - 1;
-            if (!((pos >> L) & 1ull)) {  // rounding corner: nearest lane with mass
-              const uint64_t below = pos & ((2ull << L) - 1ull);
-              L = below ? 63 - __clzll((long long)below)
-                        : (pos ? __ffsll((unsigned long long)pos) - 1 : L);
-            }
-          } else {
-            L = pos ? 63 - __clzll((long long)pos) : 0;
-          }
-          const double excl = L > 0 ? bcast(inc, L - 1) : 0.0;
-          if (lane == L) {
-            const double base = cum + (wt + excl);
-            float run = 0.0f;
-            int pick = -1, lastpos = -1;
-            for (int i = 0; i < 8; ++i) {
-              if (r8[i] > 0.0f) lastpos = i;
-              run += r8[i];
-              if (pick < 0 && base + (double)run > target) pick = i;
-            }
-            if (pick < 0 || !(r8[pick] > 0.0f)) pick = lastpos >= 0 ? lastpos : 0;
-            TS.emit = (int32_t)((s + u) * 512 + lane * 8 + pick);
-          }
-          done = true;
-          continue;
-        }
-        wt += stot;
-      }
-    }
-  }
-  block_sync_lds();
-  const int32_t emitted = TS.emit;
+  const int32_t emitted =
+      residual_draw<T, VEC, NT>(prow, qrow, has_q, draw_stats(TS.st[n]),
+                                draw_stats(has_q ? TS.st[k + 1 + n] : TS.st[n]), a, V,
+                                A.u[b * (k + 1) + k], TS.csum, &TS.emit);
   for (int j = tid; j <= k; j += NT) {
     int32_t v = -1;
     if (j < n) v = A.tokens[b * k + j];
@@ -960,76 +1055,327 @@ struct FilterArgs {
   RowStat* stats;
 };
 
+// Buffer descriptor of one aligned bf16 row's full 16-byte groups: the
+// streaming loads then take one 32-bit VGPR offset and a scalar offset per
+// load in flight, which keeps the address registers out of the way.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint16_t* row, int64_t V) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(row), (short)0,
+                                           (int)((V / 8) * 16), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 rsrc_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                             uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Streams one aligned bf16 row into the (cleared) histogram, D 16-byte loads
+// in flight per thread; the first PF vectors of each thread come from `pf`
+// when pf_ok (prefetched by prefetch_row during the previous row's scan).
+template <int PF, int D>
+__device__ __forceinline__ void hist_count_stream(uint32_t* hist, const uint16_t* row, int64_t V,
+                                                  const uint4 (&pf)[PF], bool pf_ok) {
+  constexpr uint32_t NT = 1024;
+  uint32_t tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // recomputed per row, not held across the caller's loop
+  const uint32_t nfull = (uint32_t)(V / 8);  // full 16-byte groups
+  const uint32_t ngroups = (uint32_t)((V + 7) / 8);
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, V);
+  uint32_t g = tid;
+  if (pf_ok) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const uint32_t gj = tid + (uint32_t)j * NT;
+      if (gj < nfull) {
+        hist_add8(hist, pf[j]);
+      } else {
+        for (uint32_t i = 0; i < 8 && (int64_t)gj * 8 + i < V; ++i) hist_add1(hist, row[gj * 8 + i]);
+      }
+    }
+    g = tid + (uint32_t)PF * NT;
+  }
+  for (; g + (D - 1) * NT < nfull; g += D * NT) {
+    uint4 v[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) v[d] = rsrc_load16(rs, g * 16u, (uint32_t)d * NT * 16u);
+#pragma unroll
+    for (int d = 0; d < D; ++d) hist_add8(hist, v[d]);
+  }
+  for (; g < ngroups; g += NT) {
+    if (g < nfull) {
+      hist_add8(hist, rsrc_load16(rs, g * 16u, 0u));
+    } else {
+      for (uint32_t i = 0; i < 8 && (int64_t)g * 8 + i < V; ++i) hist_add1(hist, row[g * 8 + i]);
+    }
+  }
+}
+
+template <int PF>
+__device__ __forceinline__ void prefetch_row(uint4 (&pf)[PF], const uint16_t* row, int64_t V) {
+  const uint32_t nfull = (uint32_t)(V / 8);
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, V);
+  uint32_t tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const uint32_t g = tid + (uint32_t)j * 1024u;
+    if (g < nfull) pf[j] = rsrc_load16(rs, tid * 16u, (uint32_t)j * 16384u);
+  }
+}
+
 template <bool VEC, int PF, int D>
 __global__ __launch_bounds__(1024) void k_filter_bf16_persistent(FilterArgs F) {
+  static_assert(VEC, "aligned rows only");
   constexpr int NT = 1024;
   __shared__ uint32_t hist[32768];
   __shared__ HistScratch S;
-  const int tid = threadIdx.x;
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int per_xcd = nwg >> 3;  // nwg is a multiple of 8
   const int64_t rx = (F.R + 7) / 8;
   const int64_t r_lo = (int64_t)xcd * rx, r_hi = min(F.R, r_lo + rx);
   const int64_t V = F.V;
-  const int64_t nfull = VEC ? V / 8 : 0;  // full 16-byte groups
 
   uint4 pf[PF];
-  auto prefetch = [&](int64_t r) {
-    if (r < r_hi) {
-      const uint16_t* row = F.map.template row<uint16_t>(r);
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int64_t g = tid + (int64_t)j * NT;
-        if (g < nfull) pf[j] = load16(row + g * 8);
-      }
-    }
-  };
   int64_t r = r_lo + slot;
-  prefetch(r);
+  if (r < r_hi) prefetch_row(pf, F.map.template row<uint16_t>(r), V);
   hist_clear(hist);  // afterwards each row's scan leaves the histogram zero
   for (; r < r_hi; r += per_xcd) {
     const uint16_t* row = F.map.template row<uint16_t>(r);
     block_sync_lds();
-    // count: the prefetched groups, then the rest of the row
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int64_t g = tid + (int64_t)j * NT;
-      if (g < nfull) {
-        hist_add8(hist, pf[j]);
-      } else {
-        for (int i = 0; i < 8 && g * 8 + i < V; ++i) hist_add1(hist, row[g * 8 + i]);
-      }
-    }
-    {
-      const int64_t ngroups = (V + 7) / 8;
-      int64_t g = tid + (int64_t)PF * NT;
-      if (VEC) {
-        // D 16-byte loads in flight per thread
-        for (; g + (D - 1) * NT < nfull; g += D * NT) {
-          uint4 v[D];
-#pragma unroll
-          for (int d = 0; d < D; ++d) v[d] = load16(row + (g + (int64_t)d * NT) * 8);
-#pragma unroll
-          for (int d = 0; d < D; ++d) hist_add8(hist, v[d]);
-        }
-      }
-      for (; g < ngroups; g += NT) {
-        if (g < nfull) {
-          hist_add8(hist, load16(row + g * 8));
-        } else {
-          for (int i = 0; i < 8 && g * 8 + i < V; ++i) hist_add1(hist, row[g * 8 + i]);
-        }
-      }
-    }
+    hist_count_stream<PF, D>(hist, row, V, pf, true);
     block_sync_lds();
-    prefetch(r + per_xcd);  // lands while this row's histogram is scanned
+    // the next row's first vectors land while this row's histogram is scanned
+    if (r + per_xcd < r_hi) prefetch_row(pf, F.map.template row<uint16_t>(r + per_xcd), V);
     if (hist_row_stats(hist, S, V, F.a, F.top_k, F.top_p, F.stats + r) == 2) {
       block_sync_lds();
       filter_row_bisect_call<uint16_t, VEC, NT>(row, V, F.a, F.top_k, F.top_p, F.stats + r,
                                                  S.dslot, S.uslot);
       block_sync_lds();
       hist_clear(hist);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Whole-sequence stochastic verify for large batches of aligned bf16 rows.
+// One persistent workgroup per CU takes sequences from a queue and walks each
+// one's positions in order -- target row j, draft row j, ratio test at j --
+// until the first rejection (or ill-formed position), then draws the
+// correction from the residual of the two rows just read, or, when every
+// position passes, reads the bonus row and draws from it.  Rows past the stop
+// are never read.  When accept_prob is requested every position is processed
+// (alpha is reported past the stop); the decisions are the same.
+struct SeqArgs {
+  RowMap map;
+  int64_t V;
+  int32_t k, B;
+  float a;
+  int32_t top_k;
+  float top_p;
+  const int32_t* tokens;
+  const float* u;
+  int32_t* accepted_len;
+  int32_t* out_tokens;
+  float* accept_prob;
+  uint32_t* queue;  // [2]: zero on entry; the last workgroup out zeroes it again
+};
+
+struct SeqScratch {
+  RowStat st[2 * SPEC_MAX_K + 1];  // statistics of the rows read, by row
+  int32_t tok[SPEC_MAX_K];         // draft tokens of the sequence
+  float uu[SPEC_MAX_K];            // accept draws of the sequence
+  double csum[16 * kDrawChunks];   // residual-draw chunk sums
+  int32_t emit;
+  uint32_t next;      // the sequence taken next
+  int32_t formed, accepted;  // decision at the current position
+};
+
+// Out of line, with scalar arguments, so that its registers do not burden
+// the walk's streaming loop.
+__device__ __forceinline__ int32_t residual_draw_call(const uint16_t* prow, const uint16_t* qrow,
+                                                   bool has_q, float pm, float pthr, double pz,
+                                                   float qm, float qthr, double qz, float a,
+                                                   int64_t V, float u, double* csum,
+                                                   int32_t* emit_slot) {
+  return residual_draw<uint16_t, true, 1024>(prow, qrow, has_q, DrawStats{pm, pthr, pz},
+                                             DrawStats{qm, qthr, qz}, a, V, u, csum, emit_slot);
+}
+
+template <int PF, int D>
+__global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
+  constexpr int NT = 1024;
+  __shared__ uint32_t hist[32768];
+  __shared__ HistScratch S;
+  __shared__ SeqScratch Q;
+  // thread index, opaque so that what derives from it is not held in
+  // registers across the walk
+  auto TID = []() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+  };
+  const int64_t V = A.V;
+  const int k = A.k, k1 = k + 1, nr = 2 * k + 1;
+  const bool all_pos = A.accept_prob != nullptr;
+
+  uint4 pf[PF];
+  const uint16_t* pf_row = nullptr;  // the row whose first vectors pf holds
+  hist_clear(hist);
+  if (TID() == 0) Q.next = atomicAdd(&A.queue[0], 1u);
+  block_sync_lds();
+  uint32_t cur = Q.next;
+  if (cur < (uint32_t)A.B) {
+    pf_row = A.map.template row<uint16_t>((int64_t)cur * nr);
+    prefetch_row(pf, pf_row, V);
+  }
+
+  while (cur < (uint32_t)A.B) {
+    const int64_t b = cur;
+    // the next sequence is taken from the queue late -- before the bonus row
+    // or the correction -- so a workgroup never holds one it cannot start
+    uint32_t grabbed = 0;
+    bool have_next = false;
+    // tokens and uniforms of the positions, published to LDS after the first
+    // row's stream (their loads are back by then)
+    int32_t tok_in = 0;
+    float u_in = 0.0f, lt = 0.0f, ld = 0.0f;
+    if (TID() < k) {
+      tok_in = A.tokens[b * k + TID()];
+      u_in = A.u[b * k1 + TID()];
+    }
+    uint32_t nxt = (uint32_t)A.B;
+    int j = 0, n = -1;
+    bool draft = false, valid = true;
+    for (;;) {
+      const int ridx = draft ? k1 + j : j;
+      const uint16_t* row = A.map.template row<uint16_t>(b * nr + ridx);
+      // count (the prefetched vectors first, when they belong to this row)
+      const bool bonus = !draft && j == k;
+      if (bonus && TID() == 0) grabbed = atomicAdd(&A.queue[0], 1u);
+      block_sync_lds();
+      hist_count_stream<PF, D>(hist, row, V, pf, row == pf_row);
+      if (bonus && TID() == 0) Q.next = grabbed;
+      if (ridx == 0) {
+        if (TID() < k) {
+          Q.tok[TID()] = tok_in;
+          Q.uu[TID()] = u_in;
+        }
+      }
+      if (draft && TID() == j) {
+        // the two logits of the ratio test, back before the scan ends
+        const int32_t x = Q.tok[j];
+        if (x >= 0 && (int64_t)x < V) {
+          lt = __builtin_bit_cast(float, (uint32_t)A.map.template row<uint16_t>(b * nr + j)[x] << 16);
+          ld = __builtin_bit_cast(float, (uint32_t)row[x] << 16);
+        }
+      }
+      block_sync_lds();
+      if (bonus) {
+        nxt = Q.next;
+        have_next = true;
+      }
+      // prefetch the row most likely next: d_j after t_j, t_{j+1} after d_j
+      // (acceptance), the next sequence's t_0 after the bonus row
+      const uint16_t* next_row = nullptr;
+      if (!draft && j < k) next_row = A.map.template row<uint16_t>(b * nr + k1 + j);
+      else if (draft) next_row = A.map.template row<uint16_t>(b * nr + j + 1);
+      else if (nxt < (uint32_t)A.B) next_row = A.map.template row<uint16_t>((int64_t)nxt * nr);
+      pf_row = next_row;
+      if (next_row) prefetch_row(pf, next_row, V);
+      RowStat st;
+      if (hist_row_stats(hist, S, V, A.a, A.top_k, A.top_p, nullptr) == 2) {
+        block_sync_lds();
+        filter_row_bisect_call<uint16_t, true, NT>(row, V, A.a, A.top_k, A.top_p, &S.res, S.dslot,
+                                                    S.uslot);
+        __syncthreads();
+        st = S.res;
+        hist_clear(hist);
+      } else {
+        st = S.res;
+      }
+      if (TID() == 0) Q.st[ridx] = st;
+      if (!draft) {
+        if (j == k) {  // bonus row: every position passed
+          valid = st.valid != 0;
+          n = k;
+          break;
+        }
+        if (!st.valid && !all_pos) {  // ill-formed position before any stop
+          valid = false;
+          n = j;
+          break;
+        }
+        draft = true;
+        continue;
+      }
+      // ratio test at position j (thread j holds its token, uniform, logits)
+      if (TID() == j) {
+        const RowStat st_t = Q.st[j];  // written by thread 0 before a barrier
+        const int32_t my_tok = Q.tok[j];
+        const float my_u = Q.uu[j];
+        const bool formed = st_t.valid && st.valid && my_tok >= 0 && (int64_t)my_tok < V;
+        float alpha_out = __builtin_nanf("");
+        bool acc = false;
+        if (formed) {
+          const double p = prob_at(lt, st_t, A.a);
+          const double q = prob_at(ld, st, A.a);
+          const double alpha = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
+          acc = (double)my_u < alpha;
+          alpha_out = (float)alpha;
+        }
+        if (all_pos) A.accept_prob[b * k + j] = alpha_out;
+        Q.formed = formed ? 1 : 0;
+        Q.accepted = acc ? 1 : 0;
+      }
+      block_sync_lds();
+      const bool formed = Q.formed != 0, acc = Q.accepted != 0;
+      if (n < 0 && !(formed && acc)) {
+        n = j;
+        valid = formed;
+      }
+      draft = false;
+      ++j;
+      if (n >= 0 && (!all_pos || j == k)) break;
+    }
+
+    if (!have_next && TID() == 0) grabbed = atomicAdd(&A.queue[0], 1u);
+    // correction from the residual of the rows at n, or the bonus draw
+    int32_t emitted = -1;
+    if (valid) {
+      const bool has_q = n < k;
+      const uint16_t* prow = A.map.template row<uint16_t>(b * nr + n);
+      const uint16_t* qrow = has_q ? A.map.template row<uint16_t>(b * nr + k1 + n) : prow;
+      block_sync_lds();  // Q.st written by thread 0
+      const RowStat& sp = Q.st[n];
+      const RowStat& sq = Q.st[has_q ? k1 + n : n];
+      emitted = residual_draw_call(prow, qrow, has_q, sp.m, sp.thr, sp.z, sq.m, sq.thr, sq.z, A.a,
+                                   V, A.u[b * k1 + k], Q.csum, &Q.emit);
+    }
+    int32_t* out = A.out_tokens + b * k1;
+    for (int t = TID(); t <= k; t += NT) {
+      int32_t v = -1;
+      if (valid) {
+        if (t < n) v = A.tokens[b * k + t];
+        else if (t == n) v = emitted;
+      }
+      out[t] = v;
+    }
+    if (TID() == 0) A.accepted_len[b] = valid ? n : -1;
+    if (!have_next) {
+      if (TID() == 0) Q.next = grabbed;
+      block_sync_lds();
+      nxt = Q.next;
+    }
+    cur = nxt;
+    block_sync_lds();  // everyone has read Q before the next sequence writes it
+  }
+  // The last workgroup out leaves the queue zero for the next call.
+  if (TID() == 0) {
+    const uint32_t done = atomicAdd(&A.queue[1], 1u);
+    if (done == gridDim.x - 1) {
+      atomicExch(&A.queue[0], 0u);
+      atomicExch(&A.queue[1], 0u);
     }
   }
 }
