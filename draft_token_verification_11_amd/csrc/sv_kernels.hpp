@@ -496,14 +496,14 @@ __device__ __forceinline__ int hist_row_stats(uint32_t* hist, HistScratch& S, in
     S.wbad[wv] = wbad ? 1u : 0u;
   }
   block_sync_lds();
-  uint32_t total = 0, anybad = 0, off = 0, nl = 0;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    total += S.wtot[v];
-    anybad |= S.wbad[v];
-    off += v < wv ? S.wcount[v] : 0u;
-    nl += S.wcount[v];
-  }
+  // lane v < 16 takes wave v's figures: total, validity, list offsets
+  const uint32_t vcount = lane < 16 ? S.wcount[lane] : 0u;
+  const uint32_t vtot = lane < 16 ? S.wtot[lane] : 0u;
+  const bool anybad = __ballot(lane < 16 && S.wbad[lane] != 0) != 0;
+  const uint32_t vincl = wave_incl_scan(vcount);
+  const uint32_t total = wave_sum(vtot);
+  const uint32_t nl = bcast(vincl, 15);
+  const uint32_t off = wv > 0 ? bcast(vincl, wv - 1) : 0u;
   if (cnt != 0) {
     const uint32_t pos = off + (uint32_t)__popcll(ne & ((1ull << lane) - 1ull));
     S.list[pos] = (uint16_t)g;
@@ -600,10 +600,17 @@ __device__ __forceinline__ int hist_row_stats(uint32_t* hist, HistScratch& S, in
       if (lane == 0) S.gmass[i] = gs;
     }
   }
-  const double zk = block_sum<NT>((double)acc, S.dslot);
+  {
+    const double ws = wave_sum((double)acc);
+    if (lane == 0) S.dslot[wv] = ws;
+  }
+  block_sync_lds();  // group masses and wave sums visible to wave 0
 
-  // Wave 0: the top-p cut by cumulative mass from the top.
+  // Wave 0: the normaliser, then the top-p cut by cumulative mass from the top.
   if (wv == 0) {
+    double zk = S.dslot[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) zk += S.dslot[v];
     uint32_t thr_key = tk;
     double z = zk;
     if (use_p) {
@@ -747,7 +754,7 @@ __device__ __forceinline__ float prob_offset(float m, double z, float a) {
                  (double)__builtin_amdgcn_logf((float)(2.0 * f)));
 }
 
-template <typename T, bool VEC, int NT>
+template <typename T, bool VEC, int NT, int U>
 __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const DrawStats sp,
                                  const DrawStats sq, float a, int64_t V, float u, double* csum,
                                  int32_t* emit_slot) {
@@ -790,7 +797,6 @@ __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const
     return (double)acc;
   };
   // U steps per batch: all their loads are issued before any is used.
-  constexpr int U = sizeof(T) == 2 ? 4 : 2;
   auto load_batch = [&](int64_t s, Raw8<T>* rp, Raw8<T>* rq) {
 #pragma unroll
     for (int v = 0; v < U; ++v) {
@@ -1011,7 +1017,7 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   const T* prow = A.map.row<T>(b * nr + n);
   const T* qrow = has_q ? A.map.row<T>(b * nr + k + 1 + n) : prow;
   const int32_t emitted =
-      residual_draw<T, VEC, NT>(prow, qrow, has_q, draw_stats(TS.st[n]),
+      residual_draw<T, VEC, NT, sizeof(T) == 2 ? 4 : 2>(prow, qrow, has_q, draw_stats(TS.st[n]),
                                 draw_stats(has_q ? TS.st[k + 1 + n] : TS.st[n]), a, V,
                                 A.u[b * (k + 1) + k], TS.csum, &TS.emit);
   for (int j = tid; j <= k; j += NT) {
@@ -1198,7 +1204,7 @@ __device__ __forceinline__ int32_t residual_draw_call(const uint16_t* prow, cons
                                                    float qm, float qthr, double qz, float a,
                                                    int64_t V, float u, double* csum,
                                                    int32_t* emit_slot) {
-  return residual_draw<uint16_t, true, 1024>(prow, qrow, has_q, DrawStats{pm, pthr, pz},
+  return residual_draw<uint16_t, true, 1024, 4>(prow, qrow, has_q, DrawStats{pm, pthr, pz},
                                              DrawStats{qm, qthr, qz}, a, V, u, csum, emit_slot);
 }
 
