@@ -744,14 +744,14 @@ struct DrawStats {  // what the draw needs of a processed row
 
 __device__ __forceinline__ DrawStats draw_stats(const RowStat& s) { return {s.m, s.thr, s.z}; }
 
-// Offset c with p = 2^(l a - c) for a row's processed probabilities:
-// c = m a + log2(z), log2(z) taken as exponent plus log2 of the mantissa
-// (hardware single-precision log2 on [1, 2)).
-__device__ __forceinline__ float prob_offset(float m, double z, float a) {
+// log2(z) of a row's normaliser, so that p = 2^((l - m) a - log2 z): the
+// exponent plus log2 of the mantissa (hardware single-precision log2 on
+// [1, 2)).  l - m is exact for the logits of one row, so even huge logits
+// keep their probabilities.
+__device__ __forceinline__ float log2_norm(double z) {
   int e = 0;
   const double f = __builtin_frexp(z, &e);  // z = f 2^e, f in [0.5, 1)
-  return (float)((double)m * (double)a + (double)(e - 1) +
-                 (double)__builtin_amdgcn_logf((float)(2.0 * f)));
+  return (float)((double)(e - 1) + (double)__builtin_amdgcn_logf((float)(2.0 * f)));
 }
 
 template <typename T, bool VEC, int NT, int U>
@@ -765,7 +765,7 @@ __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const
   asm volatile("" : "+v"(tid));
   const int lane = tid & (kWave - 1);
   const int w = tid / kWave;
-  const float cp = prob_offset(sp.m, sp.z, a), cq = prob_offset(sq.m, sq.z, a);
+  const float lzp = log2_norm(sp.z), lzq = log2_norm(sq.z);
   bool resid = has_q;
   const int64_t nsteps = (V + 511) / 512;
   const int64_t spw = (nsteps + NW - 1) / NW;
@@ -783,12 +783,14 @@ __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float p =
-          lp[i] >= sp.thr ? __builtin_amdgcn_exp2f(__builtin_fmaf(lp[i], a, -cp)) : 0.0f;
+      const float p = lp[i] >= sp.thr
+                          ? __builtin_amdgcn_exp2f(__builtin_fmaf(lp[i] - sp.m, a, -lzp))
+                          : 0.0f;
       float r = p;
       if (resid) {
-        const float q =
-            lq[i] >= sq.thr ? __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i], a, -cq)) : 0.0f;
+        const float q = lq[i] >= sq.thr
+                            ? __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i] - sq.m, a, -lzq))
+                            : 0.0f;
         r = fmaxf(p - q, 0.0f);
       }
       r8[i] = r;

@@ -341,6 +341,47 @@ def test_bf16_histogram_overflow_falls_back():
     _process_compare(t.reshape(-1, V), 1.0, 0, 0.9, "process overflow rows", False)
 
 
+@pytest.mark.parametrize("case", ["tiny", "huge", "edges", "zeros"])
+def test_bf16_window_edges(case):
+    """Extreme bf16 codes: many +-0 (and top-k cuts that fall on 0), non-zero
+    magnitudes below 2^-63, values of 2^65 and above (one-hot rows), and the
+    codes 2^-63 and (2 - 2^-7) 2^64 in rows of ordinary logits."""
+    rs = np.random.default_rng(29)
+    B, k, V = 6, 3, 3000
+    t = rs.normal(0, 2, (B, k + 1, V)).astype(np.float32)
+    d = (t[:, :k] + rs.normal(0, 1, (B, k, V))).astype(np.float32)
+    lo, hi = np.float32(2.0 ** -63), np.float32((2 - 2 ** -7) * 2.0 ** 64)
+    if case == "tiny":
+        t[0, :, :5] = 1e-25
+        t[1, 0, 7] = -3e-30
+        d[2, 1, 9] = 2e-22
+    elif case == "huge":
+        t[0, 1, 3] = 1e25
+        d[1, 0, 4] = -5e20
+        t[2, 2, 5] = np.float32(2.0 ** 65)
+        t[3, 0, 6] = -np.float32(2.0 ** 65)
+    elif case == "edges":
+        t[:, :, 0] = lo
+        t[:, :, 1] = -lo
+        t[:, :, 2] = -hi
+        d[:, :, 3] = -hi
+        t[0, 1, 4] = hi
+    else:  # many +-0, and rows whose top-k cut falls on 0
+        t[:, :, ::3] = 0.0
+        t[:, :, 1::6] = -0.0
+        t[3] = -np.abs(t[3])
+        t[3, :, :100] = 0.0
+    tb, db = workloads.to_bf16_bits(t), workloads.to_bf16_bits(d)
+    for T, top_k, top_p in [(1.0, 0, 0.9), (1.0, 50, 1.0), (0.7, 20, 0.8), (1.0, 0, 1.0)]:
+        toks = oracle.sample_drafts(db, rs.random((B, k)), T, top_k, top_p)
+        u = rs.random((B, k + 1)).astype(np.float32)
+        acc, out, ap = gpu_stochastic(tb, db, toks, u, T, top_k, top_p)
+        ref = oracle.verify_stochastic(tb, db, toks, u, T, top_k, top_p)
+        compare_stochastic(ref, acc, out, ap, fp32=False,
+                           label="window %s T=%g k=%d p=%g" % (case, T, top_k, top_p))
+        _process_compare(tb.reshape(-1, V), T, top_k, top_p, "process window %s" % case, False)
+
+
 def test_determinism_and_clean_workspace():
     w = workloads.generate(3, B=8)
     c = w.config
