@@ -108,6 +108,12 @@ int check_workspace(void* ws, size_t bytes, const Layout& L) {
 
 bool grid_fits(int64_t blocks, int threads) { return blocks >= 1 && blocks * threads <= kMaxWorkItems; }
 
+bool row_pass_fits(const Layout& L, int dtype, bool vec) {
+  if (!L.filtered) return grid_fits(L.rows * L.nchunks, kRowThreads);
+  if (dtype == SPEC_DTYPE_BF16 && vec) return true;  // persistent: one workgroup per CU
+  return grid_fits(L.rows, kFilterThreads);
+}
+
 float log2e_over(float T) { return float(1.4426950408889634 / double(T)); }
 
 int device_cus() {
@@ -211,15 +217,15 @@ void dispatch(int dtype, bool vec, Args&&... args) {
 template <typename T, bool VEC>
 struct StochasticRun {
   static void run(const Layout& L, const sv::RowMap& map, int64_t B, int64_t V, float a,
-                  const spec_sampling_t& s, sv::TailArgs& args, char* ws, hipStream_t st) {
+                  const spec_sampling_t& s, sv::TailArgs& args, char* ws, hipStream_t st,
+                  int walk_grid) {
     if constexpr (sizeof(T) == 2 && VEC) {
-      const int cus = device_cus();
-      if (B >= int64_t(kSeqPerCu) * cus) {
+      if (walk_grid > 0) {
         sv::SeqArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
                       args.accepted_len, args.out_tokens, args.accept_prob,
                       reinterpret_cast<uint32_t*>(ws + L.queue_off)};
-        hipLaunchKernelGGL((sv::k_verify_seq_bf16<kPrefetch, kLoadDepth>), dim3(unsigned(cus)),
-                           dim3(kFilterThreads), 0, st, A);
+        hipLaunchKernelGGL((sv::k_verify_seq_bf16<kPrefetch, kLoadDepth>),
+                           dim3(unsigned(walk_grid)), dim3(kFilterThreads), 0, st, A);
         return;
       }
     }
@@ -299,9 +305,12 @@ int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft, const int3
   if (!draft_tokens || !uniforms || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
   const Layout L = make_layout(SPEC_OP_STOCHASTIC, B, k, V, sampling);
   if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
-  if (!grid_fits(L.filtered ? L.rows : L.rows * L.nchunks,
-                 L.filtered ? kFilterThreads : kRowThreads) ||
-      !grid_fits(B, kTailThreads))
+  const bool vec = vec_ok(target) && vec_ok(draft);
+  // the whole-sequence walk: aligned bf16 rows, at least kSeqPerCu sequences per CU
+  const int cus = device_cus();
+  const int walk_grid =
+      (target.dtype == SPEC_DTYPE_BF16 && vec && int64_t(B) >= int64_t(kSeqPerCu) * cus) ? cus : 0;
+  if (!walk_grid && (!row_pass_fits(L, target.dtype, vec) || !grid_fits(B, kTailThreads)))
     return SPEC_ERR_UNSUPPORTED;
 
   sv::RowMap map{target.data, target.seq_stride, target.pos_stride, draft.data, draft.seq_stride,
@@ -317,10 +326,10 @@ int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft, const int3
   args.accepted_len = accepted_len;
   args.out_tokens = out_tokens;
   args.accept_prob = accept_prob;
-  const bool vec = vec_ok(target) && vec_ok(draft);
   (void)hipGetLastError();
   dispatch<StochasticRun>(target.dtype, vec, L, map, int64_t(B), int64_t(V), a, *sampling, args,
-                          static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+                          static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
+                          walk_grid);
   return finish_launch();
 }
 
@@ -356,8 +365,7 @@ int spec_logits_process(spec_logits_t logits, int32_t R, int32_t V, const spec_s
   if ((rc = check_logits(logits, V)) != SPEC_OK) return rc;
   const Layout L = make_layout(SPEC_OP_PROCESS, R, 1, V, sampling);
   if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
-  if (!grid_fits(L.filtered ? L.rows : L.rows * L.nchunks,
-                 L.filtered ? kFilterThreads : kRowThreads))
+  if (!row_pass_fits(L, logits.dtype, vec_ok(logits)) || !grid_fits(L.rows * L.nchunks, kRowThreads))
     return SPEC_ERR_UNSUPPORTED;
   sv::RowMap map{logits.data, logits.pos_stride, 0, logits.data, logits.pos_stride, 0, 1, 1};
   const float a = log2e_over(sampling->temperature);
