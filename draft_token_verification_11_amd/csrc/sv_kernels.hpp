@@ -1206,7 +1206,7 @@ __device__ __forceinline__ int32_t residual_draw_call(const uint16_t* prow, cons
                                                    float qm, float qthr, double qz, float a,
                                                    int64_t V, float u, double* csum,
                                                    int32_t* emit_slot) {
-  return residual_draw<uint16_t, true, 1024, 4>(prow, qrow, has_q, DrawStats{pm, pthr, pz},
+  return residual_draw<uint16_t, true, 1024, 2>(prow, qrow, has_q, DrawStats{pm, pthr, pz},
                                              DrawStats{qm, qthr, qz}, a, V, u, csum, emit_slot);
 }
 
