@@ -91,3 +91,100 @@ def test_walk_law_and_geometric_lengths(top_p):
     note("walk top_p=%g: position 0 chi-square p=%.3g, position 1 p=%.3g, length p=%.3g, beta %.4f"
          % (top_p, p0, p1, pl, beta))
     assert p0 >= 1e-3 and p1 >= 1e-3 and pl >= 1e-3
+
+
+def _pooled_chi(counts, probs, min_expected=5.0):
+    """Chi-square p-value with bins of expected count < min_expected pooled."""
+    n = counts.sum()
+    exp = probs / probs.sum() * n
+    order = np.argsort(exp)
+    c_s, e_s = counts[order].astype(np.float64), exp[order]
+    small = e_s < min_expected
+    cs = np.concatenate([c_s[~small], [c_s[small].sum()]]) if small.any() else c_s
+    es = np.concatenate([e_s[~small], [e_s[small].sum()]]) if small.any() else e_s
+    keep = es > 0
+    return scipy.stats.chisquare(cs[keep], es[keep] * cs[keep].sum() / es[keep].sum())[1]
+
+
+def test_config1_positions_follow_target_law():
+    """Workload 1 (V = 1024, fp32, k = 4): its one sequence's rows broadcast to
+    4 x 10^6 samples (four seeded batches of 10^6) with fresh draft tokens
+    (from q) and uniforms.  The first emitted token follows p_0 and the token
+    at position 1, given it exists, follows p_1 (chi-square over the pooled
+    counts, small bins merged)."""
+    w = workloads.generate(1, B=1)
+    c = w.config
+    k, V = c.k, c.V
+    ps = [oracle.process_row(w.target[0, j], c.temperature, c.top_k, c.top_p)[1] for j in range(k + 1)]
+    qs = [oracle.process_row(w.draft[0, j], c.temperature, c.top_k, c.top_p)[1] for j in range(k)]
+    tt = to_dev(w.target).expand(N, -1, -1)
+    dd = to_dev(w.draft).expand(N, -1, -1)
+    c0 = np.zeros(V, np.int64)
+    c1 = np.zeros(V, np.int64)
+    accepted0 = 0
+    for seed in (3003, 3004, 3005, 3006):
+        rs = np.random.default_rng(seed)
+        toks = np.stack([rs.choice(V, size=N, p=q / q.sum()) for q in qs], axis=1).astype(np.int32)
+        u = rs.random((N, k + 1)).astype(np.float32)
+        acc, out = _verify(tt, dd, toks, u, c.temperature, c.top_k, c.top_p)
+        assert (acc >= 0).all()
+        c0 += np.bincount(out[:, 0], minlength=V)
+        c1 += np.bincount(out[acc >= 1, 1], minlength=V)
+        accepted0 += int((acc >= 1).sum())
+    p0 = _pooled_chi(c0, ps[0])
+    p1 = _pooled_chi(c1, ps[1])
+    beta0 = float(np.minimum(ps[0], qs[0]).sum())
+    rate0 = accepted0 / (4 * N)
+    note("config 1: position 0 chi-square p=%.3g, position 1 p=%.3g, P(accept 0) %.5f vs %.5f"
+         % (p0, p1, rate0, beta0))
+    assert p0 >= 1e-3 and p1 >= 1e-3
+    assert abs(rate0 - beta0) <= 4 * np.sqrt(beta0 * (1 - beta0) / (4 * N))
+
+
+def test_u_grid_law_walk():
+    """Brute force on a tiny vocabulary (4 live tokens in bf16 rows of 8, k =
+    2): every draft string, weighted by its proposal probability, against a
+    midpoint grid of G = 64 points per uniform -- 4.2 M sequences through the
+    whole-sequence walk.  The law of the emitted string matches the exact
+    law of the rule (fractions) within 3 / G, the grid's resolution of the
+    three decision breakpoints a string meets."""
+    from fractions import Fraction
+    from oracle import exact
+
+    k, V, G = 2, 8, 64
+    live = [0, 3, 5, 6]
+    lp = np.full((k + 1, V), -np.inf, np.float32)
+    lq = np.full((k, V), -np.inf, np.float32)
+    lp[0, live] = np.log([0.4, 0.3, 0.2, 0.1])
+    lp[1, live] = np.log([0.1, 0.2, 0.3, 0.4])
+    lp[2, live] = np.log([0.25, 0.25, 0.25, 0.25])
+    lq[0, live] = np.log([0.25, 0.25, 0.3, 0.2])
+    lq[1, live] = np.log([0.4, 0.1, 0.1, 0.4])
+    tb, db = workloads.to_bf16_bits(lp[None]), workloads.to_bf16_bits(lq[None])
+    ps = [oracle.process_row(tb[0, j])[1] for j in range(k + 1)]
+    qs = [oracle.process_row(db[0, j])[1] for j in range(k)]
+    law = exact.output_law([[Fraction(float(x)) for x in p] for p in ps],
+                           [[Fraction(float(x)) for x in q] for q in qs])
+    strings = [(a, b) for a in live for b in live]
+    g = (np.arange(G, dtype=np.float64) + 0.5) / G
+    U = np.stack(np.meshgrid(g, g, g, indexing="ij"), axis=-1).reshape(-1, 3).astype(np.float32)
+    n = len(strings) * len(U)
+    toks = np.repeat(np.array(strings, np.int32), len(U), axis=0)
+    u = np.tile(U, (len(strings), 1))
+    tt = to_dev(tb).expand(n, -1, -1)
+    dd = to_dev(db).expand(n, -1, -1)
+    acc, out = _verify(tt, dd, toks, u)
+    assert (acc >= 0).all()
+    weight = np.repeat([qs[0][a] * qs[1][b] for a, b in strings], len(U)) / len(U)
+    # emitted string (accepted drafts + one token) as one integer, base V + 1
+    emitted = np.where(np.arange(k + 1)[None, :] <= acc[:, None], out + 1, 0).astype(np.int64)
+    code = (emitted * (V + 1) ** np.arange(k + 1)[None, :]).sum(axis=1)
+    keys, inv = np.unique(code, return_inverse=True)
+    mass = np.bincount(inv, weights=weight)
+    enc = lambda t: sum((x + 1) * (V + 1) ** j for j, x in enumerate(t))
+    emp = dict(zip(keys.tolist(), mass.tolist()))
+    err = max(abs(emp.get(enc(key), 0.0) - float(pr)) for key, pr in law.items())
+    extra = sum(v for c, v in emp.items() if c not in {enc(key) for key in law})
+    note("u-grid law: %d strings x %d^3 points, max |empirical - exact| = %.4f (bound %.4f), "
+         "mass outside the exact support %.2g" % (len(strings), G, err, 3 / G, extra))
+    assert err <= 3 / G and extra == 0.0
