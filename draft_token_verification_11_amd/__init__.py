@@ -22,7 +22,8 @@ import threading
 import torch
 
 __all__ = ["lib", "verify_stochastic", "verify_greedy", "logits_process", "workspace_size",
-           "status_string", "SpecError", "library_path"]
+           "verify_stochastic_pooled", "verify_greedy_pooled", "workspace_size_pooled",
+           "tree_branches", "status_string", "SpecError", "library_path"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libspecverify.so")
@@ -79,6 +80,16 @@ def lib():
             L.spec_logits_process.argtypes = [spec_logits_t, i32, i32, P(spec_sampling_t), vp, vp,
                                               vp, sz, vp]
             L.spec_logits_process.restype = ctypes.c_int
+            L.spec_workspace_size_pooled.argtypes = [i32, i32, i32, i32, i32, i32,
+                                                     P(spec_sampling_t)]
+            L.spec_workspace_size_pooled.restype = sz
+            L.spec_verify_stochastic_pooled.argtypes = [spec_logits_t, i32, vp, spec_logits_t, i32,
+                                                        vp, vp, vp, i32, i32, i32,
+                                                        P(spec_sampling_t), vp, vp, vp, vp, sz, vp]
+            L.spec_verify_stochastic_pooled.restype = ctypes.c_int
+            L.spec_verify_greedy_pooled.argtypes = [spec_logits_t, i32, vp, vp, i32, i32, i32, vp,
+                                                    vp, vp, sz, vp]
+            L.spec_verify_greedy_pooled.restype = ctypes.c_int
             L.spec_status_string.argtypes = [ctypes.c_int]
             L.spec_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -240,3 +251,147 @@ def logits_process(logits: torch.Tensor, *, temperature: float = 1.0, top_k: int
     if probs is not None:
         out["probs"] = probs
     return out
+
+
+# ---------------------------------------------------------------------------
+# Pooled rows: sequences (the branches of one request, the root-to-leaf paths
+# of a candidate tree) that share target or draft rows name them in a row pool
+# through int32 maps; each shared row is stored and processed once.
+
+
+def workspace_size_pooled(op: int, n_target_rows: int, n_draft_rows: int, B: int, k: int, V: int,
+                          temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0) -> int:
+    s = _sampling(temperature, top_k, top_p)
+    return int(lib().spec_workspace_size_pooled(int(op), int(n_target_rows), int(n_draft_rows),
+                                                int(B), int(k), int(V), ctypes.byref(s)))
+
+
+def _pool(t: torch.Tensor) -> spec_logits_t:
+    if t.dim() != 2 or not t.is_cuda or t.stride(1) != 1:
+        raise ValueError("a row pool must be a device tensor [P][V] with a contiguous last axis")
+    return spec_logits_t(t.data_ptr(), _dtype_code(t), 0, 0, t.stride(0))
+
+
+def _row_map(m, shape, dev):
+    if m is None:
+        return None
+    m = m.to(device=dev, dtype=torch.int32).contiguous()
+    if tuple(m.shape) != shape:
+        raise ValueError("row map must be %s, got %s" % (shape, tuple(m.shape)))
+    return m
+
+
+def verify_stochastic_pooled(target_pool: torch.Tensor, draft_pool: torch.Tensor,
+                             draft_tokens: torch.Tensor, uniforms: torch.Tensor, *,
+                             target_map: torch.Tensor | None = None,
+                             draft_map: torch.Tensor | None = None, temperature: float = 1.0,
+                             top_k: int = 0, top_p: float = 1.0,
+                             return_accept_prob: bool = False, out=None,
+                             workspace: torch.Tensor | None = None, stream=None):
+    """Stochastic verify over pooled rows.  target_pool [Pt][V] and
+    draft_pool [Pd][V] (same dtype); target_map [B][k+1] and draft_map [B][k]
+    int32 name each sequence's rows in the pools (None: row b (k+1) + j, row
+    b k + j).  A map entry outside its pool makes that row ill-formed.
+    Otherwise as verify_stochastic."""
+    B, k = draft_tokens.shape
+    Pt, V = target_pool.shape
+    Pd = draft_pool.shape[0]
+    if draft_pool.shape[1] != V:
+        raise ValueError("target and draft pools disagree on V")
+    tgt, drf = _pool(target_pool), _pool(draft_pool)
+    dev = target_pool.device
+    tmap = _row_map(target_map, (B, k + 1), dev)
+    dmap = _row_map(draft_map, (B, k), dev)
+    tokens = draft_tokens.to(device=dev, dtype=torch.int32).contiguous()
+    u = uniforms.to(device=dev, dtype=torch.float32).contiguous()
+    if tuple(u.shape) != (B, k + 1):
+        raise ValueError("uniforms must be [B][k+1]")
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+        ap = torch.empty((B, k), dtype=torch.float32, device=dev) if return_accept_prob else None
+    else:
+        acc, toks, ap = out
+    s = _sampling(temperature, top_k, top_p)
+    need = lib().spec_workspace_size_pooled(SPEC_OP_STOCHASTIC, Pt, Pd, B, k, V, ctypes.byref(s))
+    if need == 0:
+        _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size_pooled")
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    rc = lib().spec_verify_stochastic_pooled(
+        tgt, Pt, tmap.data_ptr() if tmap is not None else None, drf, Pd,
+        dmap.data_ptr() if dmap is not None else None, tokens.data_ptr(), u.data_ptr(), B, k, V,
+        ctypes.byref(s), acc.data_ptr(), toks.data_ptr(), ap.data_ptr() if ap is not None else None,
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "spec_verify_stochastic_pooled")
+    return (acc, toks, ap) if return_accept_prob else (acc, toks)
+
+
+def verify_greedy_pooled(target_pool: torch.Tensor, draft_tokens: torch.Tensor, *,
+                         target_map: torch.Tensor | None = None, out=None,
+                         workspace: torch.Tensor | None = None, stream=None):
+    """Greedy verify over a pooled target [Pt][V] with target_map [B][k+1]
+    (None: row b (k+1) + j).  Returns (accepted_len [B], out_tokens [B][k+1])."""
+    B, k = draft_tokens.shape
+    Pt, V = target_pool.shape
+    tgt = _pool(target_pool)
+    dev = target_pool.device
+    tmap = _row_map(target_map, (B, k + 1), dev)
+    tokens = draft_tokens.to(device=dev, dtype=torch.int32).contiguous()
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    else:
+        acc, toks = out
+    need = lib().spec_workspace_size_pooled(SPEC_OP_GREEDY, Pt, 0, B, k, V, None)
+    if need == 0:
+        _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size_pooled")
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    rc = lib().spec_verify_greedy_pooled(tgt, Pt, tmap.data_ptr() if tmap is not None else None,
+                                         tokens.data_ptr(), B, k, V, acc.data_ptr(),
+                                         toks.data_ptr(), ws.data_ptr(),
+                                         ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "spec_verify_greedy_pooled")
+    return acc, toks
+
+
+def tree_branches(parents, tokens, leaves=None):
+    """Branches of a parent-pointer candidate tree, for the pooled calls.
+
+    Node 0 is the root (the last token already accepted); node i > 0 holds
+    the drafted token ``tokens[i]`` and its parent ``parents[i] < i``.  Row i
+    of the target pool (of the draft pool) holds the target's (the
+    proposer's) logits for the token after the path root..i.  Every leaf (by
+    default, every node without children) must lie at the same depth k >= 1.
+
+    Returns (draft_tokens [B][k], target_map [B][k+1], draft_map [B][k]) as
+    int32 CPU tensors, one row per leaf: the path root = n_0, n_1, .., n_k =
+    leaf gives draft token j = tokens[n_{j+1}], target row j = n_j (row k the
+    bonus row) and draft row j = n_j."""
+    par = [int(x) for x in (parents.tolist() if hasattr(parents, "tolist") else parents)]
+    tok = [int(x) for x in (tokens.tolist() if hasattr(tokens, "tolist") else tokens)]
+    N = len(par)
+    if N < 2 or len(tok) != N or par[0] != -1:
+        raise ValueError("a tree needs a root (parent -1) and at least one child")
+    for i in range(1, N):
+        if not 0 <= par[i] < i:
+            raise ValueError("node %d: parent must precede it" % i)
+    if leaves is None:
+        has_child = [False] * N
+        for i in range(1, N):
+            has_child[par[i]] = True
+        leaves = [i for i in range(1, N) if not has_child[i]]
+    paths = []
+    for leaf in leaves:
+        leaf = int(leaf)
+        if not 0 < leaf < N:
+            raise ValueError("leaf %d is not a node below the root" % leaf)
+        path = [leaf]
+        while path[-1] != 0:
+            path.append(par[path[-1]])
+        paths.append(path[::-1])
+    k = len(paths[0]) - 1
+    if any(len(p) - 1 != k for p in paths):
+        raise ValueError("every leaf must lie at the same depth")
+    node_map = torch.tensor(paths, dtype=torch.int32)
+    draft_tokens = torch.tensor([[tok[n] for n in p[1:]] for p in paths], dtype=torch.int32)
+    return draft_tokens, node_map, node_map[:, :k].contiguous()

@@ -69,6 +69,41 @@ Layout make_layout(int op, int64_t B, int64_t k, int64_t V, const spec_sampling_
   return L;
 }
 
+// Pooled rows: the row passes run over the pools (nt target rows, then nd
+// draft rows; greedy: the nt target rows).  The row-statistics region always
+// exists: the whole-sequence walk keeps the target pool's statistics there.
+Layout make_pooled_layout(int op, int64_t nt, int64_t nd, int64_t V, const spec_sampling_t* s) {
+  Layout L;
+  const bool greedy = op == SPEC_OP_GREEDY;
+  L.rows = greedy ? nt : nt + nd;
+  L.filtered = !greedy && is_filtered(*s, V);
+  L.vpt = pick_vpt(L.rows, V);
+  L.nchunks = int((V + chunk_elems(L.vpt) - 1) / chunk_elems(L.vpt));
+  size_t off = 0;
+  if (!greedy) {
+    L.rowstat_off = off;
+    off = align256(off + size_t(L.rows) * sizeof(sv::RowStat));
+  }
+  if (!L.filtered) {
+    L.part_off = off;
+    off = align256(off + size_t(L.rows) * size_t(L.nchunks) * 16);
+  }
+  if (!greedy) {
+    L.queue_off = off;
+    off = align256(off + 2 * sizeof(uint32_t));
+  }
+  L.total = off < 256 ? 256 : off;
+  return L;
+}
+
+int check_pools(int64_t nt, int64_t nd, const int32_t* tmap, const int32_t* dmap, int64_t B,
+                int64_t k, bool need_draft) {
+  if (nt < 1 || (need_draft && nd < 1)) return SPEC_ERR_INVALID_ARG;
+  if (!tmap && nt < B * (k + 1)) return SPEC_ERR_INVALID_ARG;
+  if (need_draft && !dmap && nd < B * k) return SPEC_ERR_INVALID_ARG;
+  return SPEC_OK;
+}
+
 size_t elem_size(int dtype) { return dtype == SPEC_DTYPE_BF16 ? 2 : 4; }
 
 int check_logits(const spec_logits_t& t, int64_t V) {
@@ -223,8 +258,8 @@ struct StochasticRun {
       if (walk_grid > 0) {
         sv::SeqArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
                       args.accepted_len, args.out_tokens, args.accept_prob,
-                      reinterpret_cast<uint32_t*>(ws + L.queue_off)};
-        hipLaunchKernelGGL((sv::k_verify_seq_bf16<kPrefetch, kLoadDepth>),
+                      reinterpret_cast<uint32_t*>(ws + L.queue_off), nullptr};
+        hipLaunchKernelGGL((sv::k_verify_seq_bf16<kPrefetch, kLoadDepth, false>),
                            dim3(unsigned(walk_grid)), dim3(kFilterThreads), 0, st, A);
         return;
       }
@@ -267,6 +302,52 @@ struct ProcessRun {
     hipLaunchKernelGGL(sv::k_process_stats, dim3(unsigned((L.rows + 255) / 256)), dim3(256), 0, st,
                        L.rows, L.nchunks, a, part, rs, row_stats);
     if (probs) launch_probs<T, VEC>(L, map, V, a, rs, probs, st);
+  }
+};
+
+template <typename T, bool VEC>
+struct PooledStochasticRun {
+  static void run(const Layout& L, const sv::RowMap& map, int64_t B, int64_t V, float a,
+                  const spec_sampling_t& s, sv::TailArgs& args, char* ws, hipStream_t st,
+                  int walk_grid) {
+    auto* rs = reinterpret_cast<sv::RowStat*>(ws + L.rowstat_off);
+    int64_t clear_bytes = 0;
+    if constexpr (sizeof(T) == 2 && VEC) {
+      if (walk_grid > 0) {
+        // target pool statistics first, then the walk over the draft rows
+        const int64_t nt = map.nt;
+        sv::FilterArgs F{map, V, nt, a, s.top_k, s.top_p, rs};
+        hipLaunchKernelGGL((sv::k_filter_bf16_persistent<true, kPrefetch, kLoadDepth>),
+                           dim3(persistent_grid(nt)), dim3(kFilterThreads), 0, st, F);
+        sv::SeqArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
+                      args.accepted_len, args.out_tokens, args.accept_prob,
+                      reinterpret_cast<uint32_t*>(ws + L.queue_off), rs};
+        hipLaunchKernelGGL((sv::k_verify_seq_bf16<kPrefetch, kLoadDepth, true>),
+                           dim3(unsigned(walk_grid)), dim3(kFilterThreads), 0, st, A);
+        clear_bytes = nt * int64_t(sizeof(sv::RowStat));
+      }
+    }
+    if (clear_bytes == 0) {
+      if (L.filtered) {
+        launch_filter<T, VEC>(L, map, V, a, s, rs, st);
+        args.rowstat = rs;
+        args.part = nullptr;
+        clear_bytes = L.rows * int64_t(sizeof(sv::RowStat));
+      } else {
+        auto* part = reinterpret_cast<sv::Partial*>(ws + L.part_off);
+        launch_partials<T, VEC>(L, map, V, a, part, st);
+        args.rowstat = nullptr;
+        args.part = part;
+        clear_bytes = L.rows * L.nchunks * 16;
+      }
+      args.nchunks = L.nchunks;
+      launch_tail<T, VEC>(B, args, st);
+    }
+    // shared records are cleared once every sequence has read them
+    char* base = args.part ? ws + L.part_off : ws + L.rowstat_off;
+    const int64_t words = (clear_bytes + 15) / 16;
+    hipLaunchKernelGGL(sv::k_clear, dim3(unsigned((words + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<uint4*>(base), words);
   }
 };
 
@@ -350,7 +431,7 @@ int spec_verify_greedy(spec_logits_t target, const int32_t* draft_tokens, int32_
   auto st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   dispatch<GreedyRun>(target.dtype, vec_ok(target), L, map, int64_t(V), part, st);
-  hipLaunchKernelGGL(sv::k_greedy_tail, dim3(unsigned(B)), dim3(64), 0, st, int64_t(V), k,
+  hipLaunchKernelGGL(sv::k_greedy_tail, dim3(unsigned(B)), dim3(64), 0, st, map, int64_t(V), k,
                      L.nchunks, draft_tokens, part, accepted_len, out_tokens);
   return finish_launch();
 }
@@ -377,6 +458,101 @@ int spec_logits_process(spec_logits_t logits, int32_t R, int32_t V, const spec_s
   const int64_t words = int64_t(L.total / 16);
   hipLaunchKernelGGL(sv::k_clear, dim3(unsigned((words + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<uint4*>(workspace), words);
+  return finish_launch();
+}
+
+size_t spec_workspace_size_pooled(int32_t op, int32_t n_target_rows, int32_t n_draft_rows,
+                                  int32_t B, int32_t k, int32_t V,
+                                  const spec_sampling_t* sampling) {
+  if (op != SPEC_OP_STOCHASTIC && op != SPEC_OP_GREEDY) return 0;
+  if (check_sizes(B, k, V, true) != SPEC_OK) return 0;
+  const bool greedy = op == SPEC_OP_GREEDY;
+  if (n_target_rows < 1 || (!greedy && n_draft_rows < 1)) return 0;
+  spec_sampling_t plain = {1.0f, 0, 1.0f};
+  if (!greedy) {
+    if (check_sampling(sampling) != SPEC_OK) return 0;
+  } else {
+    sampling = &plain;
+  }
+  return make_pooled_layout(op, n_target_rows, greedy ? 0 : n_draft_rows, V, sampling).total;
+}
+
+int spec_verify_stochastic_pooled(spec_logits_t target_pool, int32_t n_target_rows,
+                                  const int32_t* target_map, spec_logits_t draft_pool,
+                                  int32_t n_draft_rows, const int32_t* draft_map,
+                                  const int32_t* draft_tokens, const float* uniforms,
+                                  int32_t B, int32_t k, int32_t V,
+                                  const spec_sampling_t* sampling, int32_t* accepted_len,
+                                  int32_t* out_tokens, float* accept_prob, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_sizes(B, k, V, true)) != SPEC_OK) return rc;
+  if ((rc = check_sampling(sampling)) != SPEC_OK) return rc;
+  if ((rc = check_pools(n_target_rows, n_draft_rows, target_map, draft_map, B, k, true)) != SPEC_OK)
+    return rc;
+  target_pool.seq_stride = target_pool.pos_stride;  // pool row r at data + r * pos_stride
+  draft_pool.seq_stride = draft_pool.pos_stride;
+  if ((rc = check_logits(target_pool, V)) != SPEC_OK) return rc;
+  if ((rc = check_logits(draft_pool, V)) != SPEC_OK) return rc;
+  if (target_pool.dtype != draft_pool.dtype) return SPEC_ERR_INVALID_ARG;
+  if (!draft_tokens || !uniforms || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
+  const Layout L = make_pooled_layout(SPEC_OP_STOCHASTIC, n_target_rows, n_draft_rows, V, sampling);
+  if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
+  const bool vec = vec_ok(target_pool) && vec_ok(draft_pool);
+  const int cus = device_cus();
+  const int walk_grid =
+      (target_pool.dtype == SPEC_DTYPE_BF16 && vec && int64_t(B) >= int64_t(kSeqPerCu) * cus) ? cus
+                                                                                               : 0;
+  if (!walk_grid && (!row_pass_fits(L, target_pool.dtype, vec) || !grid_fits(B, kTailThreads)))
+    return SPEC_ERR_UNSUPPORTED;
+
+  sv::RowMap map{target_pool.data, 0, target_pool.pos_stride, draft_pool.data, 0,
+                 draft_pool.pos_stride, 2 * k + 1, k + 1, n_target_rows, n_draft_rows,
+                 target_map, draft_map};
+  sv::TailArgs args{};
+  args.map = map;
+  args.V = V;
+  args.k = k;
+  args.a = log2e_over(sampling->temperature);
+  args.tokens = draft_tokens;
+  args.u = uniforms;
+  args.accepted_len = accepted_len;
+  args.out_tokens = out_tokens;
+  args.accept_prob = accept_prob;
+  (void)hipGetLastError();
+  dispatch<PooledStochasticRun>(target_pool.dtype, vec, L, map, int64_t(B), int64_t(V), args.a,
+                                *sampling, args, static_cast<char*>(workspace),
+                                static_cast<hipStream_t>(stream), walk_grid);
+  return finish_launch();
+}
+
+int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
+                              const int32_t* target_map, const int32_t* draft_tokens,
+                              int32_t B, int32_t k, int32_t V, int32_t* accepted_len,
+                              int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  int rc;
+  if ((rc = check_sizes(B, k, V, true)) != SPEC_OK) return rc;
+  if ((rc = check_pools(n_target_rows, 0, target_map, nullptr, B, k, false)) != SPEC_OK) return rc;
+  target_pool.seq_stride = target_pool.pos_stride;
+  if ((rc = check_logits(target_pool, V)) != SPEC_OK) return rc;
+  if (!draft_tokens || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
+  const spec_sampling_t plain = {1.0f, 0, 1.0f};
+  const Layout L = make_pooled_layout(SPEC_OP_GREEDY, n_target_rows, 0, V, &plain);
+  if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
+  if (!grid_fits(L.rows * L.nchunks, kRowThreads) || !grid_fits(B, 64)) return SPEC_ERR_UNSUPPORTED;
+  sv::RowMap map{target_pool.data, 0, target_pool.pos_stride, target_pool.data, 0,
+                 target_pool.pos_stride, k + 1, k + 1, n_target_rows, 0, target_map, nullptr};
+  auto* part = reinterpret_cast<sv::GPartial*>(static_cast<char*>(workspace) + L.part_off);
+  auto st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  dispatch<GreedyRun>(target_pool.dtype, vec_ok(target_pool), L, map, int64_t(V), part, st);
+  hipLaunchKernelGGL(sv::k_greedy_tail, dim3(unsigned(B)), dim3(64), 0, st, map, int64_t(V), k,
+                     L.nchunks, draft_tokens, part, accepted_len, out_tokens);
+  // the pooled partials are shared by sequences: cleared after the tail
+  const int64_t words = L.rows * L.nchunks;  // 16 bytes each
+  hipLaunchKernelGGL(sv::k_clear, dim3(unsigned((words + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint4*>(part), words);
   return finish_launch();
 }
 

@@ -45,8 +45,18 @@ struct GPartial {  // 16 bytes: greedy partial of one V-chunk
 constexpr uint32_t kFlagBad = 1u;
 constexpr int kDrawChunks = 16;  // chunk sums kept per wave by the residual draw
 
-// Flat row id -> row pointer.  A sequence holds `per_seq` rows: the first
-// `k1` are target rows 0..k1-1, the rest draft rows 0..per_seq-k1-1.
+// Rows of a call.  Dense layout (nt == 0): a sequence holds `per_seq` flat
+// rows, the first `k1` its target rows 0..k1-1 at (t_seq, t_pos), the rest
+// its draft rows at (d_seq, d_pos); flat row r = b per_seq + w.
+//
+// Pooled layout (nt > 0): rows shared by several sequences (the branches of
+// one request, the prefix nodes of a candidate tree) live once in a target
+// pool of nt rows and a draft pool of nd rows, each at its row stride
+// (t_pos, d_pos).  Target row j of sequence b is pool row tmap[b k1 + j]
+// (b k1 + j without a map), draft row j pool row dmap[b k + j] (b k + j
+// without a map).  The row passes number the target pool 0..nt-1 and the
+// draft pool nt..nt+nd-1; a map entry outside its pool names no row (sidx
+// -1) and makes that row ill-formed.
 struct RowMap {
   const void* tgt;
   int64_t t_seq, t_pos;
@@ -54,12 +64,40 @@ struct RowMap {
   int64_t d_seq, d_pos;
   int32_t per_seq;
   int32_t k1;
+  int32_t nt = 0, nd = 0;
+  const int32_t* tmap = nullptr;
+  const int32_t* dmap = nullptr;
+
+  // flat row r of a row pass
   template <typename T>
   __device__ __forceinline__ const T* row(int64_t r) const {
+    if (nt > 0) {
+      if (r < nt) return reinterpret_cast<const T*>(tgt) + r * t_pos;
+      return reinterpret_cast<const T*>(drf) + (r - nt) * d_pos;
+    }
     const int64_t b = r / per_seq;
     const int64_t w = r - b * per_seq;
     if (w < k1) return reinterpret_cast<const T*>(tgt) + b * t_seq + w * t_pos;
     return reinterpret_cast<const T*>(drf) + b * d_seq + (w - k1) * d_pos;
+  }
+  // flat row (index of the row's statistics) of slot w of sequence b (w < k1:
+  // target row w, else draft row w - k1); -1 for a map entry outside its pool
+  __device__ __forceinline__ int64_t sidx(int64_t b, int w) const {
+    if (nt == 0) return b * per_seq + w;
+    if (w < k1) {
+      const int64_t i = tmap ? (int64_t)tmap[b * k1 + w] : b * k1 + w;
+      return (i >= 0 && i < nt) ? i : -1;
+    }
+    const int k = k1 - 1;
+    const int64_t i = dmap ? (int64_t)dmap[b * k + (w - k1)] : b * k + (w - k1);
+    return (i >= 0 && i < nd) ? nt + i : -1;
+  }
+  // the row of slot w of sequence b (flat row 0 when its map entry is bad:
+  // readable, and never used for a decision)
+  template <typename T>
+  __device__ __forceinline__ const T* at(int64_t b, int w) const {
+    const int64_t r = sidx(b, w);
+    return row<T>(r < 0 ? 0 : r);
   }
 };
 
@@ -220,8 +258,9 @@ __global__ __launch_bounds__(256) void k_greedy_partials(RowMap map, int64_t V, 
 }
 
 // One wave per sequence: merge each target row's greedy partials, compare
-// with the drafts, stop at the first mismatch, emit, clear the partials.
-__global__ __launch_bounds__(64) void k_greedy_tail(int64_t V, int k, int nchunks,
+// with the drafts, stop at the first mismatch, emit.  Dense partials are
+// cleared here; pooled ones (shared by sequences) by a pass after the tail.
+__global__ __launch_bounds__(64) void k_greedy_tail(RowMap map, int64_t V, int k, int nchunks,
                                                     const int32_t* __restrict__ tokens,
                                                     GPartial* __restrict__ part,
                                                     int32_t* __restrict__ accepted_len,
@@ -229,9 +268,15 @@ __global__ __launch_bounds__(64) void k_greedy_tail(int64_t V, int k, int nchunk
   const int64_t b = blockIdx.x;
   const int lane = threadIdx.x;
   const int k1 = k + 1;
+  const bool pooled = map.nt > 0;
   __shared__ int32_t best_idx[SPEC_MAX_K + 1];  // -1 for an invalid row
   for (int j = lane; j < k1; j += kWave) {
-    GPartial* p = part + (b * k1 + j) * (int64_t)nchunks;
+    const int64_t r = map.sidx(b, j);
+    if (r < 0) {
+      best_idx[j] = -1;
+      continue;
+    }
+    GPartial* p = part + r * (int64_t)nchunks;
     uint64_t bb = 0;
     uint32_t fl = 0;
     for (int c = 0; c < nchunks; ++c) {
@@ -239,9 +284,11 @@ __global__ __launch_bounds__(64) void k_greedy_tail(int64_t V, int k, int nchunk
       if (p[c].key != 0 && cand > bb) bb = cand;
       fl |= p[c].flags;
     }
-    for (int c = 0; c < nchunks; ++c) {
-      GPartial zero = {0u, 0, 0u, 0u};
-      p[c] = zero;
+    if (!pooled) {
+      for (int c = 0; c < nchunks; ++c) {
+        GPartial zero = {0u, 0, 0u, 0u};
+        p[c] = zero;
+      }
     }
     const uint32_t key = (uint32_t)(bb >> 32);
     best_idx[j] = (fl == 0 && key != 0) ? (int32_t)(0xFFFFFFFFu - (uint32_t)bb) : -1;
@@ -955,20 +1002,29 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   const int64_t V = A.V;
   const float a = A.a;
 
-  // Row statistics of this sequence; the workspace records are cleared.
+  // Row statistics of this sequence.  Dense rows belong to this sequence
+  // alone and their workspace records are cleared here; pooled records are
+  // shared and cleared by a pass of their own after every sequence is done.
+  const bool pooled = A.map.nt > 0;
   for (int t = tid; t < nr; t += NT) {
-    const int64_t rr = b * nr + t;
-    RowStat s;
-    if (A.rowstat) {
-      s = A.rowstat[rr];
-      RowStat zero = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
-      A.rowstat[rr] = zero;
-    } else {
-      Partial* p = A.part + rr * A.nchunks;
-      s = merge_partials(p, A.nchunks, a);
-      for (int c = 0; c < A.nchunks; ++c) {
-        Partial zero = {0.f, 0u, 0.0};
-        p[c] = zero;
+    const int64_t rr = A.map.sidx(b, t);
+    RowStat s = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
+    if (rr >= 0) {
+      if (A.rowstat) {
+        s = A.rowstat[rr];
+        if (!pooled) {
+          RowStat zero = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
+          A.rowstat[rr] = zero;
+        }
+      } else {
+        Partial* p = A.part + rr * A.nchunks;
+        s = merge_partials(p, A.nchunks, a);
+        if (!pooled) {
+          for (int c = 0; c < A.nchunks; ++c) {
+            Partial zero = {0.f, 0u, 0.0};
+            p[c] = zero;
+          }
+        }
       }
     }
     TS.st[t] = s;
@@ -987,8 +1043,8 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
                (int64_t)x < V;
       float alpha_out = __builtin_nanf("");
       if (formed) {
-        const T* tr = A.map.row<T>(b * nr + lane);
-        const T* dr = A.map.row<T>(b * nr + k + 1 + lane);
+        const T* tr = A.map.at<T>(b, lane);
+        const T* dr = A.map.at<T>(b, k + 1 + lane);
         const double p = prob_at(Elem<T>::load1(tr + x), TS.st[lane], a);
         const double q = prob_at(Elem<T>::load1(dr + x), TS.st[k + 1 + lane], a);
         const double alpha = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
@@ -1016,8 +1072,8 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
 
   // Residual max(0, p_n - q_n) (n < k) or the bonus row's p_k (n = k).
   const bool has_q = n < k;
-  const T* prow = A.map.row<T>(b * nr + n);
-  const T* qrow = has_q ? A.map.row<T>(b * nr + k + 1 + n) : prow;
+  const T* prow = A.map.at<T>(b, n);
+  const T* qrow = has_q ? A.map.at<T>(b, k + 1 + n) : prow;
   const int32_t emitted =
       residual_draw<T, VEC, NT, sizeof(T) == 2 ? 4 : 2>(prow, qrow, has_q, draw_stats(TS.st[n]),
                                 draw_stats(has_q ? TS.st[k + 1 + n] : TS.st[n]), a, V,
@@ -1187,6 +1243,7 @@ struct SeqArgs {
   int32_t* out_tokens;
   float* accept_prob;
   uint32_t* queue;  // [2]: zero on entry; the last workgroup out zeroes it again
+  const RowStat* tstats;  // pooled rows: statistics of the target pool (flat rows 0..nt-1)
 };
 
 struct SeqScratch {
@@ -1210,7 +1267,7 @@ __device__ __forceinline__ int32_t residual_draw_call(const uint16_t* prow, cons
                                              DrawStats{qm, qthr, qz}, a, V, u, csum, emit_slot);
 }
 
-template <int PF, int D>
+template <int PF, int D, bool POOL>
 __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
   constexpr int NT = 1024;
   __shared__ uint32_t hist[32768];
@@ -1234,7 +1291,7 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
   block_sync_lds();
   uint32_t cur = Q.next;
   if (cur < (uint32_t)A.B) {
-    pf_row = A.map.template row<uint16_t>((int64_t)cur * nr);
+    pf_row = POOL ? A.map.template at<uint16_t>(cur, k1) : A.map.template row<uint16_t>((int64_t)cur * nr);
     prefetch_row(pf, pf_row, V);
   }
 
@@ -1252,29 +1309,51 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
       tok_in = A.tokens[b * k + TID()];
       u_in = A.u[b * k1 + TID()];
     }
+    // pooled rows: the target rows' statistics come from the pre-pass over
+    // the target pool; only draft rows are streamed here
+    RowStat tst_in = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
+    if constexpr (POOL) {
+      if (TID() <= k) {
+        const int64_t r = A.map.sidx(b, TID());
+        if (r >= 0) tst_in = A.tstats[r];
+      }
+    }
     uint32_t nxt = (uint32_t)A.B;
     int j = 0, n = -1;
-    bool draft = false, valid = true;
+    bool draft = POOL, valid = true;
     for (;;) {
       const int ridx = draft ? k1 + j : j;
-      const uint16_t* row = A.map.template row<uint16_t>(b * nr + ridx);
+      // pooled: a map entry outside the pool names no row (flat row 0 is
+      // read, and the row counts as invalid)
+      bool no_row = false;
+      const uint16_t* row;
+      if constexpr (POOL) {
+        const int64_t pr = A.map.sidx(b, ridx);
+        no_row = pr < 0;
+        row = A.map.template row<uint16_t>(no_row ? 0 : pr);
+      } else {
+        row = A.map.template row<uint16_t>(b * nr + ridx);
+      }
       // count (the prefetched vectors first, when they belong to this row)
       const bool bonus = !draft && j == k;
       if (bonus && TID() == 0) grabbed = atomicAdd(&A.queue[0], 1u);
       block_sync_lds();
       hist_count_stream<PF, D>(hist, row, V, pf, row == pf_row);
       if (bonus && TID() == 0) Q.next = grabbed;
-      if (ridx == 0) {
+      if (POOL ? j == 0 : ridx == 0) {
         if (TID() < k) {
           Q.tok[TID()] = tok_in;
           Q.uu[TID()] = u_in;
         }
+        if (POOL && TID() <= k) Q.st[TID()] = tst_in;
       }
       if (draft && TID() == j) {
         // the two logits of the ratio test, back before the scan ends
         const int32_t x = Q.tok[j];
         if (x >= 0 && (int64_t)x < V) {
-          lt = __builtin_bit_cast(float, (uint32_t)A.map.template row<uint16_t>(b * nr + j)[x] << 16);
+          const uint16_t* trow = POOL ? A.map.template at<uint16_t>(b, j)
+                                      : A.map.template row<uint16_t>(b * nr + j);
+          lt = __builtin_bit_cast(float, (uint32_t)trow[x] << 16);
           ld = __builtin_bit_cast(float, (uint32_t)row[x] << 16);
         }
       }
@@ -1286,7 +1365,9 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
       // prefetch the row most likely next: d_j after t_j, t_{j+1} after d_j
       // (acceptance), the next sequence's t_0 after the bonus row
       const uint16_t* next_row = nullptr;
-      if (!draft && j < k) next_row = A.map.template row<uint16_t>(b * nr + k1 + j);
+      if (POOL) {  // d_{j+1} after d_j
+        if (j + 1 < k) next_row = A.map.template at<uint16_t>(b, k1 + j + 1);
+      } else if (!draft && j < k) next_row = A.map.template row<uint16_t>(b * nr + k1 + j);
       else if (draft) next_row = A.map.template row<uint16_t>(b * nr + j + 1);
       else if (nxt < (uint32_t)A.B) next_row = A.map.template row<uint16_t>((int64_t)nxt * nr);
       pf_row = next_row;
@@ -1302,6 +1383,7 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
       } else {
         st = S.res;
       }
+      if (no_row) st.valid = 0;
       if (TID() == 0) Q.st[ridx] = st;
       if (!draft) {
         if (j == k) {  // bonus row: every position passed
@@ -1342,8 +1424,13 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
         n = j;
         valid = formed;
       }
-      draft = false;
+      draft = POOL;
       ++j;
+      if (POOL && n < 0 && j == k) {  // every position passed: the bonus row's pre-pass figures
+        valid = Q.st[k].valid != 0;
+        n = k;
+        break;
+      }
       if (n >= 0 && (!all_pos || j == k)) break;
     }
 
@@ -1352,8 +1439,11 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
     int32_t emitted = -1;
     if (valid) {
       const bool has_q = n < k;
-      const uint16_t* prow = A.map.template row<uint16_t>(b * nr + n);
-      const uint16_t* qrow = has_q ? A.map.template row<uint16_t>(b * nr + k1 + n) : prow;
+      const uint16_t* prow = POOL ? A.map.template at<uint16_t>(b, n)
+                                  : A.map.template row<uint16_t>(b * nr + n);
+      const uint16_t* qrow = !has_q ? prow
+                             : POOL ? A.map.template at<uint16_t>(b, k1 + n)
+                                    : A.map.template row<uint16_t>(b * nr + k1 + n);
       block_sync_lds();  // Q.st written by thread 0
       const RowStat& sp = Q.st[n];
       const RowStat& sq = Q.st[has_q ? k1 + n : n];

@@ -40,9 +40,14 @@
  *
  * Errors: the return value reports argument validation and launch failures
  * (spec_status_t).  Data faults are reported per sequence with
- * accepted_len[b] = -1 and out_tokens[b][*] = -1: a draft token outside
- * [0, V), a NaN or +inf logit, or a row without any finite logit, in any row
- * of that sequence.  -inf logits are allowed (vocabulary masking).
+ * accepted_len[b] = -1 and out_tokens[b][*] = -1.  A position is ill-formed
+ * when its target row or draft row holds a NaN or +inf logit or no finite
+ * logit, or its draft token lies outside [0, V).  Positions are walked in
+ * order and the first rejection (greedy: mismatch) ends the walk; the
+ * sequence is invalid when an ill-formed position comes before that end, or
+ * when every position passes and the bonus row is invalid.  Rows past the
+ * end are not consulted and cannot invalidate the sequence.  -inf logits are
+ * allowed (vocabulary masking).
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -122,7 +127,7 @@ size_t spec_workspace_size(int32_t op, int32_t B, int32_t k, int32_t V,
  *   out_tokens    [B][k+1] int32 out: drafts 0..n-1, then the corrected (n<k)
  *                 or bonus (n=k) token, then -1 padding
  *   accept_prob   [B][k] float out or NULL: alpha_j for every j < k (also past
- *                 the first rejection); NaN for an invalid sequence
+ *                 the first rejection); NaN at an ill-formed position
  *   workspace     device scratch of spec_workspace_size(SPEC_OP_STOCHASTIC...)
  *                 bytes, 256-byte aligned (see spec_workspace_size). */
 int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft,
@@ -148,6 +153,54 @@ int spec_logits_process(spec_logits_t logits, int32_t R, int32_t V,
                         const spec_sampling_t* sampling,
                         spec_row_stats_t* row_stats, float* probs,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Pooled rows: verify with rows shared by several sequences.
+ *
+ * The encyclopedia entry "Speculative decoding" (glopedia, 推测解码), section
+ * "Proposal methods and implementation forms" (提议方式与实现形态), names
+ * candidate trees beside chains; the predicted-outcome sets of "Speculative
+ * Speculative Decoding" (ai-stack.site summary, section 1 on its novelty,
+ * 研究创新性) hold several candidate outcomes per request.  Sequences (branches, or the
+ * root-to-leaf paths of a candidate tree) then share rows: the branches of
+ * one request share its target rows, and the paths through a tree node share
+ * that node's rows.  Each shared row is stored and processed once.
+ *
+ * Reading (the pages give no rule for combining branches): every sequence is
+ * verified on its own by the chain rule above, on the rows its maps name; an
+ * out-of-range map entry makes that row ill-formed (a data fault at a
+ * consulted position, as above).
+ *
+ *   target_pool   n_target_rows rows of V logits, row r at
+ *                 data + r * pos_stride (seq_stride is ignored)
+ *   target_map    [B][k+1] int32: pool row of target row j of sequence b;
+ *                 NULL = row b * (k+1) + j (needs n_target_rows >= B (k+1))
+ *   draft_pool    n_draft_rows rows, as target_pool, same dtype
+ *   draft_map     [B][k] int32: pool row of draft row j of sequence b;
+ *                 NULL = row b * k + j (needs n_draft_rows >= B k)
+ * The other arguments are those of spec_verify_stochastic, with a workspace
+ * of spec_workspace_size_pooled(SPEC_OP_STOCHASTIC, ...) bytes.  Pool sizes:
+ * 1 <= n_target_rows, n_draft_rows <= 2^31 - 1. */
+size_t spec_workspace_size_pooled(int32_t op, int32_t n_target_rows, int32_t n_draft_rows,
+                                  int32_t B, int32_t k, int32_t V,
+                                  const spec_sampling_t* sampling /* host */);
+
+int spec_verify_stochastic_pooled(spec_logits_t target_pool, int32_t n_target_rows,
+                                  const int32_t* target_map, spec_logits_t draft_pool,
+                                  int32_t n_draft_rows, const int32_t* draft_map,
+                                  const int32_t* draft_tokens, const float* uniforms,
+                                  int32_t B, int32_t k, int32_t V,
+                                  const spec_sampling_t* sampling, int32_t* accepted_len,
+                                  int32_t* out_tokens, float* accept_prob, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Greedy verify over pooled target rows (target_pool and target_map as in
+ * spec_verify_stochastic_pooled); the workspace is
+ * spec_workspace_size_pooled(SPEC_OP_GREEDY, n_target_rows, 0, B, k, V, NULL). */
+int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
+                              const int32_t* target_map, const int32_t* draft_tokens,
+                              int32_t B, int32_t k, int32_t V, int32_t* accepted_len,
+                              int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* Static description of a status code. */
 const char* spec_status_string(int status);

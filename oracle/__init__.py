@@ -91,8 +91,35 @@ def _strides(a: np.ndarray):
     return a.strides[0] // a.itemsize, a.strides[1] // a.itemsize
 
 
+def _pool_map(m, B: int, rows: int) -> np.ndarray:
+    if m is None:
+        return np.arange(B * rows, dtype=np.int64).reshape(B, rows)
+    m = np.asarray(m, dtype=np.int64)
+    if m.shape != (B, rows):
+        raise ValueError("row map must be [%d][%d]" % (B, rows))
+    return m
+
+
+def gather_rows(pool: np.ndarray, rows: np.ndarray) -> np.ndarray:
+    """The [B][r][V] logits that a row map names in a pool [P][V].  An index
+    outside [0, P) gives a row of NaN (an ill-formed row under the rule)."""
+    pool = np.asarray(pool)
+    if pool.ndim != 2:
+        raise ValueError("a row pool is [P][V]")
+    P = pool.shape[0]
+    ok = (rows >= 0) & (rows < P)
+    out = pool[np.where(ok, rows, 0)]
+    nan = np.float32(np.nan) if pool.dtype == np.float32 else np.uint16(0x7FC0)
+    out[~ok] = nan
+    return np.ascontiguousarray(out)
+
+
 class Oracle:
     """The oracle's entry points bound to one compiled library."""
+
+    # pooled rows -> [B][r][V] logits; an attribute so that tests can plant
+    # mistakes in it
+    gather = staticmethod(gather_rows)
 
     def __init__(self, lib):
         self.lib = lib
@@ -166,6 +193,25 @@ class Oracle:
             raise MemoryError("oracle allocation failed")
         return acc, out
 
+    def verify_stochastic_pooled(self, target_pool, target_map, draft_pool, draft_map, tokens,
+                                 uniforms, temperature=1.0, top_k=0, top_p=1.0):
+        """Stochastic verify over pooled rows: sequence b's target row j is
+        target_pool[target_map[b][j]] and its draft row j draft_pool[
+        draft_map[b][j]] (a map of None names rows b (k+1) + j and b k + j).
+        Each sequence is verified on its own by the same rule; a map entry
+        outside its pool stands for an ill-formed row."""
+        B, k = np.asarray(tokens).reshape(len(tokens), -1).shape
+        tm = _pool_map(target_map, B, k + 1)
+        dm = _pool_map(draft_map, B, k)
+        return self.verify_stochastic(self.gather(target_pool, tm), self.gather(draft_pool, dm),
+                                      tokens, uniforms, temperature, top_k, top_p)
+
+    def verify_greedy_pooled(self, target_pool, target_map, tokens):
+        """Greedy verify over a pooled target (as verify_stochastic_pooled)."""
+        B, k = np.asarray(tokens).reshape(len(tokens), -1).shape
+        return self.verify_greedy(self.gather(target_pool, _pool_map(target_map, B, k + 1)),
+                                  tokens)
+
     def sample_drafts(self, draft, u, temperature=1.0, top_k=0, top_p=1.0, threads=1):
         """Draw one token per draft row ([B][k][V]) from the processed q with the
         uniforms u [B][k] -- the proposer's own sampling, so that drafts meet the
@@ -235,3 +281,13 @@ def sample_drafts(draft, u, temperature=1.0, top_k=0, top_p=1.0, threads=1):
 
 def argmax_drafts(draft):
     return default().argmax_drafts(draft)
+
+
+def verify_stochastic_pooled(target_pool, target_map, draft_pool, draft_map, tokens, uniforms,
+                             temperature=1.0, top_k=0, top_p=1.0):
+    return default().verify_stochastic_pooled(target_pool, target_map, draft_pool, draft_map,
+                                              tokens, uniforms, temperature, top_k, top_p)
+
+
+def verify_greedy_pooled(target_pool, target_map, tokens):
+    return default().verify_greedy_pooled(target_pool, target_map, tokens)

@@ -424,6 +424,65 @@ def pin_chi_square(orc, n=1_000_000):
     assert abs(acc - 0.9) < 0.003, acc  # P(accept) = sum min(p, q) = 0.5 + 0.3 + 0.1
 
 
-ALL_PINS = [pin_worked_example, pin_law_of_decision_map, pin_softmax_and_filters,
+# ---------------------------------------------------------------------------
+def pin_pooled_rows(orc):
+    """Pooled rows (sequences naming shared rows through maps).  The worked
+    example's rows held once and shared by four branches give the outcomes
+    the example fixes for each branch's draft and draws; out-of-range map
+    entries count only where the walk consults them; relabelling the pool
+    rows (with the maps) changes nothing."""
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    target, draft, _ = worked_example()
+    tpool = np.ascontiguousarray(np.stack([target[0, 0], target[0, 0]]))  # row 1: bonus row (= p)
+    dpool = np.ascontiguousarray(draft[0, :1])
+    tmap = [[0, 1]] * 4 + [[0, 5], [0, 5], [0, 1], [7, 1]]
+    dmap = [[0]] * 6 + [[-1], [0]]
+    toks = [[1], [1], [0], [2], [1], [1], [1], [1]]
+    u = [[0.7, 0.0], [0.8, 0.5], [0.99, 0.3], [0.999, 0.95],
+         [0.7, 0.0], [0.8, 0.5], [0.1, 0.1], [0.1, 0.1]]
+    r = orc.verify_stochastic_pooled(tpool, np.array(tmap), dpool, np.array(dmap),
+                                     np.array(toks, np.int32), np.array(u, np.float32))
+    # B: alpha 0.3 / 0.4 = 0.75 (accept at 0.7, reject at 0.8, residual all on
+    # A); A: 0.6 / 0.5 >= 1; C: 0.1 / 0.1 = 1; bonus draws from p by inverse CDF
+    assert abs(r["accept_prob"][0, 0] - g["accept_probability"]) < 1e-6
+    assert list(r["accepted_len"]) == [1, 0, 1, 1, -1, 0, -1, -1], r["accepted_len"]
+    assert [list(x) for x in r["out_tokens"][:4]] == [[1, 0], [0, -1], [0, 0], [2, 2]]
+    assert list(r["out_tokens"][5]) == [0, -1]
+    assert np.isnan(r["accept_prob"][6, 0]) and np.isnan(r["accept_prob"][7, 0])
+    # relabelling: the same sequences through permuted pools and maps
+    rs = np.random.default_rng(61)
+    B, k, V, Pt, Pd = 12, 3, 7, 9, 8
+    tp = rs.normal(0, 1.5, (Pt, V)).astype(np.float32)
+    dp = rs.normal(0, 1.5, (Pd, V)).astype(np.float32)
+    tm = rs.integers(0, Pt, (B, k + 1))
+    dm = rs.integers(0, Pd, (B, k))
+    toks = rs.integers(0, V, (B, k)).astype(np.int32)
+    u = rs.random((B, k + 1)).astype(np.float32)
+    a = orc.verify_stochastic_pooled(tp, tm, dp, dm, toks, u, 0.9, 0, 0.9)
+    pt, pd = rs.permutation(Pt), rs.permutation(Pd)
+    b = orc.verify_stochastic_pooled(tp[pt], np.argsort(pt)[tm], dp[pd], np.argsort(pd)[dm],
+                                     toks, u, 0.9, 0, 0.9)
+    for key in ("accepted_len", "out_tokens", "flags"):
+        assert np.array_equal(a[key], b[key]), key
+    assert np.array_equal(a["accept_prob"], b["accept_prob"])
+    # two sequences naming the same rows with the same tokens and draws agree,
+    # and the draft map is not the target map
+    tm[1], dm[1], toks[1], u[1] = tm[0], dm[0], toks[0], u[0]
+    c = orc.verify_stochastic_pooled(tp, tm, dp, dm, toks, u, 0.9, 0, 0.9)
+    assert np.array_equal(c["out_tokens"][0], c["out_tokens"][1])
+    assert np.array_equal(c["accept_prob"][0], c["accept_prob"][1])
+    # greedy over pooled one-hot rows: argmaxes 2, 0, 3, 1 for pool rows 0..3
+    gp = np.full((4, 4), -1.0, np.float32)
+    for i, x in enumerate([2, 0, 3, 1]):
+        gp[i, x] = 2.0
+    gm = [[0, 1, 2], [0, 3, 2], [1, 1, 1], [0, 1, 2], [0, 1, 9], [0, 1, 9]]
+    gt = [[2, 0], [2, 1], [0, 0], [1, 0], [2, 0], [2, 1]]
+    acc, out = orc.verify_greedy_pooled(gp, np.array(gm), np.array(gt, np.int32))
+    assert list(acc) == [2, 2, 2, 0, -1, 1], acc
+    assert [list(x) for x in out] == [[2, 0, 3], [2, 1, 3], [0, 0, 0], [2, -1, -1],
+                                      [-1, -1, -1], [2, 0, -1]], out
+
+
+ALL_PINS = [pin_pooled_rows, pin_worked_example, pin_law_of_decision_map, pin_softmax_and_filters,
             pin_acceptance_rate, pin_special_cases, pin_greedy, pin_bf16_decode,
             pin_invalid_inputs, pin_boundary_flags, pin_chi_square]

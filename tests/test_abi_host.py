@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "spec_logits_process", "spec_status_string", "spec_verify_greedy",
-        "spec_verify_stochastic", "spec_workspace_size"])
+        "spec_verify_greedy_pooled", "spec_verify_stochastic", "spec_verify_stochastic_pooled",
+        "spec_workspace_size", "spec_workspace_size_pooled"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -123,3 +124,65 @@ def test_validation_codes_before_any_launch():
                                  None) == sv.SPEC_ERR_INVALID_ARG
     assert L.spec_logits_process(_desc(), 4, 1024, None, None, None, ws, wsb,
                                  None) == sv.SPEC_ERR_INVALID_ARG
+
+
+
+def test_pooled_workspace_and_validation():
+    """Pooled calls: workspace sizing and the host-side checks of the pools
+    and maps (all before any HIP call)."""
+    L = sv.lib()
+    s = sv.spec_sampling_t(1.0, 0, 0.95)
+    assert sv.workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, 160, 8192, 2048, 4, 151936, 1.0, 0, 0.95) > 0
+    assert sv.workspace_size_pooled(sv.SPEC_OP_GREEDY, 160, 0, 2048, 4, 151936) > 0
+    assert L.spec_workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, 0, 8, 2, 4, 64, ctypes.byref(s)) == 0
+    assert L.spec_workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, 8, 0, 2, 4, 64, ctypes.byref(s)) == 0
+    assert L.spec_workspace_size_pooled(sv.SPEC_OP_PROCESS, 8, 8, 2, 4, 64, ctypes.byref(s)) == 0
+    # more rows -> no smaller workspace
+    a = sv.workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, 10, 100, 64, 4, 4096)
+    b = sv.workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, 10, 1000, 64, 4, 4096)
+    assert 0 < a <= b
+    p = ctypes.c_void_p(4096)
+    ws, wsb = ctypes.c_void_p(1 << 20), 1 << 30
+    pool = sv.spec_logits_t(4096, 0, 0, 0, 1024)
+
+    def call(nt=10, tmap=p, nd=8, dmap=p, B=2, k=4, V=1024, tpool=pool, dpool=pool, w=ws):
+        return L.spec_verify_stochastic_pooled(tpool, nt, tmap, dpool, nd, dmap, p, p, B, k, V,
+                                               ctypes.byref(s), p, p, None, w, wsb, None)
+
+    assert call(nt=0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(nd=0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(tmap=None, nt=9) == sv.SPEC_ERR_INVALID_ARG    # needs B (k+1) = 10 rows
+    assert call(dmap=None, nd=7) == sv.SPEC_ERR_INVALID_ARG    # needs B k = 8 rows
+    assert call(tpool=sv.spec_logits_t(4096, 0, 0, 0, 1000)) == sv.SPEC_ERR_INVALID_ARG
+    assert call(dpool=sv.spec_logits_t(4096, 1, 0, 0, 1024)) == sv.SPEC_ERR_INVALID_ARG
+    assert call(k=65) == sv.SPEC_ERR_UNSUPPORTED
+    assert call(w=None) == sv.SPEC_ERR_WORKSPACE
+    assert L.spec_verify_greedy_pooled(pool, 9, None, p, 2, 4, 1024, p, p, ws, wsb,
+                                       None) == sv.SPEC_ERR_INVALID_ARG
+    assert L.spec_verify_greedy_pooled(pool, 0, p, p, 2, 4, 1024, p, p, ws, wsb,
+                                       None) == sv.SPEC_ERR_INVALID_ARG
+    assert L.spec_verify_greedy_pooled(pool, 10, p, p, 2, 4, 1024, p, p, None, 0,
+                                       None) == sv.SPEC_ERR_WORKSPACE
+
+
+def test_tree_branches():
+    """Parent-pointer tree -> per-branch tokens and pool-row maps."""
+    #        0
+    #      /   \
+    #     1     2
+    #    / \    |
+    #   3   4   5
+    parents = [-1, 0, 0, 1, 1, 2]
+    tokens = [0, 11, 12, 13, 14, 15]
+    toks, tmap, dmap = sv.tree_branches(parents, tokens)
+    assert toks.tolist() == [[11, 13], [11, 14], [12, 15]]
+    assert tmap.tolist() == [[0, 1, 3], [0, 1, 4], [0, 2, 5]]
+    assert dmap.tolist() == [[0, 1], [0, 1], [0, 2]]
+    toks, tmap, _ = sv.tree_branches(parents, tokens, leaves=[5])
+    assert toks.tolist() == [[12, 15]] and tmap.tolist() == [[0, 2, 5]]
+    with pytest.raises(ValueError):
+        sv.tree_branches([-1, 0, 0, 1], [0, 1, 2, 3])      # leaves at depths 1 and 2
+    with pytest.raises(ValueError):
+        sv.tree_branches([-1, 2, 0], [0, 1, 2])             # parent after its child
+    with pytest.raises(ValueError):
+        sv.tree_branches([0, 0], [0, 1])                    # no root

@@ -3,6 +3,7 @@ check that the pins catch every one of them.  The real oracle is untouched;
 each mutant is compiled into a temporary library of its own."""
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -63,3 +64,38 @@ def test_pins_catch_mutation(tmp_path, name):
         except Exception as e:  # a crash or a NaN path also counts as caught
             caught.append("%s raised %s" % (getattr(pin, "__name__", "?"), type(e).__name__))
     assert caught, "no pin caught the planted mistake: %s" % name
+
+
+# Mistakes planted in the pooled-row gather (Python), one subclass each.
+def _gather_ignoring_map(pool, rows):
+    flat = np.arange(rows.size).reshape(rows.shape) % len(pool)
+    return oracle.gather_rows(pool, flat)
+
+
+def _gather_clamping(pool, rows):
+    return oracle.gather_rows(pool, np.clip(rows, 0, len(pool) - 1))
+
+
+def _gather_off_by_one(pool, rows):
+    return oracle.gather_rows(pool, np.where(rows > 0, rows - 1, rows))
+
+
+class _TargetMapForDrafts(oracle.Oracle):
+    def verify_stochastic_pooled(self, tp, tm, dp, dm, toks, u, *args):
+        k = np.asarray(toks).shape[1]
+        return super().verify_stochastic_pooled(tp, tm, dp, np.asarray(tm)[:, :k], toks, u, *args)
+
+
+POOL_MUTATIONS = {
+    "pool map ignored": lambda lib: type("M", (oracle.Oracle,), {"gather": staticmethod(_gather_ignoring_map)})(lib),
+    "out-of-range map entry clamped": lambda lib: type("M", (oracle.Oracle,), {"gather": staticmethod(_gather_clamping)})(lib),
+    "map entries off by one": lambda lib: type("M", (oracle.Oracle,), {"gather": staticmethod(_gather_off_by_one)})(lib),
+    "target map used for the drafts": lambda lib: _TargetMapForDrafts(lib),
+}
+
+
+@pytest.mark.parametrize("name", sorted(POOL_MUTATIONS))
+def test_pins_catch_pool_mutation(name):
+    orc = POOL_MUTATIONS[name](oracle.default().lib)
+    with pytest.raises(AssertionError):
+        pins.pin_pooled_rows(orc)
