@@ -3,8 +3,9 @@
 One step = one spec_verify_stochastic call over one batch of synthetic inputs
 already resident in HBM (every hot-path step: logits processing, ratio test,
 first rejection, residual / bonus inverse-CDF draw).  The default workload is
-the branch-fanout verify: 32 requests x 16 branches = 2048 sequences, k = 4
-drafted positions, V = 151936, bf16 logits, temperature 1, top-p 0.95.
+the branch-fanout verify: 32 requests x 16 branches = 512 sequences, k = 4
+drafted positions each (2048 per call), V = 151936, bf16 logits, temperature 1,
+top-p 0.95.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """

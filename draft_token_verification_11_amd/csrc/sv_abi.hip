@@ -23,7 +23,19 @@ struct Layout {
   int nchunks = 1;   // V-chunks per row
   int64_t rows = 0;  // rows processed
   size_t rowstat_off = 0, part_off = 0, queue_off = 0, total = 0;
+  size_t help_off = 0;  // whole-sequence walk: the help region (sv::HelpView)
 };
+
+using sv::kMaxWalkGrid;
+
+// The whole-sequence walk's queue words and help region.
+size_t walk_regions(Layout& L, size_t off, int64_t k) {
+  L.queue_off = off;
+  off = (off + 4 * sizeof(uint32_t) + 255) & ~size_t(255);
+  L.help_off = off;
+  off = (off + size_t(sv::HelpView::bytes(2 * k + 1)) + 255) & ~size_t(255);
+  return off;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -61,10 +73,7 @@ Layout make_layout(int op, int64_t B, int64_t k, int64_t V, const spec_sampling_
     L.part_off = off;
     off = align256(off + size_t(L.rows) * size_t(L.nchunks) * 16);
   }
-  if (op == SPEC_OP_STOCHASTIC) {  // sequence queue of the whole-sequence kernel
-    L.queue_off = off;
-    off = align256(off + 2 * sizeof(uint32_t));
-  }
+  if (op == SPEC_OP_STOCHASTIC) off = walk_regions(L, off, k);  // whole-sequence walk
   L.total = off < 256 ? 256 : off;
   return L;
 }
@@ -72,7 +81,8 @@ Layout make_layout(int op, int64_t B, int64_t k, int64_t V, const spec_sampling_
 // Pooled rows: the row passes run over the pools (nt target rows, then nd
 // draft rows; greedy: the nt target rows).  The row-statistics region always
 // exists: the whole-sequence walk keeps the target pool's statistics there.
-Layout make_pooled_layout(int op, int64_t nt, int64_t nd, int64_t V, const spec_sampling_t* s) {
+Layout make_pooled_layout(int op, int64_t nt, int64_t nd, int64_t k, int64_t V,
+                          const spec_sampling_t* s) {
   Layout L;
   const bool greedy = op == SPEC_OP_GREEDY;
   L.rows = greedy ? nt : nt + nd;
@@ -88,10 +98,7 @@ Layout make_pooled_layout(int op, int64_t nt, int64_t nd, int64_t V, const spec_
     L.part_off = off;
     off = align256(off + size_t(L.rows) * size_t(L.nchunks) * 16);
   }
-  if (!greedy) {
-    L.queue_off = off;
-    off = align256(off + 2 * sizeof(uint32_t));
-  }
+  if (!greedy) off = walk_regions(L, off, k);
   L.total = off < 256 ? 256 : off;
   return L;
 }
@@ -159,6 +166,8 @@ int device_cus() {
     cus = 256;
   return cus;
 }
+
+int walk_grid_for(int cus) { return cus < kMaxWalkGrid ? cus : kMaxWalkGrid; }
 
 // Workgroups of the persistent filter: one per CU, a multiple of 8 (one
 // range of rows per XCD), no more than needed.
@@ -258,7 +267,8 @@ struct StochasticRun {
       if (walk_grid > 0) {
         sv::SeqArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
                       args.accepted_len, args.out_tokens, args.accept_prob,
-                      reinterpret_cast<uint32_t*>(ws + L.queue_off), nullptr};
+                      reinterpret_cast<uint32_t*>(ws + L.queue_off), nullptr,
+                      reinterpret_cast<uint64_t*>(ws + L.help_off)};
         hipLaunchKernelGGL((sv::k_verify_seq_bf16<kPrefetch, kLoadDepth, false>),
                            dim3(unsigned(walk_grid)), dim3(kFilterThreads), 0, st, A);
         return;
@@ -321,7 +331,8 @@ struct PooledStochasticRun {
                            dim3(persistent_grid(nt)), dim3(kFilterThreads), 0, st, F);
         sv::SeqArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
                       args.accepted_len, args.out_tokens, args.accept_prob,
-                      reinterpret_cast<uint32_t*>(ws + L.queue_off), rs};
+                      reinterpret_cast<uint32_t*>(ws + L.queue_off), rs,
+                      reinterpret_cast<uint64_t*>(ws + L.help_off)};
         hipLaunchKernelGGL((sv::k_verify_seq_bf16<kPrefetch, kLoadDepth, true>),
                            dim3(unsigned(walk_grid)), dim3(kFilterThreads), 0, st, A);
         clear_bytes = nt * int64_t(sizeof(sv::RowStat));
@@ -390,7 +401,7 @@ int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft, const int3
   // the whole-sequence walk: aligned bf16 rows, at least kSeqPerCu sequences per CU
   const int cus = device_cus();
   const int walk_grid =
-      (target.dtype == SPEC_DTYPE_BF16 && vec && int64_t(B) >= int64_t(kSeqPerCu) * cus) ? cus : 0;
+      (target.dtype == SPEC_DTYPE_BF16 && vec && int64_t(B) >= int64_t(kSeqPerCu) * cus) ? walk_grid_for(cus) : 0;
   if (!walk_grid && (!row_pass_fits(L, target.dtype, vec) || !grid_fits(B, kTailThreads)))
     return SPEC_ERR_UNSUPPORTED;
 
@@ -474,7 +485,7 @@ size_t spec_workspace_size_pooled(int32_t op, int32_t n_target_rows, int32_t n_d
   } else {
     sampling = &plain;
   }
-  return make_pooled_layout(op, n_target_rows, greedy ? 0 : n_draft_rows, V, sampling).total;
+  return make_pooled_layout(op, n_target_rows, greedy ? 0 : n_draft_rows, k, V, sampling).total;
 }
 
 int spec_verify_stochastic_pooled(spec_logits_t target_pool, int32_t n_target_rows,
@@ -496,13 +507,13 @@ int spec_verify_stochastic_pooled(spec_logits_t target_pool, int32_t n_target_ro
   if ((rc = check_logits(draft_pool, V)) != SPEC_OK) return rc;
   if (target_pool.dtype != draft_pool.dtype) return SPEC_ERR_INVALID_ARG;
   if (!draft_tokens || !uniforms || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
-  const Layout L = make_pooled_layout(SPEC_OP_STOCHASTIC, n_target_rows, n_draft_rows, V, sampling);
+  const Layout L = make_pooled_layout(SPEC_OP_STOCHASTIC, n_target_rows, n_draft_rows, k, V, sampling);
   if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
   const bool vec = vec_ok(target_pool) && vec_ok(draft_pool);
   const int cus = device_cus();
   const int walk_grid =
-      (target_pool.dtype == SPEC_DTYPE_BF16 && vec && int64_t(B) >= int64_t(kSeqPerCu) * cus) ? cus
-                                                                                               : 0;
+      (target_pool.dtype == SPEC_DTYPE_BF16 && vec && int64_t(B) >= int64_t(kSeqPerCu) * cus)
+          ? walk_grid_for(cus) : 0;
   if (!walk_grid && (!row_pass_fits(L, target_pool.dtype, vec) || !grid_fits(B, kTailThreads)))
     return SPEC_ERR_UNSUPPORTED;
 
@@ -538,7 +549,7 @@ int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
   if ((rc = check_logits(target_pool, V)) != SPEC_OK) return rc;
   if (!draft_tokens || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
   const spec_sampling_t plain = {1.0f, 0, 1.0f};
-  const Layout L = make_pooled_layout(SPEC_OP_GREEDY, n_target_rows, 0, V, &plain);
+  const Layout L = make_pooled_layout(SPEC_OP_GREEDY, n_target_rows, 0, k, V, &plain);
   if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
   if (!grid_fits(L.rows * L.nchunks, kRowThreads) || !grid_fits(B, 64)) return SPEC_ERR_UNSUPPORTED;
   sv::RowMap map{target_pool.data, 0, target_pool.pos_stride, target_pool.data, 0,

@@ -661,7 +661,9 @@ __device__ __forceinline__ int hist_row_stats(uint32_t* hist, HistScratch& S, in
     uint32_t thr_key = tk;
     double z = zk;
     if (use_p) {
-      const double target = (double)top_p * zk;
+      float tp = top_p;
+      asm volatile("" : "+v"(tp));  // converted here, not held in registers across the walk
+      const double target = (double)tp * zk;
       double carry = 0.0;
       for (uint32_t base = 0; base <= last; base += kWave) {
         const bool in = base + lane <= last;
@@ -1242,8 +1244,44 @@ struct SeqArgs {
   int32_t* accepted_len;
   int32_t* out_tokens;
   float* accept_prob;
-  uint32_t* queue;  // [2]: zero on entry; the last workgroup out zeroes it again
+  // [4] sequences taken, workgroups out, sequences done, help records
+  // allocated: zero on entry; the last workgroup out zeroes them again
+  uint32_t* queue;
   const RowStat* tstats;  // pooled rows: statistics of the target pool (flat rows 0..nt-1)
+  // Help with the rows of other workgroups' walks once the queue is empty,
+  // in the region at `help` (HelpView): per-workgroup progress, help entries
+  // and help records.
+  uint64_t* help;
+};
+
+// Most workgroups the whole-sequence walk launches (one per CU).
+constexpr int kMaxWalkGrid = 1024;
+
+// The help region of the whole-sequence walk, for kMaxWalkGrid workgroups
+// and walks of up to nr = 2k+1 steps:
+//   hwg[g]     (1 + sequence) << 32 | (1 + step) of the walk of workgroup g,
+//              or 0 when it walks none;
+//   hent[g][w] step w of the walk of workgroup g: (tag << 32) | (state << 30)
+//              | record, tag = 1 + the sequence; state 0: its walker counts
+//              the row, 1: a helper counts it, 2: the helper's figures are in
+//              hpool[record].  A walker's sequences grow, so an entry with a
+//              smaller tag is stale;
+//   hpool      help records: enough for every step of two sequences per
+//              workgroup (beyond that a helper publishes without figures).
+struct HelpView {
+  uint64_t* hwg;
+  uint64_t* hent;
+  RowStat* hpool;
+  uint32_t hcap;
+  __host__ __device__ static int64_t records(int64_t nr) { return 2 * kMaxWalkGrid * nr; }
+  __host__ __device__ static int64_t bytes(int64_t nr) {
+    return 8 * kMaxWalkGrid + 8 * kMaxWalkGrid * nr + 32 * records(nr);
+  }
+  __device__ HelpView(uint64_t* base, int nr)
+      : hwg(base),
+        hent(base + kMaxWalkGrid),
+        hpool(reinterpret_cast<RowStat*>(base + kMaxWalkGrid + (int64_t)kMaxWalkGrid * nr)),
+        hcap((uint32_t)records(nr)) {}
 };
 
 struct SeqScratch {
@@ -1254,7 +1292,54 @@ struct SeqScratch {
   int32_t emit;
   uint32_t next;      // the sequence taken next
   int32_t formed, accepted;  // decision at the current position
+  RowStat hst;        // figures of the current row published by a helper
+  int32_t hmode;      // 1: hst holds the current row's figures
+  uint64_t hprev;     // the next step's entry before this walker claimed it
+  int32_t hjob_g, hjob_s, hjob_slot, hjob_state;  // a helper's claimed row
+  uint32_t hjob_tag;
 };
+
+constexpr uint32_t kHelpClaimed = 1u, kHelpPublished = 2u;
+constexpr uint32_t kHelpNoRecord = 0x3FFFFFFFu;  // published without figures (records used up)
+constexpr int kHelpWaitIters = 20000;  // bound of a walker's wait for a helper (~2 ms)
+
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Walk step w -> row slot of the sequence (target rows 0..k, draft rows k+1..).
+// Whole rows: t_j is step 2j, d_j step 2j+1, the bonus row t_k step 2k.
+// Pooled rows (target figures from the pre-pass): d_j is step j.
+template <bool POOL>
+__device__ __forceinline__ int step_slot(int w, int k) {
+  if (POOL) return k + 1 + w;
+  return (w & 1) ? k + 1 + (w >> 1) : (w >> 1);
+}
+
+// A walker's view of a step it claimed one row earlier: 1 with the figures
+// in *out when a helper has published them (waiting, within a bound, for a
+// helper that is counting the row), 0 when the walker counts it itself.
+__device__ __noinline__ int help_resolve(uint64_t* ent, uint64_t prev, uint32_t tag,
+                                         const RowStat* pool, RowStat* out) {
+  if ((uint32_t)(prev >> 32) != tag) return 0;  // stale: the walker holds the step
+  uint64_t e = prev;
+  for (int it = 0; ((uint32_t)e >> 30) == kHelpClaimed; ++it) {
+    if (it == kHelpWaitIters) return 0;
+    __builtin_amdgcn_s_sleep(4);
+    e = ld_agent(ent);
+  }
+  if ((uint32_t)(e >> 32) != tag || ((uint32_t)e >> 30) != kHelpPublished) return 0;
+  const uint32_t rec = (uint32_t)e & 0x3FFFFFFFu;
+  if (rec == kHelpNoRecord) return 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const uint64_t* src = reinterpret_cast<const uint64_t*>(pool + rec);
+  uint64_t* dst = reinterpret_cast<uint64_t*>(out);
+  for (int i = 0; i < 4; ++i) dst[i] = ld_agent(src + i);
+  return 1;
+}
 
 // Out of line, with scalar arguments, so that its registers do not burden
 // the walk's streaming loop.
@@ -1282,7 +1367,9 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
   };
   const int64_t V = A.V;
   const int k = A.k, k1 = k + 1, nr = 2 * k + 1;
+  const int nsteps = POOL ? k : nr;
   const bool all_pos = A.accept_prob != nullptr;
+  const int g = blockIdx.x;
 
   uint4 pf[PF];
   const uint16_t* pf_row = nullptr;  // the row whose first vectors pf holds
@@ -1297,6 +1384,7 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
 
   while (cur < (uint32_t)A.B) {
     const int64_t b = cur;
+    const uint32_t tag = cur + 1u;
     // the next sequence is taken from the queue late -- before the bonus row
     // or the correction -- so a workgroup never holds one it cannot start
     uint32_t grabbed = 0;
@@ -1323,6 +1411,7 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
     bool draft = POOL, valid = true;
     for (;;) {
       const int ridx = draft ? k1 + j : j;
+      const int w = POOL ? j : 2 * j + (draft ? 1 : 0);  // walk step
       // pooled: a map entry outside the pool names no row (flat row 0 is
       // read, and the row counts as invalid)
       bool no_row = false;
@@ -1334,11 +1423,19 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
       } else {
         row = A.map.template row<uint16_t>(b * nr + ridx);
       }
-      // count (the prefetched vectors first, when they belong to this row)
       const bool bonus = !draft && j == k;
-      if (bonus && TID() == 0) grabbed = atomicAdd(&A.queue[0], 1u);
+      if (TID() == 0) {
+        if (bonus) grabbed = atomicAdd(&A.queue[0], 1u);
+        const HelpView H(A.help, nr);
+        st_agent(H.hwg + g, ((uint64_t)tag << 32) | (uint32_t)(w + 1));
+        // steps after the first were claimed one row earlier
+        Q.hmode = w > 0 ? help_resolve(H.hent + (int64_t)g * nr + w, Q.hprev, tag, H.hpool, &Q.hst)
+                        : 0;
+      }
       block_sync_lds();
-      hist_count_stream<PF, D>(hist, row, V, pf, row == pf_row);
+      const bool helped = Q.hmode != 0;
+      // count (the prefetched vectors first, when they belong to this row)
+      if (!helped) hist_count_stream<PF, D>(hist, row, V, pf, row == pf_row);
       if (bonus && TID() == 0) Q.next = grabbed;
       if (POOL ? j == 0 : ridx == 0) {
         if (TID() < k) {
@@ -1363,17 +1460,26 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
         have_next = true;
       }
       // prefetch the row most likely next: d_j after t_j, t_{j+1} after d_j
-      // (acceptance), the next sequence's t_0 after the bonus row
+      // (acceptance), the next sequence's t_0 after the bonus row; the
+      // walker claims a step of its own sequence before helpers can
       const uint16_t* next_row = nullptr;
       if (POOL) {  // d_{j+1} after d_j
         if (j + 1 < k) next_row = A.map.template at<uint16_t>(b, k1 + j + 1);
       } else if (!draft && j < k) next_row = A.map.template row<uint16_t>(b * nr + k1 + j);
       else if (draft) next_row = A.map.template row<uint16_t>(b * nr + j + 1);
       else if (nxt < (uint32_t)A.B) next_row = A.map.template row<uint16_t>((int64_t)nxt * nr);
+      uint64_t claim = 0;
+      const bool claim_next = w + 1 < nsteps && !bonus;
+      if (claim_next && TID() == 0)
+        claim = __hip_atomic_fetch_max(HelpView(A.help, nr).hent + (int64_t)g * nr + w + 1,
+                                       (uint64_t)tag << 32, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
       pf_row = next_row;
       if (next_row) prefetch_row(pf, next_row, V);
       RowStat st;
-      if (hist_row_stats(hist, S, V, A.a, A.top_k, A.top_p, nullptr) == 2) {
+      if (helped) {
+        st = Q.hst;
+      } else if (hist_row_stats(hist, S, V, A.a, A.top_k, A.top_p, nullptr) == 2) {
         block_sync_lds();
         filter_row_bisect_call<uint16_t, true, NT>(row, V, A.a, A.top_k, A.top_p, &S.res, S.dslot,
                                                     S.uslot);
@@ -1383,6 +1489,7 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
       } else {
         st = S.res;
       }
+      if (claim_next && TID() == 0) Q.hprev = claim;
       if (no_row) st.valid = 0;
       if (TID() == 0) Q.st[ridx] = st;
       if (!draft) {
@@ -1434,7 +1541,10 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
       if (n >= 0 && (!all_pos || j == k)) break;
     }
 
-    if (!have_next && TID() == 0) grabbed = atomicAdd(&A.queue[0], 1u);
+    if (TID() == 0) {
+      st_agent(HelpView(A.help, nr).hwg + g, 0ull);  // no more rows of this sequence to help with
+      if (!have_next) grabbed = atomicAdd(&A.queue[0], 1u);
+    }
     // correction from the residual of the rows at n, or the bonus draw
     int32_t emitted = -1;
     if (valid) {
@@ -1459,7 +1569,10 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
       }
       out[t] = v;
     }
-    if (TID() == 0) A.accepted_len[b] = valid ? n : -1;
+    if (TID() == 0) {
+      A.accepted_len[b] = valid ? n : -1;
+      atomicAdd(&A.queue[2], 1u);  // sequences done
+    }
     if (!have_next) {
       if (TID() == 0) Q.next = grabbed;
       block_sync_lds();
@@ -1468,13 +1581,128 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
     cur = nxt;
     block_sync_lds();  // everyone has read Q before the next sequence writes it
   }
-  // The last workgroup out leaves the queue zero for the next call.
-  if (TID() == 0) {
-    const uint32_t done = atomicAdd(&A.queue[1], 1u);
-    if (done == gridDim.x - 1) {
-      atomicExch(&A.queue[0], 0u);
-      atomicExch(&A.queue[1], 0u);
+
+  const HelpView H(A.help, nr);
+  // The queue is empty: count rows ahead of the other workgroups' walks (the
+  // step after the one each walker has claimed, and the one after that) and
+  // publish their figures, until every sequence is done.  A helper never
+  // waits for anything but the walks' progress, and a walker waits only for
+  // a row a helper is already counting, so every wave exits.
+  for (;;) {
+    if (TID() < kWave) {
+      const int lane = TID();
+      int found = 0;
+      uint32_t c_tag = 0;
+      int c_g = 0, c_s = 0;
+      uint64_t c_e = 0;
+      const uint32_t done = __hip_atomic_load(&A.queue[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done < (uint32_t)A.B) {
+        for (int i = lane; i < (int)gridDim.x && !found; i += kWave) {
+          const int gg = (g + 1 + i) % (int)gridDim.x;
+          const uint64_t hw = ld_agent(H.hwg + gg);
+          const uint32_t t = (uint32_t)(hw >> 32), p = (uint32_t)hw;
+          if (t == 0 || p == 0) continue;
+          for (int s = (int)p + 1; s <= (int)p + 2 && s < nsteps && !found; ++s) {
+            const uint64_t e = ld_agent(H.hent + (int64_t)gg * nr + s);
+            if ((uint32_t)(e >> 32) < t) {
+              found = 1;
+              c_tag = t;
+              c_g = gg;
+              c_s = s;
+              c_e = e;
+            }
+          }
+        }
+      }
+      const uint64_t any = __ballot(found);
+      int state = done >= (uint32_t)A.B ? -1 : 0;  // -1 exit, 0 idle, 1 job
+      if (any) {
+        const int first = __ffsll((unsigned long long)any) - 1;
+        if (lane == first) {
+          uint64_t expect = c_e;
+          const uint64_t mine = ((uint64_t)c_tag << 32) | (kHelpClaimed << 30);
+          if (__hip_atomic_compare_exchange_strong(H.hent + (int64_t)c_g * nr + c_s, &expect, mine,
+                                                   __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)) {
+            // a record for the figures, taken once the row is this helper's
+            const uint32_t slot = atomicAdd(&A.queue[3], 1u);
+            state = 1;
+            Q.hjob_g = c_g;
+            Q.hjob_s = c_s;
+            Q.hjob_slot = (int32_t)(slot < H.hcap ? slot : kHelpNoRecord);
+            Q.hjob_tag = c_tag;
+          }
+          Q.hjob_state = state;
+        }
+      } else if (lane == 0) {
+        Q.hjob_state = state;
+      }
+      if (!any && state == 0) __builtin_amdgcn_s_sleep(32);
     }
+    block_sync_lds();
+    const int state = Q.hjob_state;
+    if (state < 0) break;
+    if (state == 0) {
+      block_sync_lds();  // Q.hjob_state is rewritten only after every wave has read it
+      continue;
+    }
+    const int64_t hb = (int64_t)Q.hjob_tag - 1;
+    const int ridx = step_slot<POOL>(Q.hjob_s, k);
+    bool no_row = false;
+    const uint16_t* row;
+    if constexpr (POOL) {
+      const int64_t pr = A.map.sidx(hb, ridx);
+      no_row = pr < 0;
+      row = A.map.template row<uint16_t>(no_row ? 0 : pr);
+    } else {
+      row = A.map.template row<uint16_t>(hb * nr + ridx);
+    }
+    hist_count_stream<PF, D>(hist, row, V, pf, false);
+    block_sync_lds();
+    if (hist_row_stats(hist, S, V, A.a, A.top_k, A.top_p, nullptr) == 2) {
+      block_sync_lds();
+      filter_row_bisect_call<uint16_t, true, NT>(row, V, A.a, A.top_k, A.top_p, &S.res, S.dslot,
+                                                  S.uslot);
+      __syncthreads();
+      hist_clear(hist);
+    }
+    if (TID() == 0) {
+      RowStat st = S.res;
+      if (no_row) st.valid = 0;
+      const uint32_t slot = (uint32_t)Q.hjob_slot;
+      if (slot != kHelpNoRecord) {
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(&st);
+        uint64_t* dst = reinterpret_cast<uint64_t*>(H.hpool + slot);
+        for (int i = 0; i < 4; ++i) st_agent(dst + i, src[i]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_max(H.hent + (int64_t)Q.hjob_g * nr + Q.hjob_s,
+                             ((uint64_t)Q.hjob_tag << 32) | (kHelpPublished << 30) | slot,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    block_sync_lds();  // S and Q.hjob read before the next round rewrites them
+  }
+
+  // The last workgroup out leaves the queue, the help entries and the used
+  // help records zero for the next call.
+  block_sync_lds();  // every wave has left the helping loop
+  if (TID() == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t out = atomicAdd(&A.queue[1], 1u);
+    Q.hmode = out == gridDim.x - 1 ? 1 : 0;
+  }
+  block_sync_lds();
+  if (Q.hmode) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const uint32_t used = min(__hip_atomic_load(&A.queue[3], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT), H.hcap);
+    const int64_t nent = (int64_t)gridDim.x * nr;
+    for (int64_t i = TID(); i < nent; i += NT) H.hent[i] = 0ull;
+    for (int i = TID(); i < (int)gridDim.x; i += NT) H.hwg[i] = 0ull;
+    uint4* pool4 = reinterpret_cast<uint4*>(H.hpool);
+    for (int64_t i = TID(); i < 2 * (int64_t)used; i += NT) pool4[i] = make_uint4(0u, 0u, 0u, 0u);
+    block_sync_lds();
+    if (TID() < 4) A.queue[TID()] = 0u;
   }
 }
 

@@ -132,8 +132,8 @@ def test_pooled_workspace_and_validation():
     and maps (all before any HIP call)."""
     L = sv.lib()
     s = sv.spec_sampling_t(1.0, 0, 0.95)
-    assert sv.workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, 160, 8192, 2048, 4, 151936, 1.0, 0, 0.95) > 0
-    assert sv.workspace_size_pooled(sv.SPEC_OP_GREEDY, 160, 0, 2048, 4, 151936) > 0
+    assert sv.workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, 160, 2048, 512, 4, 151936, 1.0, 0, 0.95) > 0
+    assert sv.workspace_size_pooled(sv.SPEC_OP_GREEDY, 160, 0, 512, 4, 151936) > 0
     assert L.spec_workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, 0, 8, 2, 4, 64, ctypes.byref(s)) == 0
     assert L.spec_workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, 8, 0, 2, 4, 64, ctypes.byref(s)) == 0
     assert L.spec_workspace_size_pooled(sv.SPEC_OP_PROCESS, 8, 8, 2, 4, 64, ctypes.byref(s)) == 0

@@ -157,7 +157,7 @@ def test_config4_parity_full_size_sampled():
 
 
 def test_config5_parity_full_size_sampled():
-    _sampled_full_size(5, 12, "c5 full size (B=2048), 12 checked")
+    _sampled_full_size(5, 12, "c5 full size (B=512), 12 checked")
 
 
 # ---------------------------------------------------------------------------

@@ -60,7 +60,7 @@ CONFIGS = {
               "f32", 0.8, 0, 1.0,
               recipe="target ~ N(0, 2^2) + Zipf-ranked bias -1.1 ln(v+1); "
                      "draft = target + N(0, 1.5^2); T=0.8, no filters"),
-    5: Config(5, "branch-fanout 32x16 k=4 V=151936 bf16 top-p 0.95", "stochastic", 2048, 4,
+    5: Config(5, "branch-fanout 32x16 k=4 V=151936 bf16 top-p 0.95", "stochastic", 512, 4,
               151936, "bf16", 1.0, 0, 0.95, branches=16,
               recipe="per request a base ~ N(0, 2^2) of [k+1][V] shared by its 16 branches as "
                      "their target; each branch's draft = base[:k] + N(0, 0.7^2); T=1, top-p 0.95"),
