@@ -297,6 +297,46 @@ def main():
            100 * achieved / PEAK_HBM_GBPS, PEAK_HBM_GBPS, ms_rows, achieved_rows,
            100 * achieved_rows / PEAK_HBM_GBPS, mean_acc))
 
+    # Branch fan-out: the same call with each request's target rows held once
+    # (pooled rows: 160 target rows for 32 requests instead of one copy per
+    # branch); identical decisions and draws, fewer bytes.
+    pooled = None
+    if c.branches > 1:
+        tgt0, drf0, uni0, toks0, big0 = sets[0]
+        k1 = c.k + 1
+        tpool = tgt0[::c.branches].contiguous().view(-1, c.V)
+        dpool = big0.view(-1, c.V)
+        bidx = torch.arange(c.B, device=dev, dtype=torch.int64)
+        tmap = ((bidx // c.branches)[:, None] * k1 + torch.arange(k1, device=dev)[None, :]).to(torch.int32)
+        dmap = (bidx[:, None] * (2 * c.k + 1) + k1 + torch.arange(c.k, device=dev)[None, :]).to(torch.int32)
+        pws = torch.zeros(sv.workspace_size_pooled(sv.SPEC_OP_STOCHASTIC, tpool.shape[0],
+                                                   dpool.shape[0], c.B, c.k, c.V, c.temperature,
+                                                   c.top_k, c.top_p), dtype=torch.uint8, device=dev)
+        pacc = torch.empty_like(acc)
+        pout = torch.empty_like(out)
+
+        def pstep():
+            sv.verify_stochastic_pooled(tpool, dpool, toks0, uni0, target_map=tmap, draft_map=dmap,
+                                        temperature=c.temperature, top_k=c.top_k, top_p=c.top_p,
+                                        out=(pacc, pout, None), workspace=pws, stream=stream)
+
+        step(0)
+        for _ in range(args.warmup):
+            pstep()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(pacc, acc) and torch.equal(pout, out))
+        ev0.record(stream)
+        for _ in range(args.steps):
+            pstep()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_p = ev0.elapsed_time(ev1) / args.steps
+        pooled = {"target_rows": int(tpool.shape[0]), "ms_per_step": ms_p,
+                  "value": positions / (ms_p / 1e3), "unit": "positions/s",
+                  "same_outputs_as_dense": same}
+        log("pooled rows (%d target rows): %.4f ms, %.4g positions/s, outputs %s"
+            % (tpool.shape[0], ms_p, positions / (ms_p / 1e3), "identical" if same else "DIFFER"))
+
     cpu = None
     if args.cpu_seconds > 0:
         log("cpu baseline: oracle on a bounded sample (~%.0f s of CPU work)" % args.cpu_seconds)
@@ -330,6 +370,8 @@ def main():
                                             "frac": achieved_rows / PEAK_HBM_GBPS}},
         "cpu_baseline": cpu,
     }
+    if pooled is not None:
+        line["pooled_rows"] = pooled
     print(json.dumps(line), flush=True)
 
 
