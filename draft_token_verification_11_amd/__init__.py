@@ -23,7 +23,7 @@ import torch
 
 __all__ = ["lib", "verify_stochastic", "verify_greedy", "logits_process", "workspace_size",
            "verify_stochastic_pooled", "verify_greedy_pooled", "workspace_size_pooled",
-           "tree_branches", "status_string", "SpecError", "library_path"]
+           "tree_branches", "outcome_lookup", "status_string", "SpecError", "library_path"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libspecverify.so")
@@ -90,6 +90,8 @@ def lib():
             L.spec_verify_greedy_pooled.argtypes = [spec_logits_t, i32, vp, vp, i32, i32, i32, vp,
                                                     vp, vp, sz, vp]
             L.spec_verify_greedy_pooled.restype = ctypes.c_int
+            L.spec_outcome_lookup.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp, vp]
+            L.spec_outcome_lookup.restype = ctypes.c_int
             L.spec_status_string.argtypes = [ctypes.c_int]
             L.spec_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -395,3 +397,28 @@ def tree_branches(parents, tokens, leaves=None):
     node_map = torch.tensor(paths, dtype=torch.int32)
     draft_tokens = torch.tensor([[tok[n] for n in p[1:]] for p in paths], dtype=torch.int32)
     return draft_tokens, node_map, node_map[:, :k].contiguous()
+
+
+def outcome_lookup(accepted_len: torch.Tensor, out_tokens: torch.Tensor, pred_len: torch.Tensor,
+                   pred_token: torch.Tensor, *, return_count: bool = True, stream=None):
+    """Predicted-outcome lookup after a verify call: for each sequence the
+    index of the first entry of its predicted set ([B][P] lengths and tokens,
+    a length < 0 is an empty entry) equal to its outcome (n, out_tokens[n]),
+    or -1.  Returns hit_index [B] and, on request, the hit count [1]."""
+    B = accepted_len.shape[0]
+    k = out_tokens.shape[1] - 1
+    P = pred_len.shape[1]
+    dev = accepted_len.device
+    acc = accepted_len.to(torch.int32).contiguous()
+    out = out_tokens.to(torch.int32).contiguous()
+    pl = pred_len.to(device=dev, dtype=torch.int32).contiguous()
+    pt = pred_token.to(device=dev, dtype=torch.int32).contiguous()
+    if tuple(out.shape) != (B, k + 1) or tuple(pl.shape) != (B, P) or tuple(pt.shape) != (B, P):
+        raise ValueError("expected accepted_len [B], out_tokens [B][k+1], predicted sets [B][P]")
+    hit = torch.empty(B, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev) if return_count else None
+    rc = lib().spec_outcome_lookup(acc.data_ptr(), out.data_ptr(), B, k, pl.data_ptr(),
+                                   pt.data_ptr(), P, hit.data_ptr(),
+                                   cnt.data_ptr() if cnt is not None else None, _stream(stream))
+    _check(rc, "spec_outcome_lookup")
+    return (hit, cnt) if return_count else hit

@@ -567,6 +567,25 @@ int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
   return finish_launch();
 }
 
+int spec_outcome_lookup(const int32_t* accepted_len, const int32_t* out_tokens, int32_t B,
+                        int32_t k, const int32_t* pred_len, const int32_t* pred_token,
+                        int32_t P, int32_t* hit_index, int32_t* hit_count, void* stream) {
+  int rc;
+  if ((rc = check_sizes(B, k, 1, true)) != SPEC_OK) return rc;
+  if (P < 1) return SPEC_ERR_INVALID_ARG;
+  if (P > 4096) return SPEC_ERR_UNSUPPORTED;
+  if (!accepted_len || !out_tokens || !pred_len || !pred_token || !hit_index)
+    return SPEC_ERR_INVALID_ARG;
+  auto st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(sv::k_outcome_lookup, dim3(unsigned((int64_t(B) + 3) / 4)), dim3(256), 0, st,
+                     accepted_len, out_tokens, int64_t(B), k, pred_len, pred_token, P, hit_index);
+  if (hit_count)
+    hipLaunchKernelGGL(sv::k_count_hits, dim3(1), dim3(1024), 0, st, hit_index, int64_t(B),
+                       hit_count);
+  return finish_launch();
+}
+
 const char* spec_status_string(int status) {
   switch (status) {
     case SPEC_OK: return "SPEC_OK";

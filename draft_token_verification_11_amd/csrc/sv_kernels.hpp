@@ -43,7 +43,7 @@ struct GPartial {  // 16 bytes: greedy partial of one V-chunk
   uint32_t pad;
 };
 constexpr uint32_t kFlagBad = 1u;
-constexpr int kDrawChunks = 16;  // chunk sums kept per wave by the residual draw
+constexpr int kDrawChunks = 8;  // chunk sums kept per wave by the residual draw
 
 // Rows of a call.  Dense layout (nt == 0): a sequence holds `per_seq` flat
 // rows, the first `k1` its target rows 0..k1-1 at (t_seq, t_pos), the rest
@@ -822,7 +822,10 @@ __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const
   const int64_t s1 = min(nsteps, s0 + spw);
   // Each wave's span is cut into at most kDrawChunks chunks of cs steps whose
   // sums are kept (csum[w][c], zero past the wave's last chunk), so the
-  // crossing is located from the table and one chunk is read again.
+  // crossing is located from the table and one chunk is read again.  A
+  // chunk's sum is each lane's fp64 share over the chunk's steps, reduced
+  // once across the wave; the second pass walks the same per-step values in
+  // step order (the two differ only in the order of fp64 additions).
   const int64_t cs = (spw + kDrawChunks - 1) / kDrawChunks;
 
   // Residual (or p) of the 8 elements of lane `lane` in step s; returns their
@@ -880,9 +883,10 @@ __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const
         float r8[8];
         const double ls = step_values(rp[v], rq[v], r8);
         if (s + v < s1) {
-          cacc += bcast(wave_incl_scan(ls), kWave - 1);
+          cacc += ls;  // this lane's share of the chunk
           if (s + v + 1 == cend || s + v + 1 == s1) {
-            if (lane == 0) csum[w * kDrawChunks + ci] = cacc;
+            const double tot = wave_sum(cacc);
+            if (lane == 0) csum[w * kDrawChunks + ci] = tot;
             ++ci;
             cacc = 0.0;
             cend += cs;
@@ -1774,6 +1778,46 @@ __global__ __launch_bounds__(256) void k_probs(RowMap map, int64_t V, int nchunk
 __global__ __launch_bounds__(256) void k_clear(uint4* __restrict__ p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Predicted-outcome lookup: one wave per sequence compares its outcome (n,
+// emitted token) with its predicted set, 64 entries at a time, and keeps the
+// first match; a second pass counts the hits.
+__global__ __launch_bounds__(256) void k_outcome_lookup(const int32_t* __restrict__ acc,
+                                                        const int32_t* __restrict__ out, int64_t B,
+                                                        int k, const int32_t* __restrict__ plen,
+                                                        const int32_t* __restrict__ ptok, int P,
+                                                        int32_t* __restrict__ hit) {
+  const int64_t b = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (b >= B) return;  // whole waves
+  const int32_t n = acc[b];
+  int32_t idx = -1;
+  if (n >= 0 && n <= k) {
+    const int32_t t = out[b * (k + 1) + n];
+    const int32_t* pl = plen + b * P;
+    const int32_t* pt = ptok + b * P;
+    for (int base = 0; base < P; base += kWave) {
+      const int i = base + lane;
+      const bool m = i < P && pl[i] == n && pt[i] == t;  // empty entries (< 0) never equal n
+      const uint64_t hits = __ballot(m);
+      if (hits) {
+        idx = base + __ffsll((unsigned long long)hits) - 1;
+        break;
+      }
+    }
+  }
+  if (lane == 0) hit[b] = idx;
+}
+
+__global__ __launch_bounds__(1024) void k_count_hits(const int32_t* __restrict__ hit, int64_t B,
+                                                     int32_t* __restrict__ count) {
+  __shared__ uint32_t slots[1024 / kWave];
+  uint32_t c = 0;
+  for (int64_t i = threadIdx.x; i < B; i += 1024) c += hit[i] >= 0 ? 1u : 0u;
+  const uint32_t total = block_sum<1024>(c, slots);
+  if (threadIdx.x == 0) *count = (int32_t)total;
 }
 
 }  // namespace sv

@@ -202,6 +202,29 @@ int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
                               int32_t* out_tokens, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Predicted-outcome lookup, the step after verify in speculative
+ * speculative decoding ("Speculative Speculative Decoding", ai-stack.site
+ * summary, section 1 on its novelty, 研究创新性, and section 2 on its
+ * theory, 理论贡献与关键假设): while the target verifies, the proposer
+ * prepares drafts for a set of likely verification outcomes; when the actual
+ * outcome is in the set the prepared draft is used at once (a hit), and the
+ * share of hits is the speculation cache hit rate.
+ *
+ * Reading: the outcome of sequence b is the pair (n, t) with n =
+ * accepted_len[b] and t = out_tokens[b][n] (the corrected or bonus token);
+ * with the drafts fixed it determines the emitted string.
+ *   accepted_len  [B] int32, out_tokens [B][k+1] int32: a verify call's outputs
+ *   pred_len      [B][P] int32: predicted accepted lengths; an entry < 0 is empty
+ *   pred_token    [B][P] int32: predicted emitted tokens
+ *   hit_index     [B] int32 out: the first i with pred_len[b][i] == n and
+ *                 pred_token[b][i] == t, or -1 (also -1 for an invalid
+ *                 sequence, n < 0, and for n > k)
+ *   hit_count     [1] int32 out or NULL: the number of sequences with a hit
+ * 1 <= B <= 2^24, 1 <= k <= SPEC_MAX_K, 1 <= P <= 4096.  No workspace. */
+int spec_outcome_lookup(const int32_t* accepted_len, const int32_t* out_tokens, int32_t B,
+                        int32_t k, const int32_t* pred_len, const int32_t* pred_token,
+                        int32_t P, int32_t* hit_index, int32_t* hit_count, void* stream);
+
 /* Static description of a status code. */
 const char* spec_status_string(int status);
 

@@ -291,3 +291,30 @@ def verify_stochastic_pooled(target_pool, target_map, draft_pool, draft_map, tok
 
 def verify_greedy_pooled(target_pool, target_map, tokens):
     return default().verify_greedy_pooled(target_pool, target_map, tokens)
+
+
+def outcome_lookup(accepted_len, out_tokens, pred_len, pred_token):
+    """Predicted-outcome lookup ("Speculative Speculative Decoding", ai-stack.site
+    summary, sections 1 and 2: the proposer prepares drafts for a set of likely
+    verification outcomes; the actual outcome either is in the set, a hit, or
+    not).  The outcome of sequence b is (n, out_tokens[b][n]) with n =
+    accepted_len[b]; returns (hit_index [B], hit count): the first matching
+    entry of the sequence's set, or -1 (also for an invalid sequence).  Plain
+    loops."""
+    acc = [int(x) for x in np.asarray(accepted_len).reshape(-1)]
+    out = np.asarray(out_tokens)
+    pl = np.asarray(pred_len)
+    pt = np.asarray(pred_token)
+    k = out.shape[1] - 1
+    hits = []
+    for b, n in enumerate(acc):
+        found = -1
+        if 0 <= n <= k:
+            t = int(out[b][n])
+            for i in range(pl.shape[1]):
+                if int(pl[b][i]) == n and int(pt[b][i]) == t:
+                    found = i
+                    break
+        hits.append(found)
+    hits = np.array(hits, np.int32)
+    return hits, int((hits >= 0).sum())

@@ -483,6 +483,34 @@ def pin_pooled_rows(orc):
                                       [-1, -1, -1], [2, 0, -1]], out
 
 
-ALL_PINS = [pin_pooled_rows, pin_worked_example, pin_law_of_decision_map, pin_softmax_and_filters,
+# ---------------------------------------------------------------------------
+def pin_outcome_lookup(orc, lookup=None):
+    """Predicted-outcome lookup on the worked example's outcomes: drafting B
+    and drawing u0 = 0.8 rejects it and emits A (outcome (0, A)); u0 = 0.7
+    accepts it and the bonus draw u1 = 0 from p emits A (outcome (1, A)).
+    First match wins, empty entries never match, an invalid sequence never
+    hits."""
+    import oracle as _oracle
+    lookup = lookup or _oracle.outcome_lookup
+    target, draft, _ = worked_example()
+    tt = np.ascontiguousarray(np.broadcast_to(target, (3, 2, 3)))
+    dd = np.ascontiguousarray(np.broadcast_to(draft, (3, 1, 3)))
+    toks = np.array([[1], [1], [7]], np.int32)  # sequence 2: token out of range (invalid)
+    u = np.array([[0.8, 0.5], [0.7, 0.0], [0.1, 0.1]], np.float32)
+    r = orc.verify_stochastic(tt, dd, toks, u)
+    assert list(r["accepted_len"]) == [0, 1, -1]
+    assert [list(x) for x in r["out_tokens"][:2]] == [[0, -1], [1, 0]]
+    pred_len = np.array([[1, 0, 0, -1], [0, 1, 1, 1], [-1, 0, 1, -1]], np.int32)
+    pred_tok = np.array([[0, 1, 0, 0], [0, 2, 0, 0], [-1, 0, 0, -1]], np.int32)
+    hits, count = lookup(r["accepted_len"], r["out_tokens"], pred_len, pred_tok)
+    assert list(hits) == [2, 2, -1], hits
+    assert count == 2
+    # a miss, and an empty entry (length -1) that names the outcome's token
+    hits, count = lookup(r["accepted_len"][:1], r["out_tokens"][:1], np.array([[-1, 1, 0]]),
+                         np.array([[0, 0, 1]]))
+    assert list(hits) == [-1] and count == 0
+
+
+ALL_PINS = [pin_outcome_lookup, pin_pooled_rows, pin_worked_example, pin_law_of_decision_map, pin_softmax_and_filters,
             pin_acceptance_rate, pin_special_cases, pin_greedy, pin_bf16_decode,
             pin_invalid_inputs, pin_boundary_flags, pin_chi_square]

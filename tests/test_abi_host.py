@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "spec_logits_process", "spec_status_string", "spec_verify_greedy",
+        "spec_logits_process", "spec_outcome_lookup", "spec_status_string", "spec_verify_greedy",
         "spec_verify_greedy_pooled", "spec_verify_stochastic", "spec_verify_stochastic_pooled",
         "spec_workspace_size", "spec_workspace_size_pooled"])
 
@@ -186,3 +186,20 @@ def test_tree_branches():
         sv.tree_branches([-1, 2, 0], [0, 1, 2])             # parent after its child
     with pytest.raises(ValueError):
         sv.tree_branches([0, 0], [0, 1])                    # no root
+
+
+
+def test_outcome_lookup_validation():
+    L = sv.lib()
+    p = ctypes.c_void_p(4096)
+
+    def call(B=4, k=4, P=8, acc=p, out=p, pl=p, pt=p, hit=p):
+        return L.spec_outcome_lookup(acc, out, B, k, pl, pt, P, hit, None, None)
+
+    assert call(B=0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(k=0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(k=65) == sv.SPEC_ERR_UNSUPPORTED
+    assert call(P=0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(P=4097) == sv.SPEC_ERR_UNSUPPORTED
+    for name in ("acc", "out", "pl", "pt", "hit"):
+        assert call(**{name: None}) == sv.SPEC_ERR_INVALID_ARG, name

@@ -99,3 +99,38 @@ def test_pins_catch_pool_mutation(name):
     orc = POOL_MUTATIONS[name](oracle.default().lib)
     with pytest.raises(AssertionError):
         pins.pin_pooled_rows(orc)
+
+
+# Mistakes planted in the predicted-outcome lookup.
+def _lookup_last(acc, out, pl, pt):
+    acc, out, pl, pt = (np.asarray(x) for x in (acc, out, pl, pt))
+    hits = []
+    for b, n in enumerate(acc.reshape(-1)):
+        m = [i for i in range(pl.shape[1]) if 0 <= n < out.shape[1] and pl[b][i] == n and pt[b][i] == out[b][n]]
+        hits.append(m[-1] if m else -1)
+    hits = np.array(hits)
+    return hits, int((hits >= 0).sum())
+
+
+def _lookup_token_ignored(acc, out, pl, pt):
+    acc, pl = np.asarray(acc).reshape(-1), np.asarray(pl)
+    hits = np.array([next((i for i in range(pl.shape[1]) if n >= 0 and pl[b][i] == n), -1)
+                     for b, n in enumerate(acc)])
+    return hits, int((hits >= 0).sum())
+
+
+def _lookup_empty_matches(acc, out, pl, pt):
+    acc, out, pl, pt = (np.asarray(x) for x in (acc, out, pl, pt))
+    hits = []
+    for b, n in enumerate(acc.reshape(-1)):
+        t = out[b][n] if 0 <= n < out.shape[1] else None
+        hits.append(next((i for i in range(pl.shape[1]) if t is not None and (pl[b][i] == n or pl[b][i] < 0) and pt[b][i] == t), -1))
+    hits = np.array(hits)
+    return hits, int((hits >= 0).sum())
+
+
+@pytest.mark.parametrize("mutant", [_lookup_last, _lookup_token_ignored, _lookup_empty_matches],
+                         ids=lambda f: f.__name__)
+def test_pins_catch_lookup_mutation(mutant):
+    with pytest.raises(AssertionError):
+        pins.pin_outcome_lookup(oracle.default(), lookup=mutant)
