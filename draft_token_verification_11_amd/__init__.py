@@ -23,7 +23,8 @@ import torch
 
 __all__ = ["lib", "verify_stochastic", "verify_greedy", "logits_process", "workspace_size",
            "verify_stochastic_pooled", "verify_greedy_pooled", "workspace_size_pooled",
-           "tree_branches", "outcome_lookup", "status_string", "SpecError", "library_path"]
+           "tree_branches", "outcome_lookup", "logits_apply", "status_string", "SpecError",
+           "library_path"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libspecverify.so")
@@ -42,6 +43,13 @@ class spec_logits_t(ctypes.Structure):
 class spec_sampling_t(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
                 ("top_p", ctypes.c_float)]
+
+
+class spec_processors_t(ctypes.Structure):
+    _fields_ = [("allow", ctypes.c_void_p), ("allow_seq_stride", ctypes.c_int64),
+                ("allow_pos_stride", ctypes.c_int64), ("penalize", ctypes.c_void_p),
+                ("pen_seq_stride", ctypes.c_int64), ("pen_pos_stride", ctypes.c_int64),
+                ("theta", ctypes.c_float)]
 
 
 class SpecError(RuntimeError):
@@ -90,6 +98,9 @@ def lib():
             L.spec_verify_greedy_pooled.argtypes = [spec_logits_t, i32, vp, vp, i32, i32, i32, vp,
                                                     vp, vp, sz, vp]
             L.spec_verify_greedy_pooled.restype = ctypes.c_int
+            L.spec_logits_apply.argtypes = [spec_logits_t, i32, i32, i32, P(spec_processors_t),
+                                            spec_logits_t, vp]
+            L.spec_logits_apply.restype = ctypes.c_int
             L.spec_outcome_lookup.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp, vp]
             L.spec_outcome_lookup.restype = ctypes.c_int
             L.spec_status_string.argtypes = [ctypes.c_int]
@@ -422,3 +433,46 @@ def outcome_lookup(accepted_len: torch.Tensor, out_tokens: torch.Tensor, pred_le
                                    cnt.data_ptr() if cnt is not None else None, _stream(stream))
     _check(rc, "spec_outcome_lookup")
     return (hit, cnt) if return_count else hit
+
+
+def _mask_rows(m, S, rows, W, dev):
+    """(pointer, seq stride, pos stride) of bitmask rows [S|1][rows|1][W] (int32 words)."""
+    if m is None:
+        return None, 0, 0, None
+    if m.dim() != 3 or m.shape[2] != W or m.dtype != torch.int32 or m.stride(2) != 1:
+        raise ValueError("bitmask rows must be int32 [S|1][rows|1][%d] with contiguous words" % W)
+    if m.device != dev:
+        raise ValueError("bitmask rows must live on the logits' device")
+    if m.shape[0] not in (1, S) or m.shape[1] not in (1, rows):
+        raise ValueError("bitmask rows do not broadcast to [%d][%d]" % (S, rows))
+    ss = m.stride(0) if m.shape[0] == S and S > 1 else 0
+    ps = m.stride(1) if m.shape[1] == rows and rows > 1 else 0
+    return m.data_ptr(), ss, ps, m
+
+
+def logits_apply(logits: torch.Tensor, *, allow: torch.Tensor | None = None,
+                 penalize: torch.Tensor | None = None, theta: float = 1.0,
+                 out: torch.Tensor | None = None, out_dtype: torch.dtype | None = None,
+                 stream=None) -> torch.Tensor:
+    """Logits processors on [S][rows][V] logits: tokens outside the allow
+    mask get -inf, penalised tokens l / theta (l > 0) or l * theta.  Masks
+    are int32 words [S|1][rows|1][ceil(V/32)] (bit x % 32 of word x / 32).
+    Writes `out` (default: a new tensor of out_dtype, default the input's;
+    `out=logits` works in place) and returns it."""
+    if logits.dim() != 3 or not logits.is_cuda or logits.stride(2) != 1:
+        raise ValueError("logits must be a device tensor [S][rows][V] with a contiguous last axis")
+    S, rows, V = logits.shape
+    W = (V + 31) // 32
+    dev = logits.device
+    if out is None:
+        out = torch.empty((S, rows, V), dtype=out_dtype or logits.dtype, device=dev)
+    if tuple(out.shape) != (S, rows, V) or out.stride(2) != 1:
+        raise ValueError("out must be [S][rows][V] with a contiguous last axis")
+    ap, a_s, a_p, _a = _mask_rows(allow, S, rows, W, dev)
+    pp, p_s, p_p, _p = _mask_rows(penalize, S, rows, W, dev)
+    proc = spec_processors_t(ap, a_s, a_p, pp, p_s, p_p, float(theta))
+    src = spec_logits_t(logits.data_ptr(), _dtype_code(logits), 0, logits.stride(0), logits.stride(1))
+    dst = spec_logits_t(out.data_ptr(), _dtype_code(out), 0, out.stride(0), out.stride(1))
+    rc = lib().spec_logits_apply(src, S, rows, V, ctypes.byref(proc), dst, _stream(stream))
+    _check(rc, "spec_logits_apply")
+    return out

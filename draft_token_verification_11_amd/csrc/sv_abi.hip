@@ -362,6 +362,12 @@ struct PooledStochasticRun {
   }
 };
 
+template <typename TI, typename TO>
+void launch_apply(bool vec, unsigned nblk, const sv::ApplyArgs& A, hipStream_t st) {
+  if (vec) hipLaunchKernelGGL((sv::k_logits_apply<TI, TO, true>), dim3(nblk), dim3(256), 0, st, A);
+  else hipLaunchKernelGGL((sv::k_logits_apply<TI, TO, false>), dim3(nblk), dim3(256), 0, st, A);
+}
+
 int finish_launch() {
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
@@ -564,6 +570,38 @@ int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
   const int64_t words = L.rows * L.nchunks;  // 16 bytes each
   hipLaunchKernelGGL(sv::k_clear, dim3(unsigned((words + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<uint4*>(part), words);
+  return finish_launch();
+}
+
+int spec_logits_apply(spec_logits_t in, int32_t S, int32_t rows, int32_t V,
+                      const spec_processors_t* proc, spec_logits_t out, void* stream) {
+  int rc;
+  if ((rc = check_sizes(S, 1, V, false)) != SPEC_OK) return rc;
+  if (rows < 1) return SPEC_ERR_INVALID_ARG;
+  if (rows > 2 * SPEC_MAX_K + 1) return SPEC_ERR_UNSUPPORTED;
+  if (!proc) return SPEC_ERR_INVALID_ARG;
+  if (!std::isfinite(proc->theta) || !(proc->theta > 0.0f)) return SPEC_ERR_INVALID_ARG;
+  if ((rc = check_logits(in, V)) != SPEC_OK) return rc;
+  if ((rc = check_logits(out, V)) != SPEC_OK) return rc;
+  if (proc->allow_seq_stride < 0 || proc->allow_pos_stride < 0 || proc->pen_seq_stride < 0 ||
+      proc->pen_pos_stride < 0)
+    return SPEC_ERR_INVALID_ARG;
+  const int64_t nch = (int64_t(V) + 2047) / 2048;
+  const int64_t blocks = int64_t(S) * rows * nch;
+  if (!grid_fits(blocks, 256)) return SPEC_ERR_UNSUPPORTED;
+  sv::ApplyArgs A{in.data, in.seq_stride, in.pos_stride, const_cast<void*>(out.data),
+                  out.seq_stride, out.pos_stride, rows, int64_t(V), int(nch), proc->allow,
+                  proc->allow_seq_stride, proc->allow_pos_stride, proc->penalize,
+                  proc->pen_seq_stride, proc->pen_pos_stride, proc->theta};
+  const bool vec = vec_ok(in) && vec_ok(out);
+  auto st = static_cast<hipStream_t>(stream);
+  const unsigned nblk = unsigned(blocks);
+  (void)hipGetLastError();
+  const bool ib = in.dtype == SPEC_DTYPE_BF16, ob = out.dtype == SPEC_DTYPE_BF16;
+  if (ib && ob) launch_apply<uint16_t, uint16_t>(vec, nblk, A, st);
+  else if (ib) launch_apply<uint16_t, float>(vec, nblk, A, st);
+  else if (ob) launch_apply<float, uint16_t>(vec, nblk, A, st);
+  else launch_apply<float, float>(vec, nblk, A, st);
   return finish_launch();
 }
 

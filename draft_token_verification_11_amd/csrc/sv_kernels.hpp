@@ -1820,4 +1820,76 @@ __global__ __launch_bounds__(1024) void k_count_hits(const int32_t* __restrict__
   if (threadIdx.x == 0) *count = (int32_t)total;
 }
 
+// ---------------------------------------------------------------------------
+// Logits processors: allow mask (-inf outside it) and repetition penalty (l /
+// theta for l > 0, l * theta otherwise, on the penalised tokens), 8 elements
+// per thread, 2048 per workgroup; bf16 output rounded to nearest even.
+struct ApplyArgs {
+  const void* in;
+  int64_t in_seq, in_pos;
+  void* out;
+  int64_t out_seq, out_pos;
+  int32_t rows;
+  int64_t V;
+  int nchunks;
+  const uint32_t* allow;
+  int64_t a_seq, a_pos;
+  const uint32_t* pen;
+  int64_t p_seq, p_pos;
+  float theta;
+};
+
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  if (__builtin_isnan(f)) return 0x7FC0u;
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+template <typename TI, typename TO, bool VEC>
+__global__ __launch_bounds__(256) void k_logits_apply(ApplyArgs A) {
+  const int64_t blk = blockIdx.x;
+  const int64_t r = blk / A.nchunks;
+  const int64_t c = blk - r * A.nchunks;
+  const int64_t s = r / A.rows, j = r - s * A.rows;
+  const int64_t e0 = c * 2048 + (int64_t)threadIdx.x * 8;
+  if (e0 >= A.V) return;
+  const TI* row = reinterpret_cast<const TI*>(A.in) + s * A.in_seq + j * A.in_pos;
+  Raw8<TI> raw;
+  load8_raw<TI, VEC>(row, e0, A.V, raw);
+  float l[8];
+  unpack8<TI>(raw, l);
+  // e0 is a multiple of 8: the 8 bits lie in one word
+  const uint32_t sh = (uint32_t)(e0 & 31);
+  const uint32_t aw = A.allow ? (A.allow[s * A.a_seq + j * A.a_pos + (e0 >> 5)] >> sh) : 0xFFu;
+  const uint32_t pw = A.pen ? (A.pen[s * A.p_seq + j * A.p_pos + (e0 >> 5)] >> sh) : 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v = l[i];
+    if (!((aw >> i) & 1u)) v = -__builtin_inff();
+    else if ((pw >> i) & 1u) v = v > 0.0f ? v / A.theta : v * A.theta;
+    l[i] = v;
+  }
+  const int64_t n = A.V - e0 < 8 ? A.V - e0 : 8;
+  if constexpr (sizeof(TO) == 4) {
+    float* o = reinterpret_cast<float*>(A.out) + s * A.out_seq + j * A.out_pos + e0;
+    if (VEC && n == 8) {
+      *reinterpret_cast<float4*>(o) = make_float4(l[0], l[1], l[2], l[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(l[4], l[5], l[6], l[7]);
+    } else {
+      for (int i = 0; i < n; ++i) o[i] = l[i];
+    }
+  } else {
+    uint16_t* o = reinterpret_cast<uint16_t*>(A.out) + s * A.out_seq + j * A.out_pos + e0;
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = bf16_rne(l[i]);
+    if (VEC && n == 8) {
+      *reinterpret_cast<uint4*>(o) = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                                h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+    } else {
+      for (int i = 0; i < n; ++i) o[i] = (uint16_t)h[i];
+    }
+  }
+}
+
 }  // namespace sv

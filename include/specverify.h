@@ -202,6 +202,43 @@ int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
                               int32_t* out_tokens, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Logits processors applied before verification.  The encyclopedia entry's
+ * section "Basic steps of proposal and verification" requires the target and
+ * proposal distributions to be computed under every processing rule in force
+ * -- naming repetition penalty, vocabulary masking and structured-output
+ * constraints beside temperature, top-k and nucleus -- and consistently in
+ * the correction step.  spec_logits_apply applies the first three to rows of
+ * logits; applying the same processor rows to the target and draft logits of
+ * a position, then calling a verify entry point, meets that requirement.
+ *
+ * Bitmask rows: bit (x % 32) of word (x / 32) refers to token x; the row of
+ * (s, j) starts at words + s * seq_stride + j * pos_stride (strides in
+ * 32-bit words; 0 broadcasts).  A structured-output constraint is a
+ * per-position allow mask.
+ *
+ * Readings: a token whose allow bit is 0 gets logit -inf; a token whose
+ * penalise bit is 1 (one already in the sequence's history) gets l / theta
+ * if l > 0, else l * theta (the repetition penalty of Keskar et al., 2019),
+ * computed in fp32; masking comes first; NaN and +inf pass unchanged (the
+ * verify marks such rows invalid).  A bf16 output rounds to nearest even. */
+typedef struct {
+  const uint32_t* allow;     /* allow-mask rows, or NULL (every token allowed) */
+  int64_t allow_seq_stride;  /* words */
+  int64_t allow_pos_stride;  /* words */
+  const uint32_t* penalize;  /* penalise-mask rows, or NULL (no penalty) */
+  int64_t pen_seq_stride;    /* words */
+  int64_t pen_pos_stride;    /* words */
+  float theta;               /* repetition penalty, finite and > 0 (1 = none) */
+} spec_processors_t;
+
+/* Applies the processors to S x rows logits rows: row (s, j) of `in`
+ * (spec_logits_t addressing) is processed with bitmask row (s, j) and written
+ * to row (s, j) of `out` (F32 or BF16; out may be in itself, same strides).
+ * 1 <= S <= 2^24, 1 <= rows <= 2 * SPEC_MAX_K + 1, 1 <= V <= SPEC_MAX_V. */
+int spec_logits_apply(spec_logits_t in, int32_t S, int32_t rows, int32_t V,
+                      const spec_processors_t* proc /* host */, spec_logits_t out,
+                      void* stream);
+
 /* Predicted-outcome lookup, the step after verify in speculative
  * speculative decoding ("Speculative Speculative Decoding", ai-stack.site
  * summary, section 1 on its novelty, 研究创新性, and section 2 on its

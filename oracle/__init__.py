@@ -318,3 +318,48 @@ def outcome_lookup(accepted_len, out_tokens, pred_len, pred_token):
         hits.append(found)
     hits = np.array(hits, np.int32)
     return hits, int((hits >= 0).sum())
+
+
+def _bits(words, V):
+    """Token bits of bitmask rows [..][ceil(V/32)] (uint32 words) -> bool [..][V]."""
+    w = np.asarray(words).astype(np.uint32)
+    x = np.arange(V)
+    return ((w[..., x // 32] >> (x % 32).astype(np.uint32)) & 1).astype(bool)
+
+
+def _bf16_decode(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
+
+
+def _bf16_round(f):
+    """float32 -> bfloat16 bits, round to nearest even (NaN -> 0x7FC0)."""
+    f = np.asarray(f, np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+    return np.where(np.isnan(f), np.uint16(0x7FC0), r)
+
+
+def apply_processors(logits, allow=None, penalize=None, theta=1.0, out_dtype=None):
+    """Logits processors in the order the verify step's rule requires them to
+    be in force (the encyclopedia entry "Speculative decoding", section on
+    the basic steps of proposal and verification, names repetition penalty,
+    vocabulary masking and structured-output constraints): a token outside
+    the allow mask gets -inf; a penalised token gets l / theta if l > 0, else
+    l * theta, in float32.  logits: [S][rows][V] float32 or uint16 (bf16
+    bits); masks: uint32 words [S][rows][W] (broadcastable).  Returns float32,
+    or bf16 bits rounded to nearest even when out_dtype is "bf16"."""
+    a = np.asarray(logits)
+    V = a.shape[-1]
+    f = _bf16_decode(a) if a.dtype == np.uint16 else a.astype(np.float32).copy()
+    th = np.float32(theta)
+    ok = np.ones(f.shape, bool) if allow is None else np.broadcast_to(_bits(allow, V), f.shape)
+    pen = np.zeros(f.shape, bool) if penalize is None else np.broadcast_to(_bits(penalize, V), f.shape)
+    out = f.copy()
+    with np.errstate(invalid="ignore"):
+        pos = f > 0
+        out = np.where(pen & pos, (f / th).astype(np.float32), out)
+        out = np.where(pen & ~pos, (f * th).astype(np.float32), out)
+    out = np.where(ok, out, np.float32(-np.inf)).astype(np.float32)
+    if out_dtype == "bf16":
+        return _bf16_round(out)
+    return out

@@ -511,6 +511,39 @@ def pin_outcome_lookup(orc, lookup=None):
     assert list(hits) == [-1] and count == 0
 
 
-ALL_PINS = [pin_outcome_lookup, pin_pooled_rows, pin_worked_example, pin_law_of_decision_map, pin_softmax_and_filters,
+# ---------------------------------------------------------------------------
+def pin_logits_processors(orc, apply=None):
+    """Processors the rule requires to be in force on both sides: a masked
+    token gets -inf (probability 0 after processing), a penalised token
+    l / theta for l > 0 and l * theta otherwise (the repetition-penalty
+    reading), NaN passes unchanged; bf16 output rounds to nearest even; no
+    mask and theta = 1 change nothing."""
+    import oracle as _oracle
+    apply = apply or _oracle.apply_processors
+    l = np.array([[[2.0, -2.0, 3.0, -1.5, 0.0, np.nan, 1.00390625, 5.0]]], np.float32)
+    allow = np.array([[[0b11111011]]], np.uint32)   # token 2 masked
+    pen = np.array([[[0b00110011]]], np.uint32)     # tokens 0, 1, 4, 5 penalised
+    got = apply(l, allow, pen, 2.0)
+    want = np.array([1.0, -4.0, -np.inf, -1.5, 0.0, np.nan, 1.00390625, 5.0], np.float32)
+    assert np.array_equal(got[0, 0], want, equal_nan=True), got
+    # ties to even: 1 + 2^-8 -> 1.0 (0x3F80); 1 + 3 * 2^-8 -> 1 + 2^-6 (0x3F82)
+    b = apply(np.array([[[1.00390625, 1.01171875, -3.0]]], np.float32), None, None, 1.0, "bf16")
+    assert list(b[0, 0]) == [0x3F80, 0x3F82, 0xC040], b
+    rs = np.random.default_rng(5)
+    x = rs.normal(0, 2, (2, 3, 70)).astype(np.float32)
+    assert np.array_equal(apply(x, None, None, 1.0), x)
+    # masked tokens get probability 0 after processing, and the rest renormalise
+    m = np.zeros((1, 1, 3), np.uint32)
+    m[0, 0, :] = 0xFFFFFFFF
+    m[0, 0, 1] &= ~np.uint32(1 << 3)  # token 35 masked
+    y = apply(x[:1, :1], m, None, 1.0)
+    ok, p, _ = orc.process_row(y[0, 0])
+    ok0, p0, _ = orc.process_row(x[0, 0])
+    assert ok and ok0 and p[35] == 0.0
+    keep = np.arange(70) != 35
+    assert np.allclose(p[keep], p0[keep] / p0[keep].sum(), rtol=1e-12)
+
+
+ALL_PINS = [pin_logits_processors, pin_outcome_lookup, pin_pooled_rows, pin_worked_example, pin_law_of_decision_map, pin_softmax_and_filters,
             pin_acceptance_rate, pin_special_cases, pin_greedy, pin_bf16_decode,
             pin_invalid_inputs, pin_boundary_flags, pin_chi_square]

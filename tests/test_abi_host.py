@@ -22,7 +22,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "spec_logits_process", "spec_outcome_lookup", "spec_status_string", "spec_verify_greedy",
+        "spec_logits_apply", "spec_logits_process", "spec_outcome_lookup", "spec_status_string",
+        "spec_verify_greedy",
         "spec_verify_greedy_pooled", "spec_verify_stochastic", "spec_verify_stochastic_pooled",
         "spec_workspace_size", "spec_workspace_size_pooled"])
 
@@ -203,3 +204,24 @@ def test_outcome_lookup_validation():
     assert call(P=4097) == sv.SPEC_ERR_UNSUPPORTED
     for name in ("acc", "out", "pl", "pt", "hit"):
         assert call(**{name: None}) == sv.SPEC_ERR_INVALID_ARG, name
+
+
+
+def test_logits_apply_validation():
+    L = sv.lib()
+    desc = sv.spec_logits_t(4096, 0, 0, 5 * 1024, 1024)
+
+    def call(S=2, rows=5, V=1024, theta=1.0, src=desc, dst=desc, proc=True, stride=0):
+        pr = sv.spec_processors_t(None, stride, 0, None, 0, 0, theta)
+        return L.spec_logits_apply(src, S, rows, V, ctypes.byref(pr) if proc else None, dst, None)
+
+    assert call(S=0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(rows=0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(rows=130) == sv.SPEC_ERR_UNSUPPORTED
+    assert call(V=0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(proc=False) == sv.SPEC_ERR_INVALID_ARG
+    for th in (0.0, -1.0, float("nan"), float("inf")):
+        assert call(theta=th) == sv.SPEC_ERR_INVALID_ARG
+    assert call(stride=-1) == sv.SPEC_ERR_INVALID_ARG
+    assert call(dst=sv.spec_logits_t(4096, 9, 0, 5 * 1024, 1024)) == sv.SPEC_ERR_UNSUPPORTED
+    assert call(src=sv.spec_logits_t(4096, 0, 0, 5 * 1024, 1000)) == sv.SPEC_ERR_INVALID_ARG

@@ -134,3 +134,31 @@ def _lookup_empty_matches(acc, out, pl, pt):
 def test_pins_catch_lookup_mutation(mutant):
     with pytest.raises(AssertionError):
         pins.pin_outcome_lookup(oracle.default(), lookup=mutant)
+
+
+# Mistakes planted in the logits processors.
+def _apply_penalty_sign_blind(logits, allow=None, penalize=None, theta=1.0, out_dtype=None):
+    out = oracle.apply_processors(logits, allow, None, 1.0)
+    if penalize is not None:
+        pen = np.broadcast_to(oracle._bits(penalize, out.shape[-1]), out.shape)
+        out = np.where(pen & np.isfinite(out), (out / np.float32(theta)).astype(np.float32), out)
+    return oracle._bf16_round(out) if out_dtype == "bf16" else out
+
+
+def _apply_mask_inverted(logits, allow=None, penalize=None, theta=1.0, out_dtype=None):
+    inv = None if allow is None else ~np.asarray(allow, np.uint32)
+    return oracle.apply_processors(logits, inv, penalize, theta, out_dtype)
+
+
+def _apply_truncating_bf16(logits, allow=None, penalize=None, theta=1.0, out_dtype=None):
+    out = oracle.apply_processors(logits, allow, penalize, theta)
+    if out_dtype == "bf16":
+        return (out.view(np.uint32) >> 16).astype(np.uint16)
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_apply_penalty_sign_blind, _apply_mask_inverted,
+                                    _apply_truncating_bf16], ids=lambda f: f.__name__)
+def test_pins_catch_processor_mutation(mutant):
+    with pytest.raises(AssertionError):
+        pins.pin_logits_processors(oracle.default(), apply=mutant)
