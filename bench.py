@@ -337,6 +337,59 @@ def main():
         log("pooled rows (%d target rows): %.4f ms, %.4g positions/s, outputs %s"
             % (tpool.shape[0], ms_p, positions / (ms_p / 1e3), "identical" if same else "DIFFER"))
 
+    # The next rows built beside the verify: logits processors over every row
+    # of the input set (allow mask per position, repetition penalty per
+    # sequence) and the predicted-outcome lookup on the call's outputs.
+    next_rows = {}
+    if c.dtype == "bf16":
+        big0 = sets[0][4]
+        W = (c.V + 31) // 32
+        g = torch.Generator(device=dev).manual_seed(1234)
+        allow = torch.randint(-2**31, 2**31 - 1, (c.B, 2 * c.k + 1, W), dtype=torch.int32,
+                              device=dev, generator=g)
+        pen = torch.randint(-2**31, 2**31 - 1, (c.B, 1, W), dtype=torch.int32, device=dev,
+                            generator=g) & 0x01010101
+        pout = torch.empty_like(big0)
+
+        def apply_step():
+            sv.logits_apply(big0, allow=allow, penalize=pen, theta=1.2, out=pout, stream=stream)
+
+        apply_step()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            apply_step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_a = ev0.elapsed_time(ev1) / args.steps
+        nelem = big0.numel()
+        a_bytes = nelem * esize * 2 + allow.numel() * 4 + pen.numel() * 4
+        next_rows["logits_apply"] = {
+            "kernel": "k_logits_apply", "ms": ms_a, "bytes": a_bytes,
+            "achieved_GBps": a_bytes / (ms_a / 1e3) / 1e9,
+            "frac": a_bytes / (ms_a / 1e3) / 1e9 / PEAK_HBM_GBPS,
+            "rows": c.B * (2 * c.k + 1)}
+        P = 16
+        pl = torch.randint(-1, c.k + 1, (c.B, P), dtype=torch.int32, device=dev, generator=g)
+        pt = torch.randint(0, c.V, (c.B, P), dtype=torch.int32, device=dev, generator=g)
+        step(0)
+        pl[:, 0] = acc
+        pt[:, 0] = out.gather(1, acc.clamp(min=0).long().unsqueeze(1)).squeeze(1)
+        hits, cnt = sv.outcome_lookup(acc, out, pl, pt, stream=stream)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            sv.outcome_lookup(acc, out, pl, pt, stream=stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        next_rows["outcome_lookup"] = {"kernels": "k_outcome_lookup + k_count_hits",
+                                       "set_size": P, "us": ev0.elapsed_time(ev1) / args.steps * 1e3,
+                                       "hits": int(cnt.item())}
+        log("logits_apply over %d rows: %.4f ms = %.0f GB/s; outcome lookup (P=%d): %.1f us"
+            % (c.B * (2 * c.k + 1), ms_a, next_rows["logits_apply"]["achieved_GBps"], P,
+               next_rows["outcome_lookup"]["us"]))
+        del pout, allow, pen
+
     cpu = None
     if args.cpu_seconds > 0:
         log("cpu baseline: oracle on a bounded sample (~%.0f s of CPU work)" % args.cpu_seconds)
@@ -372,6 +425,8 @@ def main():
     }
     if pooled is not None:
         line["pooled_rows"] = pooled
+    if next_rows:
+        line["next_rows"] = next_rows
     print(json.dumps(line), flush=True)
 
 
