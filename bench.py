@@ -385,6 +385,52 @@ def main():
         next_rows["outcome_lookup"] = {"kernels": "k_outcome_lookup + k_count_hits",
                                        "set_size": P, "us": ev0.elapsed_time(ev1) / args.steps * 1e3,
                                        "hits": int(cnt.item())}
+        # fused LM head + greedy verify at the greedy workload's shape (B = 1,
+        # k = 8, V = 151936) with a synthetic head of d = 4096: the logits are
+        # never written; HBM-bound by the head (V d 2 bytes per call)
+        for Bl in (1, 48):
+            d = 4096
+            gh = torch.Generator(device=dev).manual_seed(77)
+            W = (torch.randn((c.V, d), device=dev, generator=gh) / d ** 0.5).to(torch.bfloat16)
+            Hd = torch.randn((Bl, 9, d), device=dev, generator=gh).to(torch.bfloat16)
+            lt = torch.zeros((Bl, 8), dtype=torch.int32, device=dev)
+            lws = torch.zeros(sv.workspace_size(sv.SPEC_OP_GREEDY_LMHEAD, Bl, 8, c.V),
+                              dtype=torch.uint8, device=dev)
+            la = torch.empty(Bl, dtype=torch.int32, device=dev)
+            lo = torch.empty((Bl, 9), dtype=torch.int32, device=dev)
+
+            def fused():
+                sv.verify_greedy_lmhead(Hd, W, lt, out=(la, lo), workspace=lws, stream=stream)
+
+            Wt = W.t().contiguous()
+            gws = torch.zeros(sv.workspace_size(sv.SPEC_OP_GREEDY, Bl, 8, c.V),
+                              dtype=torch.uint8, device=dev)
+
+            def unfused():
+                logits = torch.matmul(Hd.reshape(-1, d), Wt).view(Bl, 9, c.V)
+                sv.verify_greedy(logits, lt, workspace=gws, stream=stream)
+
+            res = {}
+            for name, f in (("fused", fused), ("unfused_bf16_matmul_then_verify", unfused)):
+                f()
+                torch.cuda.synchronize()
+                ev0.record(stream)
+                for _ in range(args.steps):
+                    f()
+                ev1.record(stream)
+                torch.cuda.synchronize()
+                res[name + "_ms"] = ev0.elapsed_time(ev1) / args.steps
+            wbytes = c.V * d * 2 + Bl * 9 * d * 2
+            res.update({"B": Bl, "k": 8, "d": d, "V": c.V, "rows": Bl * 9,
+                        "head_bytes": wbytes,
+                        "fused_GBps": wbytes / (res["fused_ms"] / 1e3) / 1e9,
+                        "fused_frac_hbm": wbytes / (res["fused_ms"] / 1e3) / 1e9 / PEAK_HBM_GBPS,
+                        "fused_TFLOPs": 2.0 * Bl * 9 * c.V * d / (res["fused_ms"] / 1e3) / 1e12})
+            next_rows["lmhead_greedy_B%d" % Bl] = res
+            log("fused LM head + greedy (B=%d, k=8, d=%d): %.4f ms (%.0f GB/s of head bytes), "
+                "unfused %.4f ms" % (Bl, d, res["fused_ms"], res["fused_GBps"],
+                                     res["unfused_bf16_matmul_then_verify_ms"]))
+            del W, Wt, Hd
         log("logits_apply over %d rows: %.4f ms = %.0f GB/s; outcome lookup (P=%d): %.1f us"
             % (c.B * (2 * c.k + 1), ms_a, next_rows["logits_apply"]["achieved_GBps"], P,
                next_rows["outcome_lookup"]["us"]))

@@ -23,7 +23,8 @@ import torch
 
 __all__ = ["lib", "verify_stochastic", "verify_greedy", "logits_process", "workspace_size",
            "verify_stochastic_pooled", "verify_greedy_pooled", "workspace_size_pooled",
-           "tree_branches", "outcome_lookup", "logits_apply", "status_string", "SpecError",
+           "tree_branches", "outcome_lookup", "logits_apply", "verify_greedy_lmhead",
+           "status_string", "SpecError",
            "library_path"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -31,7 +32,7 @@ _LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = range(5)
 SPEC_DTYPE_F32, SPEC_DTYPE_BF16 = 0, 1
-SPEC_OP_STOCHASTIC, SPEC_OP_GREEDY, SPEC_OP_PROCESS = 0, 1, 2
+SPEC_OP_STOCHASTIC, SPEC_OP_GREEDY, SPEC_OP_PROCESS, SPEC_OP_GREEDY_LMHEAD = 0, 1, 2, 3
 
 
 class spec_logits_t(ctypes.Structure):
@@ -98,6 +99,10 @@ def lib():
             L.spec_verify_greedy_pooled.argtypes = [spec_logits_t, i32, vp, vp, i32, i32, i32, vp,
                                                     vp, vp, sz, vp]
             L.spec_verify_greedy_pooled.restype = ctypes.c_int
+            i64 = ctypes.c_int64
+            L.spec_verify_greedy_lmhead.argtypes = [vp, i64, i64, vp, i64, i32, vp, i32, i32, i32,
+                                                    vp, vp, vp, sz, vp]
+            L.spec_verify_greedy_lmhead.restype = ctypes.c_int
             L.spec_logits_apply.argtypes = [spec_logits_t, i32, i32, i32, P(spec_processors_t),
                                             spec_logits_t, vp]
             L.spec_logits_apply.restype = ctypes.c_int
@@ -476,3 +481,36 @@ def logits_apply(logits: torch.Tensor, *, allow: torch.Tensor | None = None,
     rc = lib().spec_logits_apply(src, S, rows, V, ctypes.byref(proc), dst, _stream(stream))
     _check(rc, "spec_logits_apply")
     return out
+
+
+def verify_greedy_lmhead(hidden: torch.Tensor, weight: torch.Tensor, draft_tokens: torch.Tensor,
+                         *, out=None, workspace: torch.Tensor | None = None, stream=None):
+    """Fused LM head + greedy verify: hidden [B][k+1][d] and weight [V][d]
+    (bf16, last axis contiguous, rows 16-byte aligned); the logits hidden @
+    weight^T are reduced to per-row argmaxes on the matrix cores and never
+    stored.  Returns (accepted_len [B], out_tokens [B][k+1])."""
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise TypeError("hidden and weight must be bfloat16")
+    if hidden.dim() != 3 or weight.dim() != 2 or hidden.stride(2) != 1 or weight.stride(1) != 1:
+        raise ValueError("expected hidden [B][k+1][d] and weight [V][d] with contiguous last axes")
+    B, k = draft_tokens.shape
+    V, d = weight.shape
+    if tuple(hidden.shape) != (B, k + 1, d):
+        raise ValueError("hidden must be [B][k+1][d] with the weight's d")
+    dev = hidden.device
+    tokens = draft_tokens.to(device=dev, dtype=torch.int32).contiguous()
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+    else:
+        acc, toks = out
+    need = lib().spec_workspace_size(SPEC_OP_GREEDY_LMHEAD, B, k, V, None)
+    if need == 0:
+        _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size")
+    ws = workspace if workspace is not None else _workspace(dev, need)
+    rc = lib().spec_verify_greedy_lmhead(hidden.data_ptr(), hidden.stride(0), hidden.stride(1),
+                                         weight.data_ptr(), weight.stride(0), d, tokens.data_ptr(),
+                                         B, k, V, acc.data_ptr(), toks.data_ptr(), ws.data_ptr(),
+                                         ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "spec_verify_greedy_lmhead")
+    return acc, toks

@@ -368,6 +368,15 @@ void launch_apply(bool vec, unsigned nblk, const sv::ApplyArgs& A, hipStream_t s
   else hipLaunchKernelGGL((sv::k_logits_apply<TI, TO, false>), dim3(nblk), dim3(256), 0, st, A);
 }
 
+// Fused LM head: 256-wide vocabulary tiles (4 waves x 4 column blocks of 16;
+// narrower tiles measured slower), one greedy record per (row, tile).
+constexpr int64_t kLmTile = 256;
+size_t lmhead_workspace(int64_t B, int64_t k, int64_t V) {
+  const int64_t tiles = (V + kLmTile - 1) / kLmTile;
+  const size_t bytes = size_t(B) * size_t(k + 1) * size_t(tiles) * sizeof(sv::GPartial);
+  return bytes < 256 ? 256 : align256(bytes);
+}
+
 int finish_launch() {
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
@@ -378,6 +387,10 @@ extern "C" {
 
 size_t spec_workspace_size(int32_t op, int32_t B, int32_t k, int32_t V,
                            const spec_sampling_t* sampling) {
+  if (op == SPEC_OP_GREEDY_LMHEAD) {
+    if (check_sizes(B, k, V, true) != SPEC_OK) return 0;
+    return lmhead_workspace(B, k, V);
+  }
   if (op != SPEC_OP_STOCHASTIC && op != SPEC_OP_GREEDY && op != SPEC_OP_PROCESS) return 0;
   if (check_sizes(B, k, V, op != SPEC_OP_PROCESS) != SPEC_OK) return 0;
   spec_sampling_t plain = {1.0f, 0, 1.0f};
@@ -570,6 +583,51 @@ int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
   const int64_t words = L.rows * L.nchunks;  // 16 bytes each
   hipLaunchKernelGGL(sv::k_clear, dim3(unsigned((words + 255) / 256)), dim3(256), 0, st,
                      reinterpret_cast<uint4*>(part), words);
+  return finish_launch();
+}
+
+int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
+                              int64_t hidden_pos_stride, const void* weight,
+                              int64_t weight_stride, int32_t d, const int32_t* draft_tokens,
+                              int32_t B, int32_t k, int32_t V, int32_t* accepted_len,
+                              int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  int rc;
+  if ((rc = check_sizes(B, k, V, true)) != SPEC_OK) return rc;
+  if (!hidden || !weight || !draft_tokens || !accepted_len || !out_tokens)
+    return SPEC_ERR_INVALID_ARG;
+  if (d < 32 || d % 32 != 0) return SPEC_ERR_INVALID_ARG;
+  if (d > 65536) return SPEC_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(hidden) % 16 || reinterpret_cast<uintptr_t>(weight) % 16)
+    return SPEC_ERR_INVALID_ARG;
+  if (hidden_seq_stride < 0 || hidden_pos_stride < 0 || hidden_seq_stride % 8 ||
+      hidden_pos_stride % 8 || weight_stride < d || weight_stride % 8)
+    return SPEC_ERR_INVALID_ARG;
+  const size_t need = lmhead_workspace(B, k, V);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return SPEC_ERR_WORKSPACE;
+  const int64_t M = int64_t(B) * (k + 1);
+  const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int64_t tiles = (int64_t(V) + kLmTile - 1) / kLmTile;
+  const int64_t chunks = (M + 16 * mb - 1) / (16 * mb);
+  const int64_t nblk = tiles * chunks;
+  const int64_t grid = (nblk + 7) / 8 * 8;
+  if (!grid_fits(grid, 256) || !grid_fits(B, 64)) return SPEC_ERR_UNSUPPORTED;
+  auto* part = static_cast<sv::GPartial*>(workspace);
+  sv::LmHeadArgs A{static_cast<const uint16_t*>(hidden), hidden_seq_stride, hidden_pos_stride,
+                   k + 1, static_cast<const uint16_t*>(weight), weight_stride, M, int64_t(V), d,
+                   int32_t(tiles), int32_t(chunks), part};
+  auto st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  switch (mb) {
+    case 1: hipLaunchKernelGGL((sv::k_lmhead_argmax<1, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
+    case 2: hipLaunchKernelGGL((sv::k_lmhead_argmax<2, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
+    default: hipLaunchKernelGGL((sv::k_lmhead_argmax<4, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
+  }
+  // the greedy rule over the per-tile records (dense rows: b (k+1) + j)
+  sv::RowMap map{nullptr, 0, 0, nullptr, 0, 0, k + 1, k + 1};
+  hipLaunchKernelGGL(sv::k_greedy_tail, dim3(unsigned(B)), dim3(64), 0, st, map, int64_t(V), k,
+                     int(tiles), draft_tokens, part, accepted_len, out_tokens);
   return finish_launch();
 }
 

@@ -1892,4 +1892,155 @@ __global__ __launch_bounds__(256) void k_logits_apply(ApplyArgs A) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Fused LM head + greedy verify: logits[m][v] = sum_c hidden[m][c] W[v][c]
+// (bf16 inputs, fp32 MFMA accumulation) reduced on the fly to each row's
+// (largest logit, lowest index) per 256-wide vocabulary tile; the logits
+// never reach memory.  The tiles' records are GPartial, merged by
+// k_greedy_tail.
+//
+// v_mfma_f32_16x16x32_bf16 lane layout (checked on gfx950): lane l holds
+// A[l % 16][8 (l / 16) .. +8] and Bt[l % 16][8 (l / 16) .. +8] (B as its
+// transpose, here W rows), and C[4 (l / 16) + r][l % 16] for r = 0..3.
+typedef __bf16 sv_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float sv_f32x4 __attribute__((ext_vector_type(4)));
+
+struct LmHeadArgs {
+  const uint16_t* hidden;  // row (b, j) at hidden + b * h_seq + j * h_pos, d elements
+  int64_t h_seq, h_pos;
+  int32_t k1;              // rows per sequence
+  const uint16_t* weight;  // W[v] at weight + v * w_stride, d elements
+  int64_t w_stride;
+  int64_t M, V;
+  int32_t d;
+  int32_t n_tiles, m_chunks;
+  GPartial* part;          // [M][n_tiles]
+};
+
+__device__ __forceinline__ sv_bf16x8 ld_bf16x8(const uint16_t* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(sv_bf16x8, v);
+}
+
+template <int MB, int KU, int NB>
+__global__ __launch_bounds__(256) void k_lmhead_argmax(LmHeadArgs A) {
+  constexpr int TW = 4 * 16 * NB;  // vocabulary tile: 4 waves x NB column blocks of 16
+  constexpr int MR = 16 * MB;  // rows per chunk
+  __shared__ uint64_t best_s[4][MR];
+  __shared__ uint32_t bad_s[4][MR];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // XCD-aware order: the workgroups of one XCD take a contiguous range of
+  // (tile, chunk) pairs, chunks fastest, so one tile's W is reused from L2
+  const int64_t nblk = (int64_t)A.n_tiles * A.m_chunks;
+  const int64_t per_xcd = (nblk + 7) / 8;
+  const int64_t pidx = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (pidx >= nblk) return;
+  const int64_t tile = pidx / A.m_chunks, chunk = pidx - tile * A.m_chunks;
+  const int64_t n0 = tile * TW + (int64_t)w * 16 * NB;  // this wave's columns
+  const int64_t m0 = chunk * MR;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+
+  // row pointers of this lane's A fragments (rows past M read row 0: their
+  // results are discarded) and W fragments (columns past V read row 0)
+  const uint16_t* ap[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    int64_t m = m0 + 16 * mb + r16;
+    if (m >= A.M) m = 0;
+    const int64_t b = m / A.k1, j = m - b * A.k1;
+    ap[mb] = A.hidden + b * A.h_seq + j * A.h_pos + kq;
+  }
+  const uint16_t* bp[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    int64_t v = n0 + 16 * cb + r16;
+    if (v >= A.V) v = 0;
+    bp[cb] = A.weight + v * A.w_stride + kq;
+  }
+  sv_f32x4 acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) acc[mb][cb] = sv_f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // KU steps of 32 per batch: every fragment of a batch is loaded before the
+  // first MFMA uses one (steps past d, when d is not a multiple of 32 KU,
+  // are zero and add nothing)
+  const sv_bf16x8 zero8 = __builtin_bit_cast(sv_bf16x8, make_uint4(0u, 0u, 0u, 0u));
+  for (int c = 0; c < A.d; c += 32 * KU) {
+    sv_bf16x8 af[KU][MB], bfr[KU][NB];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const bool in = c + 32 * u < A.d;
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) bfr[u][cb] = in ? ld_bf16x8(bp[cb] + c + 32 * u) : zero8;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) af[u][mb] = in ? ld_bf16x8(ap[mb] + c + 32 * u) : zero8;
+    }
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+          acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[u][mb], bfr[u][cb], acc[mb][cb],
+                                                                0, 0, 0);
+  }
+
+  // epilogue: per row, the best (order key, lowest index) of this lane's
+  // columns, then over the 16 lanes that hold the same rows, then the waves
+  const int rq = (lane >> 4) * 4;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint64_t best = 0;
+      uint32_t bad = 0;
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int64_t v = n0 + 16 * cb + r16;
+        const float x = acc[mb][cb][r];
+        if (v < A.V) {
+          if (bad_logit(x)) {
+            bad = 1u;
+          } else if (x > -__builtin_inff()) {
+            const uint64_t cand = pack_best(key_of(x), (int32_t)v);
+            best = cand > best ? cand : best;
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {  // the 16 lanes holding these rows
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)best, off, 16);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), off, 16);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        best = o > best ? o : best;
+        bad |= (uint32_t)__shfl_xor((int)bad, off, 16);
+      }
+      if (r16 == 0) {
+        best_s[w][16 * mb + rq + r] = best;
+        bad_s[w][16 * mb + rq + r] = bad;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < MR; i += 256) {
+    const int64_t m = m0 + i;
+    if (m >= A.M) continue;
+    uint64_t best = 0;
+    uint32_t bad = 0;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      best = best_s[ww][i] > best ? best_s[ww][i] : best;
+      bad |= bad_s[ww][i];
+    }
+    GPartial g;
+    g.key = (uint32_t)(best >> 32);
+    g.idx = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
+    g.flags = bad ? kFlagBad : 0u;
+    g.pad = 0u;
+    A.part[m * A.n_tiles + tile] = g;
+  }
+}
+
 }  // namespace sv

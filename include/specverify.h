@@ -105,7 +105,8 @@ typedef struct {
 typedef enum {
   SPEC_OP_STOCHASTIC = 0,
   SPEC_OP_GREEDY = 1,
-  SPEC_OP_PROCESS = 2
+  SPEC_OP_PROCESS = 2,
+  SPEC_OP_GREEDY_LMHEAD = 3
 } spec_op_t;
 
 /* Bytes of device workspace the given call needs (0 for invalid arguments).
@@ -198,6 +199,28 @@ int spec_verify_stochastic_pooled(spec_logits_t target_pool, int32_t n_target_ro
  * spec_workspace_size_pooled(SPEC_OP_GREEDY, n_target_rows, 0, B, k, V, NULL). */
 int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
                               const int32_t* target_map, const int32_t* draft_tokens,
+                              int32_t B, int32_t k, int32_t V, int32_t* accepted_len,
+                              int32_t* out_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Fused LM head + greedy verify.  The target scores every drafted position
+ * in one pass (the entry's section "Concept and scope"): its logits are the
+ * hidden states times the LM head, logits[b][j][v] = sum_c hidden[b][j][c] *
+ * weight[v][c].  This call computes them tile by tile on the matrix cores
+ * (bf16 inputs, fp32 accumulation) and reduces each row to its argmax
+ * (lowest index on ties) without writing the logits to memory, then runs the
+ * greedy rule of spec_verify_greedy.
+ *   hidden        [B][k+1][d] bf16, row (b, j) at hidden + b * hidden_seq_stride
+ *                 + j * hidden_pos_stride (elements; multiples of 8; 16-byte aligned)
+ *   weight        [V][d] bf16, row v at weight + v * weight_stride (>= d, a
+ *                 multiple of 8; 16-byte aligned) -- the LM head as stored
+ *   d             hidden size, a multiple of 32, 32 <= d <= 65536
+ * Workspace: spec_workspace_size(SPEC_OP_GREEDY_LMHEAD, B, k, V, NULL).
+ * Reading: the argmax is taken on fp32 logits; where two logits lie within
+ * the fp32 rounding of their sums, either may be reported. */
+int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
+                              int64_t hidden_pos_stride, const void* weight,
+                              int64_t weight_stride, int32_t d, const int32_t* draft_tokens,
                               int32_t B, int32_t k, int32_t V, int32_t* accepted_len,
                               int32_t* out_tokens, void* workspace, size_t workspace_bytes,
                               void* stream);

@@ -363,3 +363,63 @@ def apply_processors(logits, allow=None, penalize=None, theta=1.0, out_dtype=Non
     if out_dtype == "bf16":
         return _bf16_round(out)
     return out
+
+
+def lmhead_logits(hidden_bits, weight_bits, rows=None, chunk=16384):
+    """fp64 logits hidden @ weight^T of bf16 inputs (exact products, fp64
+    sums) for the rows (flat indices into [B][k+1]) asked for, with, per
+    logit, the sum of |products| (for rounding bounds).  numpy matmul."""
+    H = _bf16_decode(hidden_bits).astype(np.float64)
+    H = H.reshape(-1, H.shape[-1])
+    if rows is not None:
+        H = H[np.asarray(rows)]
+    V = weight_bits.shape[0]
+    L = np.empty((H.shape[0], V))
+    S = np.empty((H.shape[0], V))
+    for lo in range(0, V, chunk):
+        W = _bf16_decode(weight_bits[lo:lo + chunk]).astype(np.float64)
+        L[:, lo:lo + chunk] = H @ W.T
+        S[:, lo:lo + chunk] = np.abs(H) @ np.abs(W).T
+    return L, S
+
+
+def lmhead_greedy(hidden_bits, weight_bits, tokens):
+    """Greedy verify on LM-head logits (the encyclopedia entry's greedy rule:
+    compare each draft with the target's most probable token, replace the
+    first mismatch; lowest index on ties).  Returns (accepted_len [B],
+    out_tokens [B][k+1], near_tie [B][k+1]): near_tie marks rows where another
+    token's logit lies within the fp32 summation bound gamma_d (|a| + |b|)
+    of the largest (gamma_d = d u / (1 - d u), u = 2^-24), so that a kernel
+    accumulating in fp32 may report either."""
+    B, k1, d = hidden_bits.shape
+    k = k1 - 1
+    L, S = lmhead_logits(hidden_bits, weight_bits)
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    best = np.argmax(L, axis=1)  # first maximum
+    top = L[np.arange(len(L)), best]
+    stop = S[np.arange(len(L)), best]
+    near = (L >= top[:, None] - gamma * (stop[:, None] + S)).sum(axis=1) > 1
+    best = best.reshape(B, k1)
+    near = near.reshape(B, k1)
+    V = weight_bits.shape[0]
+    toks = np.asarray(tokens, np.int64).reshape(B, k)
+    acc = np.zeros(B, np.int32)
+    out = np.full((B, k1), -1, np.int32)
+    for b in range(B):
+        n, valid = k, True
+        for j in range(k):
+            x = int(toks[b, j])
+            if not 0 <= x < V:
+                valid = False
+                break
+            if x != best[b, j]:
+                n = j
+                break
+        if not valid:
+            acc[b] = -1
+            continue
+        acc[b] = n
+        out[b, :n] = toks[b, :n]
+        out[b, n] = best[b, n]
+    return acc, out, near

@@ -544,6 +544,52 @@ def pin_logits_processors(orc, apply=None):
     assert np.allclose(p[keep], p0[keep] / p0[keep].sum(), rtol=1e-12)
 
 
-ALL_PINS = [pin_logits_processors, pin_outcome_lookup, pin_pooled_rows, pin_worked_example, pin_law_of_decision_map, pin_softmax_and_filters,
+# ---------------------------------------------------------------------------
+def _bf16_bits_exact(x):
+    """bf16 bits of values exactly representable in bf16."""
+    b = np.asarray(x, np.float32).view(np.uint32)
+    assert ((b & 0xFFFF) == 0).all()
+    return (b >> 16).astype(np.uint16)
+
+
+def pin_lmhead_greedy(orc, greedy=None):
+    """Greedy verify on LM-head logits: logits are the exact dot products of
+    the bf16 inputs; the greedy rule takes the lowest index among equal
+    maxima; a row with another logit within the fp32 summation bound of the
+    largest is marked as a near tie, a clearly separated one is not."""
+    import oracle as _oracle
+    greedy = greedy or _oracle.lmhead_greedy
+    d = 32
+    w = np.zeros((4, d), np.float32)
+    w[0, 0], w[1, 0], w[2, 0], w[3, 1] = 2.0, 3.0, 3.0, 1.0
+    h = np.zeros((1, 3, d), np.float32)
+    h[0, 0, 0] = 1.0            # logits 2, 3, 3, 0: tie between tokens 1 and 2
+    h[0, 1, 1] = 5.0            # logits 0, 0, 0, 5
+    h[0, 2, 0] = -1.0           # logits -2, -3, -3, 0
+    hb, wb = _bf16_bits_exact(h), _bf16_bits_exact(w)
+    L, S = _oracle.lmhead_logits(hb, wb)
+    assert np.array_equal(L, [[2, 3, 3, 0], [0, 0, 0, 5], [-2, -3, -3, 0]])
+    acc, out, near = greedy(hb, wb, np.array([[1, 3]], np.int32))
+    assert list(acc) == [2] and list(out[0]) == [1, 3, 3], (acc, out)
+    assert list(near[0]) == [True, False, False], near
+    acc, out, near = greedy(hb, wb, np.array([[2, 3]], np.int32))  # 2 ties but 1 is first
+    assert list(acc) == [0] and list(out[0]) == [1, -1, -1], (acc, out)
+    acc, out, near = greedy(hb, wb, np.array([[1, 4]], np.int32))  # token outside V
+    assert list(acc) == [-1]
+    # near tie: the two logits differ by 2^-14 while large terms that cancel
+    # in both make the sum of |products| ~3 x 10^4 (fp32 bound ~0.1); the
+    # second row's gap of 2^-7 with |products| ~1 is clear
+    w2 = np.ones((2, d), np.float32)
+    w2[1, :2] = 1.0 + 2.0 ** -7
+    h2 = np.zeros((1, 2, d), np.float32)
+    h2[0, 0, 0], h2[0, 0, 1] = 1.0, -(1.0 - 2.0 ** -7)
+    h2[0, 0, 2:] = np.tile([1024.0, -1024.0], (d - 2) // 2)
+    h2[0, 1, 0] = 1.0
+    acc, out, near = greedy(_bf16_bits_exact(h2), _bf16_bits_exact(w2), np.array([[1]], np.int32))
+    assert list(near[0]) == [True, False], near
+    assert list(out[0]) == [1, 1]
+
+
+ALL_PINS = [pin_lmhead_greedy, pin_logits_processors, pin_outcome_lookup, pin_pooled_rows, pin_worked_example, pin_law_of_decision_map, pin_softmax_and_filters,
             pin_acceptance_rate, pin_special_cases, pin_greedy, pin_bf16_decode,
             pin_invalid_inputs, pin_boundary_flags, pin_chi_square]

@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "spec_logits_apply", "spec_logits_process", "spec_outcome_lookup", "spec_status_string",
-        "spec_verify_greedy",
+        "spec_verify_greedy", "spec_verify_greedy_lmhead",
         "spec_verify_greedy_pooled", "spec_verify_stochastic", "spec_verify_stochastic_pooled",
         "spec_workspace_size", "spec_workspace_size_pooled"])
 
@@ -225,3 +225,23 @@ def test_logits_apply_validation():
     assert call(stride=-1) == sv.SPEC_ERR_INVALID_ARG
     assert call(dst=sv.spec_logits_t(4096, 9, 0, 5 * 1024, 1024)) == sv.SPEC_ERR_UNSUPPORTED
     assert call(src=sv.spec_logits_t(4096, 0, 0, 5 * 1024, 1000)) == sv.SPEC_ERR_INVALID_ARG
+
+
+
+def test_lmhead_validation():
+    L = sv.lib()
+    p = ctypes.c_void_p(4096)
+    ws, wsb = ctypes.c_void_p(1 << 20), 1 << 30
+
+    def call(d=64, hs=5 * 64, hp=64, wstr=64, B=1, k=4, V=1000, h=p, w=p, work=ws):
+        return L.spec_verify_greedy_lmhead(h, hs, hp, w, wstr, d, p, B, k, V, p, p, work, wsb, None)
+
+    assert sv.workspace_size(sv.SPEC_OP_GREEDY_LMHEAD, 1, 8, 151936) > 0
+    assert call(d=0) == sv.SPEC_ERR_INVALID_ARG
+    assert call(d=48) == sv.SPEC_ERR_INVALID_ARG          # not a multiple of 32
+    assert call(d=65536 + 32, wstr=65568, hp=65568, hs=5 * 65568) == sv.SPEC_ERR_UNSUPPORTED
+    assert call(h=ctypes.c_void_p(4104)) == sv.SPEC_ERR_INVALID_ARG   # misaligned
+    assert call(hp=60) == sv.SPEC_ERR_INVALID_ARG          # stride not a multiple of 8
+    assert call(wstr=32) == sv.SPEC_ERR_INVALID_ARG        # weight stride < d
+    assert call(work=None) == sv.SPEC_ERR_WORKSPACE
+    assert call(B=0) == sv.SPEC_ERR_INVALID_ARG

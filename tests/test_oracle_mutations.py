@@ -162,3 +162,35 @@ def _apply_truncating_bf16(logits, allow=None, penalize=None, theta=1.0, out_dty
 def test_pins_catch_processor_mutation(mutant):
     with pytest.raises(AssertionError):
         pins.pin_logits_processors(oracle.default(), apply=mutant)
+
+
+# Mistakes planted in the LM-head greedy oracle.
+def _lm_last_max(hidden, weight, tokens):
+    import oracle as o
+    L, S = o.lmhead_logits(hidden, weight)
+    V = L.shape[1]
+    best = V - 1 - np.argmax(L[:, ::-1], axis=1)  # last maximum
+    B, k1, _ = hidden.shape
+    acc, out, near = o.lmhead_greedy(hidden, weight, tokens)
+    best = best.reshape(B, k1)
+    toks = np.asarray(tokens).reshape(B, k1 - 1)
+    for b in range(B):
+        if acc[b] < 0:
+            continue
+        n = next((j for j in range(k1 - 1) if toks[b, j] != best[b, j]), k1 - 1)
+        acc[b] = n
+        out[b] = -1
+        out[b, :n] = toks[b, :n]
+        out[b, n] = best[b, n]
+    return acc, out, near
+
+
+def _lm_no_bound(hidden, weight, tokens):
+    acc, out, near = oracle.lmhead_greedy(hidden, weight, tokens)
+    return acc, out, np.zeros_like(near)
+
+
+@pytest.mark.parametrize("mutant", [_lm_last_max, _lm_no_bound], ids=lambda f: f.__name__)
+def test_pins_catch_lmhead_mutation(mutant):
+    with pytest.raises(AssertionError):
+        pins.pin_lmhead_greedy(oracle.default(), greedy=mutant)

@@ -178,3 +178,19 @@ def worked_example():
     draft = q[None, None, :].copy()          # [1][1][3]
     tokens = np.array([[1]], np.int32)       # B
     return target, draft, tokens
+
+
+def lmhead(B: int, k: int, d: int, V: int, seed: int = 7, boost: float = 0.3,
+           stream_base: int = 20):
+    """Synthetic LM-head inputs (bf16 bits): weight W [V][d] ~ N(0, 1/d) and
+    hidden [B][k+1][d] ~ N(0, 1) plus, per row, boost * sqrt(d) * W[v*] for a
+    uniformly drawn token v* (peaked rows, as the greedy workload's +8 boost).
+    Returns (hidden_bits, weight_bits, boosted token ids [B][k+1])."""
+    rw = np.random.default_rng([9000 + seed, stream_base])
+    w = (rw.standard_normal((V, d), np.float32) / np.float32(np.sqrt(d))).astype(np.float32)
+    rh = np.random.default_rng([9000 + seed, stream_base + 1])
+    h = rh.standard_normal((B, k + 1, d), np.float32)
+    vs = rh.integers(0, V, size=(B, k + 1))
+    if boost:
+        h += np.float32(boost * np.sqrt(d)) * w[vs]
+    return to_bf16_bits(h), to_bf16_bits(w), vs.astype(np.int32)
