@@ -369,12 +369,14 @@ void launch_apply(bool vec, unsigned nblk, const sv::ApplyArgs& A, hipStream_t s
 }
 
 // Fused LM head: 256-wide vocabulary tiles (4 waves x 4 column blocks of 16;
-// narrower tiles measured slower), one greedy record per (row, tile).
+// narrower tiles measured slower); per row one merged 8-byte record and a
+// 4-byte flag word.
 constexpr int64_t kLmTile = 256;
+size_t lmhead_bad_off(int64_t M) { return align256(size_t(M) * 8); }
 size_t lmhead_workspace(int64_t B, int64_t k, int64_t V) {
-  const int64_t tiles = (V + kLmTile - 1) / kLmTile;
-  const size_t bytes = size_t(B) * size_t(k + 1) * size_t(tiles) * sizeof(sv::GPartial);
-  return bytes < 256 ? 256 : align256(bytes);
+  (void)V;
+  const int64_t M = B * (k + 1);
+  return lmhead_bad_off(M) + align256(size_t(M) * 4);
 }
 
 int finish_launch() {
@@ -462,7 +464,7 @@ int spec_verify_greedy(spec_logits_t target, const int32_t* draft_tokens, int32_
   (void)hipGetLastError();
   dispatch<GreedyRun>(target.dtype, vec_ok(target), L, map, int64_t(V), part, st);
   hipLaunchKernelGGL(sv::k_greedy_tail, dim3(unsigned(B)), dim3(64), 0, st, map, int64_t(V), k,
-                     L.nchunks, draft_tokens, part, accepted_len, out_tokens);
+                     L.nchunks, draft_tokens, part, nullptr, nullptr, accepted_len, out_tokens);
   return finish_launch();
 }
 
@@ -578,7 +580,7 @@ int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
   (void)hipGetLastError();
   dispatch<GreedyRun>(target_pool.dtype, vec_ok(target_pool), L, map, int64_t(V), part, st);
   hipLaunchKernelGGL(sv::k_greedy_tail, dim3(unsigned(B)), dim3(64), 0, st, map, int64_t(V), k,
-                     L.nchunks, draft_tokens, part, accepted_len, out_tokens);
+                     L.nchunks, draft_tokens, part, nullptr, nullptr, accepted_len, out_tokens);
   // the pooled partials are shared by sequences: cleared after the tail
   const int64_t words = L.rows * L.nchunks;  // 16 bytes each
   hipLaunchKernelGGL(sv::k_clear, dim3(unsigned((words + 255) / 256)), dim3(256), 0, st,
@@ -613,10 +615,11 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   const int64_t nblk = tiles * chunks;
   const int64_t grid = (nblk + 7) / 8 * 8;
   if (!grid_fits(grid, 256) || !grid_fits(B, 64)) return SPEC_ERR_UNSUPPORTED;
-  auto* part = static_cast<sv::GPartial*>(workspace);
+  auto* best = static_cast<uint64_t*>(workspace);
+  auto* bad = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + lmhead_bad_off(M));
   sv::LmHeadArgs A{static_cast<const uint16_t*>(hidden), hidden_seq_stride, hidden_pos_stride,
                    k + 1, static_cast<const uint16_t*>(weight), weight_stride, M, int64_t(V), d,
-                   int32_t(tiles), int32_t(chunks), part};
+                   int32_t(tiles), int32_t(chunks), best, bad};
   auto st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   switch (mb) {
@@ -626,8 +629,8 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   }
   // the greedy rule over the per-tile records (dense rows: b (k+1) + j)
   sv::RowMap map{nullptr, 0, 0, nullptr, 0, 0, k + 1, k + 1};
-  hipLaunchKernelGGL(sv::k_greedy_tail, dim3(unsigned(B)), dim3(64), 0, st, map, int64_t(V), k,
-                     int(tiles), draft_tokens, part, accepted_len, out_tokens);
+  hipLaunchKernelGGL(sv::k_greedy_tail, dim3(unsigned(B)), dim3(64), 0, st, map, int64_t(V), k, 1,
+                     draft_tokens, nullptr, best, bad, accepted_len, out_tokens);
   return finish_launch();
 }
 

@@ -263,6 +263,8 @@ __global__ __launch_bounds__(256) void k_greedy_partials(RowMap map, int64_t V, 
 __global__ __launch_bounds__(64) void k_greedy_tail(RowMap map, int64_t V, int k, int nchunks,
                                                     const int32_t* __restrict__ tokens,
                                                     GPartial* __restrict__ part,
+                                                    uint64_t* __restrict__ pbest,
+                                                    uint32_t* __restrict__ pbad,
                                                     int32_t* __restrict__ accepted_len,
                                                     int32_t* __restrict__ out_tokens) {
   const int64_t b = blockIdx.x;
@@ -270,28 +272,68 @@ __global__ __launch_bounds__(64) void k_greedy_tail(RowMap map, int64_t V, int k
   const int k1 = k + 1;
   const bool pooled = map.nt > 0;
   __shared__ int32_t best_idx[SPEC_MAX_K + 1];  // -1 for an invalid row
-  for (int j = lane; j < k1; j += kWave) {
-    const int64_t r = map.sidx(b, j);
-    if (r < 0) {
-      best_idx[j] = -1;
-      continue;
+  if (pbest) {
+    // one merged record per row (pack_best order; bad flags or-ed), cleared here
+    for (int j = lane; j < k1; j += kWave) {
+      const int64_t r = map.sidx(b, j);
+      const uint64_t bb = pbest[r];
+      const uint32_t fl = pbad[r];
+      pbest[r] = 0ull;
+      pbad[r] = 0u;
+      const uint32_t key = (uint32_t)(bb >> 32);
+      best_idx[j] = (fl == 0 && key != 0) ? (int32_t)(0xFFFFFFFFu - (uint32_t)bb) : -1;
     }
-    GPartial* p = part + r * (int64_t)nchunks;
-    uint64_t bb = 0;
-    uint32_t fl = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const uint64_t cand = pack_best(p[c].key, p[c].idx);
-      if (p[c].key != 0 && cand > bb) bb = cand;
-      fl |= p[c].flags;
-    }
-    if (!pooled) {
-      for (int c = 0; c < nchunks; ++c) {
-        GPartial zero = {0u, 0, 0u, 0u};
-        p[c] = zero;
+  } else if (nchunks > 16) {
+    // many chunks per row (e.g. the fused LM head's vocabulary tiles): the
+    // whole wave merges one row's records at a time
+    for (int j = 0; j < k1; ++j) {
+      const int64_t r = map.sidx(b, j);
+      if (r < 0) {
+        if (lane == 0) best_idx[j] = -1;
+        continue;
       }
+      GPartial* p = part + r * (int64_t)nchunks;
+      uint64_t bb = 0;
+      uint32_t fl = 0;
+      for (int c = lane; c < nchunks; c += kWave) {
+        const GPartial g = p[c];
+        const uint64_t cand = pack_best(g.key, g.idx);
+        if (g.key != 0 && cand > bb) bb = cand;
+        fl |= g.flags;
+        if (!pooled) {
+          GPartial zero = {0u, 0, 0u, 0u};
+          p[c] = zero;
+        }
+      }
+      bb = wave_max_u64(bb);
+      fl = wave_or(fl);
+      const uint32_t key = (uint32_t)(bb >> 32);
+      if (lane == 0) best_idx[j] = (fl == 0 && key != 0) ? (int32_t)(0xFFFFFFFFu - (uint32_t)bb) : -1;
     }
-    const uint32_t key = (uint32_t)(bb >> 32);
-    best_idx[j] = (fl == 0 && key != 0) ? (int32_t)(0xFFFFFFFFu - (uint32_t)bb) : -1;
+  } else {
+    for (int j = lane; j < k1; j += kWave) {
+      const int64_t r = map.sidx(b, j);
+      if (r < 0) {
+        best_idx[j] = -1;
+        continue;
+      }
+      GPartial* p = part + r * (int64_t)nchunks;
+      uint64_t bb = 0;
+      uint32_t fl = 0;
+      for (int c = 0; c < nchunks; ++c) {
+        const uint64_t cand = pack_best(p[c].key, p[c].idx);
+        if (p[c].key != 0 && cand > bb) bb = cand;
+        fl |= p[c].flags;
+      }
+      if (!pooled) {
+        for (int c = 0; c < nchunks; ++c) {
+          GPartial zero = {0u, 0, 0u, 0u};
+          p[c] = zero;
+        }
+      }
+      const uint32_t key = (uint32_t)(bb >> 32);
+      best_idx[j] = (fl == 0 && key != 0) ? (int32_t)(0xFFFFFFFFu - (uint32_t)bb) : -1;
+    }
   }
   __syncthreads();
   // Positions in order up to the first mismatch; only what the walk consults
@@ -1896,8 +1938,8 @@ __global__ __launch_bounds__(256) void k_logits_apply(ApplyArgs A) {
 // Fused LM head + greedy verify: logits[m][v] = sum_c hidden[m][c] W[v][c]
 // (bf16 inputs, fp32 MFMA accumulation) reduced on the fly to each row's
 // (largest logit, lowest index) per 256-wide vocabulary tile; the logits
-// never reach memory.  The tiles' records are GPartial, merged by
-// k_greedy_tail.
+// never reach memory.  Each row's tiles are merged with one 64-bit atomic max
+// per (row, tile) into a per-row record that k_greedy_tail reads.
 //
 // v_mfma_f32_16x16x32_bf16 lane layout (checked on gfx950): lane l holds
 // A[l % 16][8 (l / 16) .. +8] and Bt[l % 16][8 (l / 16) .. +8] (B as its
@@ -1914,7 +1956,8 @@ struct LmHeadArgs {
   int64_t M, V;
   int32_t d;
   int32_t n_tiles, m_chunks;
-  GPartial* part;          // [M][n_tiles]
+  uint64_t* best;          // [M]: merged (order key, lowest index) of each row, pack_best order
+  uint32_t* bad;           // [M]: NaN / +inf seen
 };
 
 __device__ __forceinline__ sv_bf16x8 ld_bf16x8(const uint16_t* p) {
@@ -2034,12 +2077,10 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(LmHeadArgs A) {
       best = best_s[ww][i] > best ? best_s[ww][i] : best;
       bad |= bad_s[ww][i];
     }
-    GPartial g;
-    g.key = (uint32_t)(best >> 32);
-    g.idx = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
-    g.flags = bad ? kFlagBad : 0u;
-    g.pad = 0u;
-    A.part[m * A.n_tiles + tile] = g;
+    // merged across tiles on the fly: the largest packed word is the largest
+    // logit with the lowest index
+    if (best) __hip_atomic_fetch_max(A.best + m, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (bad) atomicOr(A.bad + m, 1u);
   }
 }
 
