@@ -120,3 +120,16 @@ def test_lmhead_every_row_argmax(d, V):
     best = np.argmax(L, axis=1).reshape(B, k + 1)
     acc, out, racc, near = _check(h, w, _tokens(rs, best, V, 0.0), "lmhead every row d=%d V=%d" % (d, V))
     assert (racc[~near.any(axis=1)] == k).all()
+
+
+@pytest.mark.parametrize("d", [32, 96, 160])
+def test_lmhead_k_tail(d):
+    """d a multiple of 32 but not of the 64 the kernel loads per batch: the
+    batch's second step lies past d and must add nothing."""
+    rs = np.random.default_rng(d)
+    B, k, V = 5, 3, 3001
+    h, w, vs = workloads.lmhead(B, k, d, V, seed=d, boost=2.0)
+    L, _ = oracle.lmhead_logits(h, w)
+    best = np.argmax(L, axis=1).reshape(B, k + 1)
+    acc, out, racc, near = _check(h, w, _tokens(rs, best, V, 0.0), "lmhead d=%d" % d)
+    assert (acc[~near.any(axis=1)] == k).all()

@@ -283,3 +283,23 @@ def test_config5_pooled_full_size_sampled():
     ref = oracle.verify_stochastic(sub.target, sub.draft, toks[check], sub.uniforms,
                                    c.temperature, c.top_k, c.top_p)
     compare_stochastic(ref, acc, out, ap, rows=check, fp32=False, label="c5 pooled, 12 checked")
+
+
+def test_pooled_walk_max_k():
+    """k = 64 (the maximum) on the pooled walk: 64 draft steps per sequence,
+    target statistics for 65 rows per sequence from the pool pass."""
+    rs = np.random.default_rng(79)
+    k, V = 64, 64
+    nreq = (_walk_batch() + 3) // 4 + 1
+    tp, tm, dp, toks, u = _fanout(rs, nreq, 4, k, V, "bf16", 1.0, 0, 0.9, drop=1)
+    ref, *_ = _check(tp, tm, dp, None, toks, u, 1.0, 0, 0.9, "pooled walk k=64")
+    note("  deepest accepted length %d" % ref["accepted_len"].max())
+
+
+def test_pooled_unaligned_rows():
+    """Pools whose rows are not 16-byte aligned (V = 777 at stride 777, bf16
+    and fp32): the scalar-load row pass."""
+    rs = np.random.default_rng(80)
+    for dtype in ("bf16", "f32"):
+        tp, tm, dp, toks, u = _fanout(rs, 3, 8, 3, 777, dtype, 1.0, 0, 0.95)
+        _check(tp, tm, dp, None, toks, u, 1.0, 0, 0.95, "pooled unaligned %s" % dtype)
