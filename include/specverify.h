@@ -203,8 +203,10 @@ int spec_verify_greedy_pooled(spec_logits_t target_pool, int32_t n_target_rows,
                               int32_t* out_tokens, void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Fused LM head + greedy verify.  The target scores every drafted position
- * in one pass (the entry's section "Concept and scope"): its logits are the
+/* Fused LM head + greedy verify.  The target processes the prefix extended
+ * by the candidates once and gets its distribution at every drafted position
+ * (the entry's section "Basic steps of proposal and verification"): its
+ * logits are the
  * hidden states times the LM head, logits[b][j][v] = sum_c hidden[b][j][c] *
  * weight[v][c].  This call computes them tile by tile on the matrix cores
  * (bf16 inputs, fp32 accumulation) and reduces each row to its argmax
