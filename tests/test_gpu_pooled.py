@@ -303,3 +303,15 @@ def test_pooled_unaligned_rows():
     for dtype in ("bf16", "f32"):
         tp, tm, dp, toks, u = _fanout(rs, 3, 8, 3, 777, dtype, 1.0, 0, 0.95)
         _check(tp, tm, dp, None, toks, u, 1.0, 0, 0.95, "pooled unaligned %s" % dtype)
+
+
+def test_pooled_walk_single_request():
+    """One request, every branch sharing its five target rows (a pool of 5
+    rows: the pre-pass has fewer rows than XCD ranges), enough branches for
+    the walk."""
+    rs = np.random.default_rng(81)
+    k, V = 4, 2000
+    nb = _walk_batch() + 20
+    tp, tm, dp, toks, u = _fanout(rs, 1, nb, k, V, "bf16", 1.0, 0, 0.95, drop=0)
+    assert len(tp) == k + 1
+    _check(tp, tm, dp, None, toks, u, 1.0, 0, 0.95, "pooled walk, one request x %d branches" % nb)
