@@ -309,8 +309,12 @@ struct ProcessRun {
       part = reinterpret_cast<sv::Partial*>(ws + L.part_off);
       launch_partials<T, VEC>(L, map, V, a, part, st);
     }
-    hipLaunchKernelGGL(sv::k_process_stats, dim3(unsigned((L.rows + 255) / 256)), dim3(256), 0, st,
-                       L.rows, L.nchunks, a, part, rs, row_stats);
+    if (part && L.nchunks > 16)  // many chunks per row: one wave per row merges them
+      hipLaunchKernelGGL(sv::k_process_stats_wide, dim3(unsigned((L.rows + 3) / 4)), dim3(256), 0,
+                         st, L.rows, L.nchunks, a, part, rs, row_stats);
+    else
+      hipLaunchKernelGGL(sv::k_process_stats, dim3(unsigned((L.rows + 255) / 256)), dim3(256), 0,
+                         st, L.rows, L.nchunks, a, part, rs, row_stats);
     if (probs) launch_probs<T, VEC>(L, map, V, a, rs, probs, st);
   }
 };

@@ -184,6 +184,33 @@ __device__ __forceinline__ RowStat merge_partials(const Partial* p, int nchunks,
   return st;
 }
 
+// The same merge by all 64 lanes of a wave (rows split into many chunks, e.g.
+// a single sequence's rows spread over the chip); every lane gets the result.
+__device__ __forceinline__ RowStat merge_partials_wave(const Partial* p, int nchunks, float a,
+                                                       int lane) {
+  float m = -__builtin_inff();
+  uint32_t flags = 0;
+  for (int c = lane; c < nchunks; c += kWave) {
+    m = fmaxf(m, p[c].m);
+    flags |= p[c].flags;
+  }
+  m = wave_max(m);
+  flags = wave_or(flags);
+  double z = 0.0;
+  if (m > -__builtin_inff()) {
+    for (int c = lane; c < nchunks; c += kWave)
+      if (p[c].m > -__builtin_inff()) z += p[c].s * exp2_d(((double)p[c].m - (double)m) * (double)a);
+  }
+  z = wave_sum(z);
+  RowStat st;
+  st.m = m;
+  st.thr = -__builtin_inff();
+  st.z = z;
+  st.valid = (!(flags & kFlagBad) && m > -__builtin_inff()) ? 1 : 0;
+  st.pad[0] = st.pad[1] = st.pad[2] = 0;
+  return st;
+}
+
 // ---------------------------------------------------------------------------
 // Greedy: per (row, chunk) largest finite logit (as an order key) and its
 // lowest index.
@@ -1054,28 +1081,49 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   // alone and their workspace records are cleared here; pooled records are
   // shared and cleared by a pass of their own after every sequence is done.
   const bool pooled = A.map.nt > 0;
-  for (int t = tid; t < nr; t += NT) {
-    const int64_t rr = A.map.sidx(b, t);
-    RowStat s = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
-    if (rr >= 0) {
-      if (A.rowstat) {
-        s = A.rowstat[rr];
-        if (!pooled) {
-          RowStat zero = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
-          A.rowstat[rr] = zero;
-        }
-      } else {
+  if (!A.rowstat && A.nchunks > 16) {
+    // many chunks per row (a small batch spread over the chip): one wave
+    // merges each row's partials
+    constexpr int NW = NT / kWave;
+    for (int t = w; t < nr; t += NW) {
+      const int64_t rr = A.map.sidx(b, t);
+      RowStat s = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
+      if (rr >= 0) {
         Partial* p = A.part + rr * A.nchunks;
-        s = merge_partials(p, A.nchunks, a);
+        s = merge_partials_wave(p, A.nchunks, a, lane);
         if (!pooled) {
-          for (int c = 0; c < A.nchunks; ++c) {
+          for (int c = lane; c < A.nchunks; c += kWave) {
             Partial zero = {0.f, 0u, 0.0};
             p[c] = zero;
           }
         }
       }
+      if (lane == 0) TS.st[t] = s;
     }
-    TS.st[t] = s;
+  } else {
+    for (int t = tid; t < nr; t += NT) {
+      const int64_t rr = A.map.sidx(b, t);
+      RowStat s = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
+      if (rr >= 0) {
+        if (A.rowstat) {
+          s = A.rowstat[rr];
+          if (!pooled) {
+            RowStat zero = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
+            A.rowstat[rr] = zero;
+          }
+        } else {
+          Partial* p = A.part + rr * A.nchunks;
+          s = merge_partials(p, A.nchunks, a);
+          if (!pooled) {
+            for (int c = 0; c < A.nchunks; ++c) {
+              Partial zero = {0.f, 0u, 0.0};
+              p[c] = zero;
+            }
+          }
+        }
+      }
+      TS.st[t] = s;
+    }
   }
   block_sync_lds();
 
@@ -1755,6 +1803,35 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
 // ---------------------------------------------------------------------------
 // Logits processing: merge (unfiltered) partials or copy (filtered) stats into
 // the caller's per-row records; keep a RowStat per row for the dense pass.
+__device__ __forceinline__ void write_row_stats(const RowStat& s, spec_row_stats_t* out) {
+  spec_row_stats_t o;
+  if (s.valid) {
+    o.max_logit = s.m;
+    o.threshold = s.thr;
+    o.log_norm = (float)log(s.z);
+    o.valid = 1;
+  } else {
+    o.max_logit = o.threshold = o.log_norm = __builtin_nanf("");
+    o.valid = 0;
+  }
+  *out = o;
+}
+
+// Rows split into many chunks: one wave merges each row's partials.
+__global__ __launch_bounds__(256) void k_process_stats_wide(int64_t R, int nchunks, float a,
+                                                            Partial* __restrict__ part,
+                                                            RowStat* __restrict__ rowstat,
+                                                            spec_row_stats_t* __restrict__ out) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (r >= R) return;  // whole waves
+  const RowStat s = merge_partials_wave(part + r * nchunks, nchunks, a, lane);
+  if (lane == 0) {
+    rowstat[r] = s;
+    if (out) write_row_stats(s, out + r);
+  }
+}
+
 __global__ __launch_bounds__(256) void k_process_stats(int64_t R, int nchunks, float a,
                                                        Partial* __restrict__ part,
                                                        RowStat* __restrict__ rowstat,
@@ -1768,19 +1845,7 @@ __global__ __launch_bounds__(256) void k_process_stats(int64_t R, int nchunks, f
   } else {
     s = rowstat[r];
   }
-  if (out) {
-    spec_row_stats_t o;
-    if (s.valid) {
-      o.max_logit = s.m;
-      o.threshold = s.thr;
-      o.log_norm = (float)log(s.z);
-      o.valid = 1;
-    } else {
-      o.max_logit = o.threshold = o.log_norm = __builtin_nanf("");
-      o.valid = 0;
-    }
-    out[r] = o;
-  }
+  if (out) write_row_stats(s, out + r);
 }
 
 template <typename T, bool VEC, int VPT>
