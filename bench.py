@@ -216,7 +216,7 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # Large batches of aligned bf16 rows take the whole-sequence walk (one
+    # Large batches of aligned bf16 rows take the position-task kernel (one
     # kernel: rows in walk order, nothing past the first rejection); other
     # shapes a row pass over every row and a per-sequence tail kernel.
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -280,7 +280,7 @@ def main():
     if walk:
         # the call is one kernel: its bytes are the rows it consults plus the
         # draw's second pass over the rows at the stop
-        kernel = "k_verify_seq_bf16 (whole-sequence walk, exact bf16 key histogram)"
+        kernel = "k_verify_task_bf16 (position-task queue, exact bf16 key histogram)"
         alg_bytes = np.mean([walk_rows[i % len(sets)] for i in range(args.steps)]) * row_bytes + draw_bytes
         kernel_ms = ms
     else:

@@ -24,16 +24,23 @@ struct Layout {
   int64_t rows = 0;  // rows processed
   size_t rowstat_off = 0, part_off = 0, queue_off = 0, total = 0;
   size_t help_off = 0;  // whole-sequence walk: the help region (sv::HelpView)
+  size_t slots_off = 0;  // position-task queue: the appended tasks (sv::TaskArgs::slots)
 };
 
 using sv::kMaxWalkGrid;
 
-// The whole-sequence walk's queue words and help region.
-size_t walk_regions(Layout& L, size_t off, int64_t k) {
+// The whole-sequence walk's queue words and help region, and (B > 0) the
+// position-task queue's slots (at most B k appended tasks plus one exit
+// entry per workgroup) followed by one state word per sequence.
+size_t walk_regions(Layout& L, size_t off, int64_t k, int64_t B) {
   L.queue_off = off;
   off = (off + 4 * sizeof(uint32_t) + 255) & ~size_t(255);
   L.help_off = off;
   off = (off + size_t(sv::HelpView::bytes(2 * k + 1)) + 255) & ~size_t(255);
+  if (B > 0) {
+    L.slots_off = off;
+    off = (off + size_t(B * k + kMaxWalkGrid + B) * sizeof(uint32_t) + 255) & ~size_t(255);
+  }
   return off;
 }
 
@@ -73,7 +80,7 @@ Layout make_layout(int op, int64_t B, int64_t k, int64_t V, const spec_sampling_
     L.part_off = off;
     off = align256(off + size_t(L.rows) * size_t(L.nchunks) * 16);
   }
-  if (op == SPEC_OP_STOCHASTIC) off = walk_regions(L, off, k);  // whole-sequence walk
+  if (op == SPEC_OP_STOCHASTIC) off = walk_regions(L, off, k, B);  // whole-sequence kernels
   L.total = off < 256 ? 256 : off;
   return L;
 }
@@ -98,7 +105,7 @@ Layout make_pooled_layout(int op, int64_t nt, int64_t nd, int64_t k, int64_t V,
     L.part_off = off;
     off = align256(off + size_t(L.rows) * size_t(L.nchunks) * 16);
   }
-  if (!greedy) off = walk_regions(L, off, k);
+  if (!greedy) off = walk_regions(L, off, k, 0);
   L.total = off < 256 ? 256 : off;
   return L;
 }
@@ -264,6 +271,16 @@ struct StochasticRun {
                   const spec_sampling_t& s, sv::TailArgs& args, char* ws, hipStream_t st,
                   int walk_grid) {
     if constexpr (sizeof(T) == 2 && VEC) {
+      if (walk_grid > 0 && !args.accept_prob) {
+        sv::TaskArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
+                       args.accepted_len, args.out_tokens,
+                       reinterpret_cast<uint32_t*>(ws + L.queue_off),
+                       reinterpret_cast<uint32_t*>(ws + L.slots_off),
+                       reinterpret_cast<uint32_t*>(ws + L.slots_off) + (B * args.k + kMaxWalkGrid)};
+        hipLaunchKernelGGL((sv::k_verify_task_bf16<kPrefetch, kLoadDepth>),
+                           dim3(unsigned(walk_grid)), dim3(kFilterThreads), 0, st, A);
+        return;
+      }
       if (walk_grid > 0) {
         sv::SeqArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
                       args.accepted_len, args.out_tokens, args.accept_prob,
