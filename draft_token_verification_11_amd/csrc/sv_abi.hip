@@ -25,6 +25,10 @@ struct Layout {
   size_t rowstat_off = 0, part_off = 0, queue_off = 0, total = 0;
   size_t help_off = 0;  // whole-sequence walk: the help region (sv::HelpView)
   size_t slots_off = 0;  // position-task queue: the appended tasks (sv::TaskArgs::slots)
+  // correction draw spread over the chip (small batches on the row-pass path)
+  bool split_draw = false;
+  int64_t draw_chunks = 0;
+  size_t jobs_off = 0, dsums_off = 0;
 };
 
 using sv::kMaxWalkGrid;
@@ -45,6 +49,10 @@ size_t walk_regions(Layout& L, size_t off, int64_t k, int64_t B) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Batches of at most this many sequences may spread their correction draws
+// over the chip (when they leave most CUs idle and the rows span chunks).
+constexpr int64_t kSplitDrawMaxB = 128;
 
 int64_t chunk_elems(int vpt) { return int64_t(kRowThreads) * vpt * 8; }
 
@@ -81,6 +89,15 @@ Layout make_layout(int op, int64_t B, int64_t k, int64_t V, const spec_sampling_
     off = align256(off + size_t(L.rows) * size_t(L.nchunks) * 16);
   }
   if (op == SPEC_OP_STOCHASTIC) off = walk_regions(L, off, k, B);  // whole-sequence kernels
+  if (op == SPEC_OP_STOCHASTIC && B <= kSplitDrawMaxB) {
+    // per sequence a draw job and the residual's sum over each chunk
+    L.split_draw = true;
+    L.draw_chunks = (V + sv::kDrawChunk - 1) / sv::kDrawChunk;
+    L.jobs_off = off;
+    off = align256(off + size_t(B) * sizeof(sv::DrawJob));
+    L.dsums_off = off;
+    off = align256(off + size_t(B) * size_t(L.draw_chunks) * sizeof(double));
+  }
   L.total = off < 256 ? 256 : off;
   return L;
 }
@@ -303,7 +320,21 @@ struct StochasticRun {
       args.part = part;
     }
     args.nchunks = L.nchunks;
+    // small batches: the draws spread over the chip instead of one tail
+    // workgroup per sequence reading its two rows alone
+    const bool split = VEC && L.split_draw && L.draw_chunks >= 2 && 2 * B <= device_cus();
+    auto* jobs = reinterpret_cast<sv::DrawJob*>(ws + L.jobs_off);
+    auto* dsums = reinterpret_cast<double*>(ws + L.dsums_off);
+    args.jobs = split ? jobs : nullptr;
     launch_tail<T, VEC>(B, args, st);
+    if (split) {
+      hipLaunchKernelGGL((sv::k_draw_sums<T, VEC>), dim3(unsigned(L.draw_chunks), unsigned(B)),
+                         dim3(sv::kDrawThreads), 0, st, map, V, args.k, a, jobs, L.draw_chunks,
+                         dsums);
+      hipLaunchKernelGGL((sv::k_draw_pick<T, VEC>), dim3(unsigned(B)), dim3(sv::kDrawThreads), 0,
+                         st, map, V, args.k, a, jobs, L.draw_chunks, dsums, args.u,
+                         args.accepted_len, args.out_tokens);
+    }
   }
 };
 

@@ -824,6 +824,8 @@ __global__ __launch_bounds__(1024) void k_filter_bf16_hist(RowMap map, int64_t V
 // wave-contiguous segments of the row, 8 elements per lane per step, fp64
 // running sums (wave totals -> crossing wave -> crossing step -> crossing
 // lane -> crossing element, all from the same additions).
+struct DrawJob;
+
 struct TailArgs {
   RowMap map;
   int64_t V;
@@ -837,6 +839,10 @@ struct TailArgs {
   int32_t* accepted_len;
   int32_t* out_tokens;
   float* accept_prob;
+  // non-null: the correction draw is left to k_draw_sums / k_draw_pick; the
+  // tail writes each valid sequence's job and every output but the drawn
+  // token and the accepted length
+  DrawJob* jobs = nullptr;
 };
 
 struct TailScratch {
@@ -1067,6 +1073,285 @@ __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const
   return *emit_slot;
 }
 
+// ---------------------------------------------------------------------------
+// Correction draw spread over the chip, for small batches on the row-pass
+// path (one tail workgroup per sequence would read the two rows at the stop
+// alone while the other CUs sit idle).  The tail writes each sequence's
+// DrawJob; k_draw_sums computes the residual's sum over every chunk of
+// kDrawChunk elements of the two rows at the stop (one workgroup per
+// chunk); k_draw_pick finds the chunk where the running sum in ascending
+// vocabulary order passes u S, and the element inside it.  Both kernels
+// form a chunk's sum by the same additions (per-thread fp64 sums of fp32
+// group sums, then one block scan), so the chunk picked from the table
+// always holds the crossing.
+struct DrawJob {  // 48 bytes
+  DrawStats sp, sq;  // processed target row at the stop, and draft row (unused for the bonus)
+  int32_t n;         // the stop (k: the bonus draw from p_k)
+  int32_t active;    // 0: nothing to draw (invalid sequence, outputs already written)
+  int32_t pad[2];
+};
+constexpr int kDrawThreads = 256;
+constexpr int kDrawGroups = 4;  // groups of 8 elements per thread
+constexpr int64_t kDrawChunk = (int64_t)kDrawThreads * kDrawGroups * 8;  // 8,192 elements
+
+// The residual (or p) of the 8 elements at e, fp32, as in residual_draw.
+template <typename T, bool VEC>
+__device__ __forceinline__ void draw_group(const T* prow, const T* qrow, bool resid,
+                                           const DrawJob& J, float lzp, float lzq, float a,
+                                           int64_t V, int64_t e, float* r8) {
+  Raw8<T> rp, rq;
+  load8_raw<T, VEC>(prow, e, V, rp);
+  if (resid) load8_raw<T, VEC>(qrow, e, V, rq);
+  float lp[8], lq[8];
+  unpack8<T>(rp, lp);
+  if (resid) unpack8<T>(rq, lq);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float p = lp[i] >= J.sp.thr
+                        ? __builtin_amdgcn_exp2f(__builtin_fmaf(lp[i] - J.sp.m, a, -lzp))
+                        : 0.0f;
+    float r = p;
+    if (resid) {
+      const float q = lq[i] >= J.sq.thr
+                          ? __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i] - J.sq.m, a, -lzq))
+                          : 0.0f;
+      r = fmaxf(p - q, 0.0f);
+    }
+    r8[i] = r;
+  }
+}
+
+// This thread's share of chunk c: the fp32 sums of its groups (in element
+// order) and their fp64 total (in group order).
+template <typename T, bool VEC>
+__device__ __forceinline__ double draw_thread_sum(const T* prow, const T* qrow, bool resid,
+                                                  const DrawJob& J, float lzp, float lzq, float a,
+                                                  int64_t V, int64_t c, int tid, float* gs) {
+  const int64_t e0 = c * kDrawChunk + (int64_t)tid * (kDrawGroups * 8);
+  Raw8<T> rp[kDrawGroups], rq[kDrawGroups];
+#pragma unroll
+  for (int g = 0; g < kDrawGroups; ++g) {  // every load issued before any is used
+    load8_raw<T, VEC>(prow, e0 + 8 * g, V, rp[g]);
+    if (resid) load8_raw<T, VEC>(qrow, e0 + 8 * g, V, rq[g]);
+  }
+  double tot = 0.0;
+#pragma unroll
+  for (int g = 0; g < kDrawGroups; ++g) {
+    float lp[8], lq[8];
+    unpack8<T>(rp[g], lp);
+    if (resid) unpack8<T>(rq[g], lq);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = lp[i] >= J.sp.thr
+                          ? __builtin_amdgcn_exp2f(__builtin_fmaf(lp[i] - J.sp.m, a, -lzp))
+                          : 0.0f;
+      float r = p;
+      if (resid) {
+        const float q = lq[i] >= J.sq.thr
+                            ? __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i] - J.sq.m, a, -lzq))
+                            : 0.0f;
+        r = fmaxf(p - q, 0.0f);
+      }
+      acc += r;
+    }
+    gs[g] = acc;
+    tot += (double)acc;
+  }
+  return tot;
+}
+
+// Inclusive scan of one double per thread over the 256 threads (wave scans,
+// then the four wave totals added in wave order); *total is the last
+// thread's value, formed by the same additions.
+__device__ __forceinline__ double block_incl_scan256(double x, double* slots, double* total) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const double inc = wave_incl_scan(x);
+  if (lane == kWave - 1) slots[w] = inc;
+  block_sync_lds();
+  double base = 0.0;
+  for (int v = 0; v < w; ++v) base += slots[v];
+  *total = ((slots[0] + slots[1]) + slots[2]) + slots[3];
+  return base + inc;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_sums(RowMap map, int64_t V, int k, float a,
+                                                           const DrawJob* __restrict__ jobs,
+                                                           int64_t nch, double* __restrict__ sums) {
+  __shared__ double slots[kDrawThreads / kWave];
+  const int64_t b = blockIdx.y, c = blockIdx.x;
+  const DrawJob J = jobs[b];
+  if (!J.active) return;  // the sums of an inactive sequence stay zero
+  const bool resid = J.n < k;
+  const T* prow = map.template at<T>(b, J.n);
+  const T* qrow = resid ? map.template at<T>(b, k + 1 + J.n) : prow;
+  const float lzp = log2_norm(J.sp.z), lzq = resid ? log2_norm(J.sq.z) : 0.0f;
+  float gs[kDrawGroups];
+  const double x = draw_thread_sum<T, VEC>(prow, qrow, resid, J, lzp, lzq, a, V, c,
+                                           (int)threadIdx.x, gs);
+  double total;
+  (void)block_incl_scan256(x, slots, &total);
+  if (threadIdx.x == 0) sums[b * nch + c] = total;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_pick(RowMap map, int64_t V, int k, float a,
+                                                           DrawJob* __restrict__ jobs, int64_t nch,
+                                                           double* __restrict__ sums,
+                                                           const float* __restrict__ u,
+                                                           int32_t* __restrict__ accepted_len,
+                                                           int32_t* __restrict__ out_tokens) {
+  __shared__ double slots[kDrawThreads / kWave];
+  __shared__ int32_t emit;
+  __shared__ int64_t sh_chunk;
+  __shared__ double sh_target, sh_S;
+  __shared__ int32_t sh_last, sh_pick;
+  __shared__ uint64_t sh_hits[kDrawThreads / kWave], sh_pos[kDrawThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int64_t b = blockIdx.x;
+  const DrawJob J = jobs[b];
+  if (!J.active) return;
+  const int n = J.n;
+  bool resid = n < k;
+  const T* prow = map.template at<T>(b, n);
+  const T* qrow = resid ? map.template at<T>(b, k + 1 + n) : prow;
+  const float uu = u[b * (k + 1) + k];
+  double* sb = sums + b * nch;
+  const float lzp = log2_norm(J.sp.z), lzq = resid ? log2_norm(J.sq.z) : 0.0f;
+
+  // A residual without mass falls back to p at the stop: this workgroup
+  // forms p's chunk sums (the rows are read once more; rounding makes this
+  // case all but unreachable).
+  if (w == 0) {
+    double carry = 0.0;
+    for (int64_t base = 0; base < nch; base += kWave)
+      carry += wave_sum(base + lane < nch ? sb[base + lane] : 0.0);
+    if (lane == 0) sh_S = carry;
+  }
+  block_sync_lds();
+  if (resid && !(sh_S > 0.0)) {
+    resid = false;
+    for (int64_t c = 0; c < nch; ++c) {
+      float gs[kDrawGroups];
+      const double x = draw_thread_sum<T, VEC>(prow, qrow, false, J, lzp, lzq, a, V, c, tid, gs);
+      double total;
+      (void)block_incl_scan256(x, slots, &total);
+      if (tid == 0) sb[c] = total;
+      block_sync_lds();  // slots are rewritten by the next chunk's scan
+    }
+    __syncthreads();  // the new sums (global memory) visible to wave 0
+  }
+
+  // Wave 0: S, the target u S, and the first chunk whose running sum
+  // exceeds it (if rounding leaves none, the last chunk with mass).
+  if (w == 0) {
+    double carry = 0.0;
+    for (int64_t base = 0; base < nch; base += kWave)
+      carry += wave_sum(base + lane < nch ? sb[base + lane] : 0.0);
+    const double S = carry, target = (double)uu * S;
+    int64_t pick = -1, lastpos = -1;
+    double before = 0.0, before_last = 0.0, run = 0.0;
+    for (int64_t base = 0; base < nch && pick < 0; base += kWave) {
+      const double x = base + lane < nch ? sb[base + lane] : 0.0;
+      const double inc = wave_incl_scan(x) + run;
+      const uint64_t hit = __ballot(base + lane < nch && inc > target);
+      const uint64_t pos = __ballot(base + lane < nch && x > 0.0);
+      if (pos) {
+        const int L = 63 - __clzll((long long)pos);
+        lastpos = base + L;
+        before_last = bcast(inc - x, L);
+      }
+      if (hit) {
+        const int L = __ffsll((unsigned long long)hit) - 1;
+        pick = base + L;
+        before = bcast(inc - x, L);
+      }
+      run = bcast(inc, kWave - 1);
+    }
+    if (lane == 0) {
+      sh_S = S;
+      sh_last = pick < 0 ? 1 : 0;
+      sh_chunk = pick >= 0 ? pick : (lastpos >= 0 ? lastpos : 0);
+      sh_target = target - (pick >= 0 ? before : before_last);
+    }
+  }
+  block_sync_lds();
+  int32_t emitted;
+  {
+    const int64_t c = sh_chunk;
+    const bool last = sh_last != 0;
+    const double tc = sh_target;  // the target within chunk c
+    float gs[kDrawGroups];
+    const double x = draw_thread_sum<T, VEC>(prow, qrow, resid, J, lzp, lzq, a, V, c, tid, gs);
+    double total;
+    const double inc = block_incl_scan256(x, slots, &total);
+    // the first thread whose running sum exceeds the target, else the last
+    // thread with mass
+    const uint64_t hit = __ballot(!last && inc > tc);
+    const uint64_t pos = __ballot(x > 0.0);
+    if (lane == 0) {
+      sh_hits[w] = hit;
+      sh_pos[w] = pos;
+    }
+    block_sync_lds();
+    if (tid == 0) {
+      int t = -1;
+      for (int v = 0; v < kDrawThreads / kWave && t < 0; ++v)
+        if (sh_hits[v]) t = v * kWave + __ffsll((unsigned long long)sh_hits[v]) - 1;
+      if (t < 0)
+        for (int v = kDrawThreads / kWave - 1; v >= 0 && t < 0; --v)
+          if (sh_pos[v]) t = v * kWave + 63 - __clzll((long long)sh_pos[v]);
+      sh_pick = t < 0 ? 0 : t;
+      emit = -1;
+    }
+    block_sync_lds();
+    if (tid == sh_pick) {
+      // walk this thread's groups, then the elements of the crossing group
+      const bool crossing = !last && inc > tc;
+      double run = inc - x;
+      const int64_t e0 = c * kDrawChunk + (int64_t)tid * (kDrawGroups * 8);
+      int64_t found = -1, lastpos = -1;
+      for (int g = 0; g < kDrawGroups && found < 0; ++g) {
+        if (crossing && !(run + (double)gs[g] > tc)) {
+          run += (double)gs[g];
+          continue;
+        }
+        float r8[8];
+        draw_group<T, VEC>(prow, qrow, resid, J, lzp, lzq, a, V, e0 + 8 * g, r8);
+        for (int i = 0; i < 8; ++i) {
+          if (r8[i] > 0.0f) lastpos = e0 + 8 * g + i;
+          if (crossing && found < 0 && run + (double)r8[i] > tc) found = e0 + 8 * g + i;
+          run += (double)r8[i];
+        }
+        if (crossing) break;  // the crossing group: rounding inside it ends the walk here
+      }
+      emit = (int32_t)(found >= 0 ? found : (lastpos >= 0 ? lastpos : c * kDrawChunk));
+    }
+    block_sync_lds();
+    emitted = emit;
+  }
+  if (tid == 0) {
+    out_tokens[b * (k + 1) + n] = emitted;
+    accepted_len[b] = n;
+  }
+  // leave this sequence's job and chunk sums zero for the next call
+  block_sync_lds();
+  for (int64_t i = tid; i < nch; i += kDrawThreads) sums[b * nch + i] = 0.0;
+  if (tid < (int)(sizeof(DrawJob) / 4)) reinterpret_cast<int32_t*>(jobs + b)[tid] = 0;
+}
+
+__device__ __forceinline__ void write_draw_job(DrawJob* job, const DrawStats& sp, const DrawStats& sq,
+                                               int n) {
+  DrawJob J;
+  J.sp = sp;
+  J.sq = sq;
+  J.n = n;
+  J.active = 1;
+  J.pad[0] = J.pad[1] = 0;
+  *job = J;
+}
+
 template <typename T, bool VEC, int NT>
 __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   const int k = A.k;
@@ -1168,6 +1453,13 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
 
   // Residual max(0, p_n - q_n) (n < k) or the bonus row's p_k (n = k).
   const bool has_q = n < k;
+  if (A.jobs) {
+    for (int j = tid; j <= k; j += NT)
+      if (j != n) out[j] = j < n ? A.tokens[b * k + j] : -1;
+    if (tid == 0) write_draw_job(A.jobs + b, draw_stats(TS.st[n]),
+                                 draw_stats(has_q ? TS.st[k + 1 + n] : TS.st[n]), n);
+    return;
+  }
   const T* prow = A.map.at<T>(b, n);
   const T* qrow = has_q ? A.map.at<T>(b, k + 1 + n) : prow;
   const int32_t emitted =

@@ -61,12 +61,19 @@ def compare_stochastic(ref, acc, out, ap, rows=None, fp32=True, label=""):
     a_gpu = g_ap[~nan_ref].astype(np.float64)
     # alpha = min(1, p/q) is a probability: 1e-6 absolute for fp32 inputs
     # (plus the fp32 rounding of the reported value), 2e-3 relative for bf16.
+    # Where a row's top-p cut mass lies within 1e-6 of top_p (flag bit 2),
+    # which tokens are kept is itself undecided at that tolerance, so the
+    # normaliser may legitimately differ by the mass of the tokens at the
+    # cut: those sequences get a sanity bound of 1e-4 instead.
+    cut = np.broadcast_to(((flags & 4) != 0)[:, None], ref["accept_prob"].shape)[~nan_ref]
     if fp32:
         bound = 1e-6 + 1.2e-7 * np.abs(a_ref)
     else:
         bound = 2e-3 * np.abs(a_ref) + 1e-7
+    bound = np.where(cut, np.maximum(bound, 1e-4), bound)
     err = np.abs(a_gpu - a_ref)
-    assert (err <= bound).all(), (label, float((err - bound).max()))
+    assert (err <= bound).all(), (label, float((err - bound).max()),
+                                  "cut-flagged" if bool(cut[np.argmax(err - bound)]) else "unflagged")
     nflag = int((flags != 0).sum())
     note("%s: %d sequences, %d boundary-flagged, mean accepted %.3f"
          % (label, len(rows), nflag, float(ref["accepted_len"][valid].mean()) if valid.any() else -1))
