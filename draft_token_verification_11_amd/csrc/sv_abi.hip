@@ -54,6 +54,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // over the chip (when they leave most CUs idle and the rows span chunks).
 constexpr int64_t kSplitDrawMaxB = 128;
 
+// Unfiltered rows of at most this many elements get their statistics in the
+// tail (one launch fewer; a wave reads such a row in a few steps).
+constexpr int64_t kDirectMaxV = 4096;
+
 int64_t chunk_elems(int vpt) { return int64_t(kRowThreads) * vpt * 8; }
 
 int pick_vpt(int64_t rows, int64_t V) {
@@ -312,6 +316,10 @@ struct StochasticRun {
       auto* rs = reinterpret_cast<sv::RowStat*>(ws + L.rowstat_off);
       launch_filter<T, VEC>(L, map, V, a, s, rs, st);
       args.rowstat = rs;
+      args.part = nullptr;
+    } else if (V <= kDirectMaxV) {
+      // small unfiltered rows: the tail computes their statistics itself
+      args.rowstat = nullptr;
       args.part = nullptr;
     } else {
       auto* part = reinterpret_cast<sv::Partial*>(ws + L.part_off);

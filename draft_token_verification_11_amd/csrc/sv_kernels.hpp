@@ -1366,7 +1366,48 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   // alone and their workspace records are cleared here; pooled records are
   // shared and cleared by a pass of their own after every sequence is done.
   const bool pooled = A.map.nt > 0;
-  if (!A.rowstat && A.nchunks > 16) {
+  if (!A.rowstat && !A.part) {
+    // small unfiltered rows (no row pass): each wave computes the max and
+    // the sum of 2^((l - m) a) of its rows, reading each row twice (the
+    // second read from cache)
+    constexpr int NW = NT / kWave;
+    for (int t = w; t < nr; t += NW) {
+      const int64_t rr = A.map.sidx(b, t);
+      RowStat s = {0.f, 0.f, 0.0, 0, {0, 0, 0}};
+      if (rr >= 0) {
+        const T* row = A.map.template row<T>(rr);
+        float m = -__builtin_inff();
+        bool bad = false;
+        for (int64_t e = (int64_t)lane * 8; e < V; e += kWave * 8) {
+          float x[8];
+          load8<T, VEC>(row, e, V, x);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            bad = bad || bad_logit(x[i]);
+            m = fmaxf(m, x[i]);
+          }
+        }
+        m = wave_max(m);
+        bad = __ballot(bad) != 0;
+        double z = 0.0;
+        if (!bad && m > -__builtin_inff()) {
+          for (int64_t e = (int64_t)lane * 8; e < V; e += kWave * 8) {
+            float x[8], ex[8];
+            load8<T, VEC>(row, e, V, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ex[i] = __builtin_amdgcn_exp2f((x[i] - m) * a);
+            z += (double)(((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7])));
+          }
+          z = wave_sum(z);
+        }
+        s.m = m;
+        s.thr = -__builtin_inff();
+        s.z = z;
+        s.valid = (!bad && m > -__builtin_inff()) ? 1 : 0;
+      }
+      if (lane == 0) TS.st[t] = s;
+    }
+  } else if (!A.rowstat && A.nchunks > 16) {
     // many chunks per row (a small batch spread over the chip): one wave
     // merges each row's partials
     constexpr int NW = NT / kWave;
