@@ -276,6 +276,9 @@ def main():
     row_kernel = ("k_filter_bf16_persistent (exact bf16 key histogram, top-k/top-p)"
                   if c.dtype == "bf16" and (c.top_k or c.top_p < 1.0) else
                   "k_filter_bisect (fp32 top-k/top-p)" if (c.top_k or c.top_p < 1.0) else
+                  "k_row_partials (split-V max / sum of exponentials; rows of V <= 4096 get "
+                  "their statistics in the tail instead, this line times the row pass alone)"
+                  if c.V <= 4096 else
                   "k_row_partials (split-V max / sum of exponentials)")
     if walk:
         # the call is one kernel: its bytes are the rows it consults plus the
