@@ -71,3 +71,21 @@ def test_split_draw_invalid_and_workspace():
     assert np.array_equal(acc[ok], ref["accepted_len"][ok])
     assert np.array_equal(out[ok], ref["out_tokens"][ok])
     assert (out[:3] == -1).all()
+
+
+def test_split_draw_strided_ragged_and_batch_edges():
+    """V = 20001 at a padded row stride of 20008 (aligned rows, a partial last
+    vector), and batches on both sides of the spread draw's batch limit
+    (B = 128 spreads its draws on a 256-CU part, B = 129 does not)."""
+    rs = np.random.default_rng(83)
+    k, V, Sd = 2, 20001, 20008
+    for B in (128, 129):
+        t, d, toks, u = _case(rs, B, k, V, 1.0, 0, 0.95, True, 0.7)
+        tp = np.zeros((B, k + 1, Sd), np.uint16)
+        tp[:, :, :V] = t
+        dp = np.zeros((B, k, Sd), np.uint16)
+        dp[:, :, :V] = d
+        ref = oracle.verify_stochastic(t, d, toks, u, 1.0, 0, 0.95)
+        acc, out, ap = gpu_stochastic(to_dev(tp)[:, :, :V], to_dev(dp)[:, :, :V], toks, u,
+                                      1.0, 0, 0.95)
+        compare_stochastic(ref, acc, out, ap, fp32=False, label="split draw strided B=%d" % B)
