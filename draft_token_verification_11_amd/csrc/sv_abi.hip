@@ -669,7 +669,10 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
     return SPEC_ERR_WORKSPACE;
   const int64_t M = int64_t(B) * (k + 1);
-  const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  // 16-row blocks per workgroup: more rows per chunk re-read the head fewer
+  // times; beyond 96 the accumulators leave one wave per SIMD, which
+  // measured slower (128 and 144 rows against 96 at 72 to 864 rows)
+  const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 6));
   const int64_t tiles = (int64_t(V) + kLmTile - 1) / kLmTile;
   const int64_t chunks = (M + 16 * mb - 1) / (16 * mb);
   const int64_t nblk = tiles * chunks;
@@ -685,6 +688,7 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   switch (mb) {
     case 1: hipLaunchKernelGGL((sv::k_lmhead_argmax<1, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
     case 2: hipLaunchKernelGGL((sv::k_lmhead_argmax<2, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
+    case 6: hipLaunchKernelGGL((sv::k_lmhead_argmax<6, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
     default: hipLaunchKernelGGL((sv::k_lmhead_argmax<4, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
   }
   // the greedy rule over the per-tile records (dense rows: b (k+1) + j)
