@@ -669,12 +669,16 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
     return SPEC_ERR_WORKSPACE;
   const int64_t M = int64_t(B) * (k + 1);
-  // 16-row blocks per workgroup: more rows per chunk re-read the head fewer
-  // times; beyond 96 the accumulators leave one wave per SIMD, which
-  // measured slower (128 and 144 rows against 96 at 72 to 864 rows)
+  // Up to 256 rows: 256-entry tiles, fragments loaded straight from memory,
+  // 16, 32, 64 or 96 rows per chunk (more rows per chunk re-read the head
+  // fewer times; beyond 96 the accumulators leave one wave per SIMD, which
+  // measured slower).  More rows: the LDS-staged tiling of 128 x 128 tiles
+  // (at 144 rows its padded second row tile made it slower).
+  const bool gemm = M > 256;
   const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 6));
-  const int64_t tiles = (int64_t(V) + kLmTile - 1) / kLmTile;
-  const int64_t chunks = (M + 16 * mb - 1) / (16 * mb);
+  const int64_t tw = gemm ? sv::kGemmBN : kLmTile, mr = gemm ? sv::kGemmBM : 16 * mb;
+  const int64_t tiles = (int64_t(V) + tw - 1) / tw;
+  const int64_t chunks = (M + mr - 1) / mr;
   const int64_t nblk = tiles * chunks;
   const int64_t grid = (nblk + 7) / 8 * 8;
   if (!grid_fits(grid, 256) || !grid_fits(B, 64)) return SPEC_ERR_UNSUPPORTED;
@@ -685,7 +689,10 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
                    int32_t(tiles), int32_t(chunks), best, bad};
   auto st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  switch (mb) {
+  if (gemm) {
+    // stages of 128 along d: half the latency waits of 64-wide stages
+    hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<128>), dim3(unsigned(grid)), dim3(256), 0, st, A);
+  } else switch (mb) {
     case 1: hipLaunchKernelGGL((sv::k_lmhead_argmax<1, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
     case 2: hipLaunchKernelGGL((sv::k_lmhead_argmax<2, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
     case 6: hipLaunchKernelGGL((sv::k_lmhead_argmax<6, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
