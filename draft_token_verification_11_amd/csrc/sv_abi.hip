@@ -718,7 +718,7 @@ int spec_logits_apply(spec_logits_t in, int32_t S, int32_t rows, int32_t V,
   if (proc->allow_seq_stride < 0 || proc->allow_pos_stride < 0 || proc->pen_seq_stride < 0 ||
       proc->pen_pos_stride < 0)
     return SPEC_ERR_INVALID_ARG;
-  const int64_t nch = (int64_t(V) + 2047) / 2048;
+  const int64_t nch = (int64_t(V) + sv::kApplyChunk - 1) / sv::kApplyChunk;
   const int64_t blocks = int64_t(S) * rows * nch;
   if (!grid_fits(blocks, 256)) return SPEC_ERR_UNSUPPORTED;
   sv::ApplyArgs A{in.data, in.seq_stride, in.pos_stride, const_cast<void*>(out.data),

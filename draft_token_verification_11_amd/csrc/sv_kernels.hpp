@@ -2625,49 +2625,68 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Four groups of 8 elements per thread, 2,048 elements apart (each load
+// instruction of a wave covers 1,024 consecutive elements), all loads in
+// flight together.
+constexpr int kApplyGroups = 4;
+constexpr int64_t kApplyChunk = 256 * kApplyGroups * 8;  // elements per workgroup
+
 template <typename TI, typename TO, bool VEC>
 __global__ __launch_bounds__(256) void k_logits_apply(ApplyArgs A) {
   const int64_t blk = blockIdx.x;
   const int64_t r = blk / A.nchunks;
   const int64_t c = blk - r * A.nchunks;
   const int64_t s = r / A.rows, j = r - s * A.rows;
-  const int64_t e0 = c * 2048 + (int64_t)threadIdx.x * 8;
+  const int64_t e0 = c * kApplyChunk + (int64_t)threadIdx.x * 8;
   if (e0 >= A.V) return;
   const TI* row = reinterpret_cast<const TI*>(A.in) + s * A.in_seq + j * A.in_pos;
-  Raw8<TI> raw;
-  load8_raw<TI, VEC>(row, e0, A.V, raw);
-  float l[8];
-  unpack8<TI>(raw, l);
-  // e0 is a multiple of 8: the 8 bits lie in one word
-  const uint32_t sh = (uint32_t)(e0 & 31);
-  const uint32_t aw = A.allow ? (A.allow[s * A.a_seq + j * A.a_pos + (e0 >> 5)] >> sh) : 0xFFu;
-  const uint32_t pw = A.pen ? (A.pen[s * A.p_seq + j * A.p_pos + (e0 >> 5)] >> sh) : 0u;
+  const uint32_t* am = A.allow ? A.allow + s * A.a_seq + j * A.a_pos : nullptr;
+  const uint32_t* pm = A.pen ? A.pen + s * A.p_seq + j * A.p_pos : nullptr;
+  Raw8<TI> raw[kApplyGroups];
+  uint32_t aw[kApplyGroups], pw[kApplyGroups];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float v = l[i];
-    if (!((aw >> i) & 1u)) v = -__builtin_inff();
-    else if ((pw >> i) & 1u) v = v > 0.0f ? v / A.theta : v * A.theta;
-    l[i] = v;
-  }
-  const int64_t n = A.V - e0 < 8 ? A.V - e0 : 8;
-  if constexpr (sizeof(TO) == 4) {
-    float* o = reinterpret_cast<float*>(A.out) + s * A.out_seq + j * A.out_pos + e0;
-    if (VEC && n == 8) {
-      *reinterpret_cast<float4*>(o) = make_float4(l[0], l[1], l[2], l[3]);
-      *reinterpret_cast<float4*>(o + 4) = make_float4(l[4], l[5], l[6], l[7]);
-    } else {
-      for (int i = 0; i < n; ++i) o[i] = l[i];
+  for (int q = 0; q < kApplyGroups; ++q) {
+    const int64_t eq = e0 + 2048 * q;
+    if (eq < A.V) {
+      load8_raw<TI, VEC>(row, eq, A.V, raw[q]);
+      // eq is a multiple of 8: its 8 bits lie in one word
+      aw[q] = am ? am[eq >> 5] >> (uint32_t)(eq & 31) : 0xFFu;
+      pw[q] = pm ? pm[eq >> 5] >> (uint32_t)(eq & 31) : 0u;
     }
-  } else {
-    uint16_t* o = reinterpret_cast<uint16_t*>(A.out) + s * A.out_seq + j * A.out_pos + e0;
-    uint32_t h[8];
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = bf16_rne(l[i]);
-    if (VEC && n == 8) {
-      *reinterpret_cast<uint4*>(o) = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
-                                                h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  for (int q = 0; q < kApplyGroups; ++q) {
+    const int64_t eq = e0 + 2048 * q;
+    if (eq >= A.V) break;
+    float l[8];
+    unpack8<TI>(raw[q], l);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v = l[i];
+      if (!((aw[q] >> i) & 1u)) v = -__builtin_inff();
+      else if ((pw[q] >> i) & 1u) v = v > 0.0f ? v / A.theta : v * A.theta;
+      l[i] = v;
+    }
+    const int64_t n = A.V - eq < 8 ? A.V - eq : 8;
+    if constexpr (sizeof(TO) == 4) {
+      float* o = reinterpret_cast<float*>(A.out) + s * A.out_seq + j * A.out_pos + eq;
+      if (VEC && n == 8) {
+        *reinterpret_cast<float4*>(o) = make_float4(l[0], l[1], l[2], l[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(l[4], l[5], l[6], l[7]);
+      } else {
+        for (int i = 0; i < n; ++i) o[i] = l[i];
+      }
     } else {
-      for (int i = 0; i < n; ++i) o[i] = (uint16_t)h[i];
+      uint16_t* o = reinterpret_cast<uint16_t*>(A.out) + s * A.out_seq + j * A.out_pos + eq;
+      uint32_t h[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[i] = bf16_rne(l[i]);
+      if (VEC && n == 8) {
+        *reinterpret_cast<uint4*>(o) = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16),
+                                                  h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      } else {
+        for (int i = 0; i < n; ++i) o[i] = (uint16_t)h[i];
+      }
     }
   }
 }
