@@ -456,7 +456,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": c.dtype,
+        # the arithmetic of the path: per-element probabilities in fp32 (sums and
+        # the ratio test in fp64); the logits themselves are config.logits_dtype
+        "dtype": "fp32",
         "data": "synthetic (seeded generators, see workloads/)",
         "config": {"workload": c.name, "B": c.B, "k": c.k, "V": c.V, "logits_dtype": c.dtype,
                    "temperature": c.temperature, "top_k": c.top_k, "top_p": c.top_p,
