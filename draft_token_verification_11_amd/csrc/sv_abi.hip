@@ -669,13 +669,11 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256)
     return SPEC_ERR_WORKSPACE;
   const int64_t M = int64_t(B) * (k + 1);
-  // Up to 256 rows: 256-entry tiles, fragments loaded straight from memory,
-  // 16, 32, 64 or 96 rows per chunk (more rows per chunk re-read the head
-  // fewer times; beyond 96 the accumulators leave one wave per SIMD, which
-  // measured slower).  More rows: the LDS-staged tiling of 128 x 128 tiles
-  // (at 144 rows its padded second row tile made it slower).
-  const bool gemm = M > 256;
-  const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 6));
+  // Up to 64 rows: 256-entry tiles, fragments loaded straight from memory,
+  // 16, 32 or 64 rows per chunk.  More rows: the LDS-staged tiling of
+  // 128 x 128 tiles, two workgroups per CU.
+  const bool gemm = M > 64;
+  const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   const int64_t tw = gemm ? sv::kGemmBN : kLmTile, mr = gemm ? sv::kGemmBM : 16 * mb;
   const int64_t tiles = (int64_t(V) + tw - 1) / tw;
   const int64_t chunks = (M + mr - 1) / mr;
@@ -690,12 +688,10 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   auto st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (gemm) {
-    // stages of 128 along d: half the latency waits of 64-wide stages
-    hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<128>), dim3(unsigned(grid)), dim3(256), 0, st, A);
+    hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<64>), dim3(unsigned(grid)), dim3(256), 0, st, A);
   } else switch (mb) {
     case 1: hipLaunchKernelGGL((sv::k_lmhead_argmax<1, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
     case 2: hipLaunchKernelGGL((sv::k_lmhead_argmax<2, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
-    case 6: hipLaunchKernelGGL((sv::k_lmhead_argmax<6, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
     default: hipLaunchKernelGGL((sv::k_lmhead_argmax<4, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
   }
   // the greedy rule over the per-tile records (dense rows: b (k+1) + j)

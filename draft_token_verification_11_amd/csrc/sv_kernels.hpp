@@ -2849,12 +2849,14 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(LmHeadArgs A) {
 // current stage's fragments are read from LDS and multiplied, so every
 // fragment is loaded from memory once per workgroup instead of once per
 // wave.  LDS rows are padded by 16 bytes so that the 16 rows a fragment
-// read touches fall on different banks.  One stage in flight leaves the
-// kernel bound by memory latency: wider stages wait fewer times.
+// read touches fall on different banks.  With one stage in flight per
+// workgroup the kernel is bound by memory latency, so it is built for two
+// workgroups per CU (64-wide stages: 75 KiB of LDS and at most 256
+// registers per lane each), whose stages overlap.
 constexpr int kGemmBM = 128, kGemmBN = 128;
 
 template <int BK>
-__global__ __launch_bounds__(256) void k_lmhead_gemm_argmax(LmHeadArgs A) {
+__global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
   constexpr int kGemmBK = BK;
   constexpr int kGemmRow = BK + 8;  // bf16 per padded LDS row
   constexpr int TPR = BK / 8;       // threads per row in the global -> LDS copy
