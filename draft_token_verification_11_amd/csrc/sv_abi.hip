@@ -670,11 +670,13 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
     return SPEC_ERR_WORKSPACE;
   const int64_t M = int64_t(B) * (k + 1);
   // Up to 64 rows: 256-entry tiles, fragments loaded straight from memory,
-  // 16, 32 or 64 rows per chunk.  More rows: the LDS-staged tiling of
-  // 128 x 128 tiles, two workgroups per CU.
-  const bool gemm = M > 64;
+  // 16, 32 or 64 rows per chunk.  More rows: the LDS-staged tiling, two
+  // workgroups per CU, 128 x 128 tiles in 64-wide stages up to 128 rows,
+  // 128 x 256 tiles in 32-wide stages beyond (fewer LDS reads per product;
+  // measured best of 128 x 128, 256 x 128 and 128 x 256 at 72 to 864 rows).
+  const bool gemm = M > 64, wide = M > 128;
   const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  const int64_t tw = gemm ? sv::kGemmBN : kLmTile, mr = gemm ? sv::kGemmBM : 16 * mb;
+  const int64_t tw = gemm ? (wide ? 256 : 128) : kLmTile, mr = gemm ? 128 : 16 * mb;
   const int64_t tiles = (int64_t(V) + tw - 1) / tw;
   const int64_t chunks = (M + mr - 1) / mr;
   const int64_t nblk = tiles * chunks;
@@ -688,7 +690,10 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   auto st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (gemm) {
-    hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<64>), dim3(unsigned(grid)), dim3(256), 0, st, A);
+    if (wide)
+      hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<128, 256, 32>), dim3(unsigned(grid)), dim3(256), 0, st, A);
+    else
+      hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<128, 128, 64>), dim3(unsigned(grid)), dim3(256), 0, st, A);
   } else switch (mb) {
     case 1: hipLaunchKernelGGL((sv::k_lmhead_argmax<1, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;
     case 2: hipLaunchKernelGGL((sv::k_lmhead_argmax<2, 2, 4>), dim3(unsigned(grid)), dim3(256), 0, st, A); break;

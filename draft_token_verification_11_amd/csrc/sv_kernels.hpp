@@ -2842,32 +2842,32 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(LmHeadArgs A) {
 }
 
 // The fused LM head for larger batches, tiled as a matrix product: a
-// 256-thread workgroup computes a 128-row x 128-entry tile, the four waves
-// as 2 x 2 blocks of 64 x 64 (4 x 4 MFMA blocks of 16 x 16 each).  The
-// hidden and head tiles pass through LDS in stages of BK along d, double
+// 256-thread workgroup computes a BM-row x BN-entry tile, the four waves as
+// 2 x 2 blocks of (BM / 2) x (BN / 2), each made of 16 x 16 MFMA blocks.
+// The hidden and head tiles pass through LDS in stages of BK along d, double
 // buffered: the next stage's 16-byte global loads are in flight while the
 // current stage's fragments are read from LDS and multiplied, so every
 // fragment is loaded from memory once per workgroup instead of once per
 // wave.  LDS rows are padded by 16 bytes so that the 16 rows a fragment
 // read touches fall on different banks.  With one stage in flight per
 // workgroup the kernel is bound by memory latency, so it is built for two
-// workgroups per CU (64-wide stages: 75 KiB of LDS and at most 256
-// registers per lane each), whose stages overlap.
-constexpr int kGemmBM = 128, kGemmBN = 128;
-
-template <int BK>
+// workgroups per CU (at most 80 KiB of LDS and 256 registers per lane
+// each), whose stages overlap.
+template <int BM, int BN, int BK>
 __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
-  constexpr int kGemmBK = BK;
-  constexpr int kGemmRow = BK + 8;  // bf16 per padded LDS row
-  constexpr int TPR = BK / 8;       // threads per row in the global -> LDS copy
-  constexpr int RPP = 256 / TPR;    // rows per pass
-  constexpr int NP = kGemmBM / RPP; // passes
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kGemmBM * kGemmRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kGemmBN * kGemmRow];
-  __shared__ uint64_t best_s[2][kGemmBM];
-  __shared__ uint32_t bad_s[2][kGemmBM];
+  constexpr int WM = BM / 2, WN = BN / 2;       // this wave's block
+  constexpr int MBk = WM / 16, NBk = WN / 16;   // its MFMA blocks
+  constexpr int kRow = BK + 8;                  // bf16 per padded LDS row
+  constexpr int TPR = BK / 8;                   // threads per row in the global -> LDS copy
+  constexpr int RPP = 256 / TPR;                // rows per pass
+  constexpr int NPA = BM / RPP, NPB = BN / RPP;  // passes
+  static_assert(NPA * RPP == BM && NPB * RPP == BN, "tile rows must fill whole passes");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kRow];
+  __shared__ uint64_t best_s[2][BM];
+  __shared__ uint32_t bad_s[2][BM];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;  // this wave's 64 x 64 block
+  const int wm = w >> 1, wn = w & 1;
   // XCD-aware order: the workgroups of one XCD take a contiguous range of
   // (tile, chunk) pairs, chunks fastest, so a head tile is reused from L2
   const int64_t nblk = (int64_t)A.n_tiles * A.m_chunks;
@@ -2875,70 +2875,75 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
   const int64_t pidx = (int64_t)(blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (pidx >= nblk) return;
   const int64_t tile = pidx / A.m_chunks, chunk = pidx - tile * A.m_chunks;
-  const int64_t n0 = tile * kGemmBN, m0 = chunk * kGemmBM;
+  const int64_t n0 = tile * BN, m0 = chunk * BM;
 
   // global -> LDS copy: thread t moves 16-byte column (t % TPR) of rows
-  // (t / TPR) + RPP i, i < NP, of both tiles (rows past M or V read row 0:
-  // their results are discarded)
+  // (t / TPR) + RPP i of both tiles (rows past M or V read row 0: their
+  // results are discarded)
   const int cc = tid % TPR, r0 = tid / TPR;
-  const uint16_t* ag[NP];
-  const uint16_t* bg[NP];
+  const uint16_t* ag[NPA];
+  const uint16_t* bg[NPB];
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
+  for (int i = 0; i < NPA; ++i) {
     int64_t m = m0 + r0 + RPP * i;
     if (m >= A.M) m = 0;
     const int64_t b = m / A.k1, j = m - b * A.k1;
     ag[i] = A.hidden + b * A.h_seq + j * A.h_pos + 8 * cc;
+  }
+#pragma unroll
+  for (int i = 0; i < NPB; ++i) {
     int64_t v = n0 + r0 + RPP * i;
     if (v >= A.V) v = 0;
     bg[i] = A.weight + v * A.w_stride + 8 * cc;
   }
-  auto load_stage = [&](int c, uint4 (&ra)[NP], uint4 (&rb)[NP]) {
+  auto load_stage = [&](int c, uint4 (&ra)[NPA], uint4 (&rb)[NPB]) {
     const bool in = c + 8 * cc < A.d;  // d is a multiple of 32: whole 16-byte columns
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
+    for (int i = 0; i < NPA; ++i)
       ra[i] = in ? *reinterpret_cast<const uint4*>(ag[i] + c) : make_uint4(0u, 0u, 0u, 0u);
-      rb[i] = in ? *reinterpret_cast<const uint4*>(bg[i] + c) : make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_stage = [&](int buf, const uint4 (&ra)[NP], const uint4 (&rb)[NP]) {
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      *reinterpret_cast<uint4*>(&As[buf][(r0 + RPP * i) * kGemmRow + 8 * cc]) = ra[i];
-      *reinterpret_cast<uint4*>(&Bs[buf][(r0 + RPP * i) * kGemmRow + 8 * cc]) = rb[i];
-    }
+    for (int i = 0; i < NPB; ++i)
+      rb[i] = in ? *reinterpret_cast<const uint4*>(bg[i] + c) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto store_stage = [&](int buf, const uint4 (&ra)[NPA], const uint4 (&rb)[NPB]) {
+#pragma unroll
+    for (int i = 0; i < NPA; ++i)
+      *reinterpret_cast<uint4*>(&As[buf][(r0 + RPP * i) * kRow + 8 * cc]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < NPB; ++i)
+      *reinterpret_cast<uint4*>(&Bs[buf][(r0 + RPP * i) * kRow + 8 * cc]) = rb[i];
   };
 
-  sv_f32x4 acc[4][4];
+  sv_f32x4 acc[MBk][NBk];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MBk; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = sv_f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NBk; ++nb) acc[mb][nb] = sv_f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  uint4 ra[NP], rb[NP];
+  uint4 ra[NPA], rb[NPB];
   load_stage(0, ra, rb);
   store_stage(0, ra, rb);
   __syncthreads();
   int buf = 0;
-  for (int c = 0; c < A.d; c += kGemmBK) {
-    const bool more = c + kGemmBK < A.d;
-    if (more) load_stage(c + kGemmBK, ra, rb);  // in flight during this stage's MFMAs
+  for (int c = 0; c < A.d; c += BK) {
+    const bool more = c + BK < A.d;
+    if (more) load_stage(c + BK, ra, rb);  // in flight during this stage's MFMAs
 #pragma unroll
-    for (int ks = 0; ks < kGemmBK; ks += 32) {
-      sv_bf16x8 af[4], bfr[4];
+    for (int ks = 0; ks < BK; ks += 32) {
+      sv_bf16x8 af[MBk], bfr[NBk];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MBk; ++mb)
         af[mb] = __builtin_bit_cast(sv_bf16x8, *reinterpret_cast<const uint4*>(
-                     &As[buf][(wm * 64 + 16 * mb + r16) * kGemmRow + ks + kq]));
+                     &As[buf][(wm * WM + 16 * mb + r16) * kRow + ks + kq]));
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < NBk; ++nb)
         bfr[nb] = __builtin_bit_cast(sv_bf16x8, *reinterpret_cast<const uint4*>(
-                      &Bs[buf][(wn * 64 + 16 * nb + r16) * kGemmRow + ks + kq]));
+                      &Bs[buf][(wn * WN + 16 * nb + r16) * kRow + ks + kq]));
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MBk; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NBk; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
     }
     if (more) {
@@ -2953,14 +2958,14 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
   // waves sharing those rows; one atomic per (row, tile)
   const int rq = (lane >> 4) * 4;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < MBk; ++mb) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       uint64_t best = 0;
       uint32_t bad = 0;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int64_t v = n0 + wn * 64 + 16 * nb + r16;
+      for (int nb = 0; nb < NBk; ++nb) {
+        const int64_t v = n0 + wn * WN + 16 * nb + r16;
         const float x = acc[mb][nb][r];
         if (v < A.V) {
           if (bad_logit(x)) {
@@ -2980,17 +2985,17 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
         bad |= (uint32_t)__shfl_xor((int)bad, off, 16);
       }
       if (r16 == 0) {
-        best_s[wn][wm * 64 + 16 * mb + rq + r] = best;
-        bad_s[wn][wm * 64 + 16 * mb + rq + r] = bad;
+        best_s[wn][wm * WM + 16 * mb + rq + r] = best;
+        bad_s[wn][wm * WM + 16 * mb + rq + r] = bad;
       }
     }
   }
   __syncthreads();
-  if (tid < kGemmBM) {
-    const int64_t m = m0 + tid;
+  for (int i = tid; i < BM; i += 256) {
+    const int64_t m = m0 + i;
     if (m < A.M) {
-      const uint64_t best = best_s[0][tid] > best_s[1][tid] ? best_s[0][tid] : best_s[1][tid];
-      const uint32_t bad = bad_s[0][tid] | bad_s[1][tid];
+      const uint64_t best = best_s[0][i] > best_s[1][i] ? best_s[0][i] : best_s[1][i];
+      const uint32_t bad = bad_s[0][i] | bad_s[1][i];
       if (best) __hip_atomic_fetch_max(A.best + m, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (bad) atomicOr(A.bad + m, 1u);
     }
