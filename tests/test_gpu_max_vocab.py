@@ -1,0 +1,98 @@
+"""Parity at the largest vocabulary the library accepts (V = 2^24): one
+sequence, k = 2, logits ~ N(0, 2) with the draft a noisy copy of the target.
+Rows this long take the row pass, the histogram filter (bf16) or the
+bisection filter (fp32), and the correction draw split over 2,048 chunks.
+
+At this size single-token probabilities (~1e-7) lie below the oracle's 1e-6
+boundary margin, so the oracle flags most draws (and every top-p cut) as
+near a boundary.  The accept/reject decisions are still compared exactly
+where they are not near one; the emitted token of a draw-flagged sequence
+must lie where the oracle's cumulative distribution (residual max(0, p - q)
+at a rejection, p after every acceptance) passes u S, within 1e-6 of S on
+either side.  Greedy is compared exactly."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_11_amd as sv
+import oracle
+import workloads
+from tests.gpu_common import DEV, compare_stochastic, gpu_stochastic, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+V = 1 << 24
+B, K = 1, 2
+ORC_NEAR_ACCEPT, ORC_NEAR_SAMPLE, ORC_NEAR_TOPP = 1, 2, 4
+
+
+@pytest.fixture(scope="module")
+def rows():
+    rs = np.random.default_rng(2024)
+    t = rs.normal(0, 2, (B, K + 1, V)).astype(np.float32)
+    d = (t[:, :K] + rs.normal(0, 0.7, (B, K, V))).astype(np.float32)
+    return t, d
+
+
+@pytest.mark.parametrize("dtype,T,top_k,top_p,reject", [("bf16", 1.0, 0, 1.0, False),
+                                                        ("f32", 0.8, 50, 1.0, False),
+                                                        ("bf16", 1.0, 0, 0.95, False),
+                                                        ("bf16", 1.0, 0, 1.0, True)])
+def test_max_vocabulary_stochastic(rows, dtype, T, top_k, top_p, reject):
+    rs = np.random.default_rng(top_k + int(100 * top_p))
+    t, d = rows
+    if dtype == "bf16":
+        t, d = workloads.to_bf16_bits(t), workloads.to_bf16_bits(d)
+    toks = oracle.sample_drafts(d, rs.random((B, K)), T, top_k, top_p)
+    u = rs.random((B, K + 1)).astype(np.float32)
+    if reject:
+        # position 0 drafts the token the draft favours most over the target
+        # and draws u near 1: a rejection there, so the correction draw runs
+        # over the whole residual of two 2^24 rows
+        tf, df = workloads.bf16_bits_to_f32(t[0, 0]), workloads.bf16_bits_to_f32(d[0, 0])
+        toks[0, 0] = int(np.argmax(df - tf))
+        u[0, 0] = 0.999
+    ref = oracle.verify_stochastic(t, d, toks, u, T, top_k, top_p)
+    acc, out, ap = gpu_stochastic(t, d, toks, u, T, top_k, top_p)
+    label = "V=2^24 %s T=%g k=%d p=%g%s" % (dtype, T, top_k, top_p, " reject" if reject else "")
+    compare_stochastic(ref, acc, out, ap, fp32=(dtype == "f32"), label=label)
+    flags, n = int(ref["flags"][0]), int(acc[0])
+    if flags & ORC_NEAR_ACCEPT == 0 and flags & ORC_NEAR_TOPP == 0:
+        # only the draw is near a boundary: the decisions match exactly
+        assert n == int(ref["accepted_len"][0]), label
+        assert np.array_equal(out[0, :n], ref["out_tokens"][0, :n]), label
+        assert (out[0, n + 1:] == -1).all(), label
+        x = int(out[0, n])
+        assert 0 <= x < V, label
+        _, p, _ = oracle.process_row(t[0, n], T, top_k, top_p)
+        r = p
+        if n < K:
+            _, q, _ = oracle.process_row(d[0, n], T, top_k, top_p)
+            r = np.maximum(p - q, 0.0)
+            if not r.sum() > 0.0:
+                r = p
+        assert p[x] > 0.0, label  # inside p's support
+        c = np.cumsum(r)
+        S, target = c[-1], float(u[0, K]) * c[-1]
+        before = c[x - 1] if x > 0 else 0.0
+        assert before <= target + 1e-6 * S and c[x] >= target - 1e-6 * S, (label, before, c[x], target)
+    if reject:
+        assert int(ref["accepted_len"][0]) == 0 and n == 0, label
+    note("%s: n=%d oracle n=%d flags=%d" % (label, n, int(ref["accepted_len"][0]), flags))
+
+
+def test_max_vocabulary_greedy(rows):
+    t, _ = rows
+    tb = workloads.to_bf16_bits(t)
+    tgt = to_dev(tb)
+    am = np.array([[oracle.argmax_row(tb[0, j]) for j in range(K + 1)]], np.int32)
+    for toks in (am[:, :K].copy(), np.array([[am[0, 0], (am[0, 1] + 1) % V]], np.int32)):
+        acc, out = sv.verify_greedy(tgt, torch.from_numpy(toks).to(DEV))
+        torch.cuda.synchronize()
+        racc, rout = oracle.verify_greedy(tb, toks)
+        assert np.array_equal(acc.cpu().numpy(), racc)
+        assert np.array_equal(out.cpu().numpy(), rout)
+    # the last call rejected position 1: its output is the argmax there
+    assert int(racc[0]) == 1 and int(rout[0, 1]) == int(am[0, 1])
