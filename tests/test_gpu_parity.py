@@ -403,3 +403,37 @@ def test_determinism_and_clean_workspace():
     sv.logits_process(args[1].reshape(-1, c.V), workspace=wsp)
     torch.cuda.synchronize()
     assert int(wsg.count_nonzero()) == 0 and int(wsp.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("V", [300, 5000])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_max_k_row_pass(V, dtype):
+    """k = 64 (the largest) on the small-batch row pass: the draft a close copy
+    of the target so that accepted runs reach deep positions and the bonus."""
+    rs = np.random.default_rng(64 + V)
+    B, k = 5, 64
+    for T, top_k, top_p in [(1.0, 0, 1.0), (1.0, 20, 0.9)]:
+        t = rs.normal(0, 2.0, (B, k + 1, V)).astype(np.float32)
+        d = (t[:, :k] + rs.normal(0, 0.02, (B, k, V))).astype(np.float32)
+        if dtype == "bf16":
+            t, d = workloads.to_bf16_bits(t), workloads.to_bf16_bits(d)
+        toks = oracle.sample_drafts(d, rs.random((B, k)), T, top_k, top_p)
+        u = rs.random((B, k + 1)).astype(np.float32)
+        acc, out, ap = gpu_stochastic(t, d, toks, u, T, top_k, top_p)
+        ref = oracle.verify_stochastic(t, d, toks, u, T, top_k, top_p)
+        compare_stochastic(ref, acc, out, ap, fp32=(dtype == "f32"),
+                           label="k=64 V=%d %s T=%g k=%d p=%g" % (V, dtype, T, top_k, top_p))
+        assert ref["accepted_len"].max() >= 32
+    # greedy at k = 64: every draft the target's argmax, then one miss at 40
+    am = oracle.argmax_drafts(t)
+    full = am[:, :k].astype(np.int32)
+    miss = full.copy()
+    miss[1:, 40] = (am[1:, 40] + 1) % V
+    tgt = to_dev(t)
+    for tk in (full, miss):
+        g_acc, g_out = sv.verify_greedy(tgt, torch.from_numpy(tk).to(DEV))
+        torch.cuda.synchronize()
+        racc, rout = oracle.verify_greedy(t, tk)
+        assert np.array_equal(g_acc.cpu().numpy(), racc)
+        assert np.array_equal(g_out.cpu().numpy(), rout)
+    assert (racc[1:] == 40).all() and racc[0] == k
