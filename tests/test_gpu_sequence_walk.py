@@ -143,3 +143,23 @@ def test_walk_queue_and_workspace():
         assert torch.equal(a, b)
     assert torch.equal(r1[0], r3[0]) and torch.equal(r1[1], r3[1])
     assert int((r1[0] >= 0).sum()) == B
+
+
+def test_walk_threshold_both_sides():
+    """Two sequences per CU less one takes the row pass, exactly two per CU the
+    position-task kernel: the same sequences, the oracle's results on both
+    sides wherever its decisions are clear."""
+    rs = np.random.default_rng(59)
+    B, k, V = 2 * torch.cuda.get_device_properties(0).multi_processor_count, 3, 1000
+    for T, top_k, top_p in [(1.0, 0, 0.95), (0.8, 20, 1.0)]:
+        t, d, toks, u = _case(rs, B, k, V, T, top_k, top_p)
+        ref = oracle.verify_stochastic(t, d, toks, u, T, top_k, top_p)
+        ok = ref["flags"] == 0
+        a_walk, o_walk = _walk_only(t, d, toks, u, T, top_k, top_p)
+        a_rows, o_rows = _walk_only(t[: B - 1], d[: B - 1], toks[: B - 1], u[: B - 1], T, top_k, top_p)
+        assert np.array_equal(a_walk[ok], ref["accepted_len"][ok])
+        assert np.array_equal(o_walk[ok], ref["out_tokens"][ok])
+        okr = ok[: B - 1]
+        assert np.array_equal(a_rows[okr], ref["accepted_len"][: B - 1][okr])
+        assert np.array_equal(o_rows[okr], ref["out_tokens"][: B - 1][okr])
+        note("threshold B=%d/%d T=%g k=%d p=%g: %d flagged" % (B - 1, B, T, top_k, top_p, int((~ok).sum())))
