@@ -133,3 +133,17 @@ def test_lmhead_k_tail(d):
     best = np.argmax(L, axis=1).reshape(B, k + 1)
     acc, out, racc, near = _check(h, w, _tokens(rs, best, V, 0.0), "lmhead d=%d" % d)
     assert (acc[~near.any(axis=1)] == k).all()
+
+
+@pytest.mark.parametrize("B,k", [(1, 1), (9, 7)])
+def test_lmhead_largest_hidden_size(B, k):
+    """d = 65536, the largest hidden size accepted: 2 rows on the direct-load
+    kernel, 72 rows on the LDS-staged tiling; every consulted row compared
+    away from near ties (their bound grows with d)."""
+    rs = np.random.default_rng(65536 + B)
+    d, V = 65536, 300
+    h, w, vs = workloads.lmhead(B, k, d, V, seed=B, boost=0.5)
+    L, _ = oracle.lmhead_logits(h, w)
+    best = np.argmax(L, axis=1).reshape(B, k + 1)
+    acc, out, racc, near = _check(h, w, _tokens(rs, best, V, 0.2), "lmhead d=65536 B=%d k=%d" % (B, k))
+    assert (~near).any()
