@@ -70,6 +70,29 @@ def test_apply_bit_exact(din, dout, V):
                           np.nan_to_num(ref.astype(np.float64), nan=7.0))
 
 
+
+@pytest.mark.parametrize("din,dout", [("bf16", "bf16"), ("f32", "f32")])
+def test_apply_largest_row_count_ragged_chunks(din, dout):
+    """129 rows per sequence (2 k + 1 at k = 64, the largest) over a
+    vocabulary of three 8192-element chunks plus 5; per-row and broadcast
+    masks with the penalty."""
+    rs = np.random.default_rng(129)
+    S, rows, V = 3, 129, 3 * 8192 + 5
+    x = rs.normal(0, 3, (S, rows, V)).astype(np.float32)
+    xin = workloads.to_bf16_bits(x) if din == "bf16" else x
+    allow, pen = _masks(rs, S, rows, V)
+    for a in (allow, allow[:, :1]):
+        ref = oracle.apply_processors(xin, a, pen, 1.2, "bf16" if dout == "bf16" else None)
+        got = sv.logits_apply(to_dev(xin), allow=_t(a), penalize=_t(pen), theta=1.2,
+                              out_dtype=torch.bfloat16 if dout == "bf16" else torch.float32)
+        torch.cuda.synchronize()
+        g = _back(got)
+        if dout == "bf16":
+            assert np.array_equal(g, ref)
+        else:
+            assert np.array_equal(g.view(np.uint32), ref.view(np.uint32))
+
+
 def _processed_case(rs, B, k, V, dtype, T, top_k, top_p, theta):
     t = rs.normal(0, 2.0, (B, k + 1, V)).astype(np.float32)
     d = (t[:, :k] + rs.normal(0, 0.7, (B, k, V))).astype(np.float32)
