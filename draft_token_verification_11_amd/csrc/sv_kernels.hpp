@@ -1594,6 +1594,22 @@ __device__ __forceinline__ void hist_count_stream(uint32_t* hist, const uint16_t
 #pragma unroll
     for (int d = 0; d < D; ++d) hist_add8(hist, v[d]);
   }
+  // Fewer than D full vectors per thread remain.  Two or more are loaded
+  // together (one at a time, each would wait a full memory latency: at
+  // V = 128,256 five or six per thread); a single one, and the partial
+  // group, one at a time.
+  if (g + NT < nfull) {
+    uint4 v[D - 1];
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d) {
+      const uint32_t gd = g + (uint32_t)d * NT;
+      v[d] = gd < nfull ? rsrc_load16(rs, gd * 16u, 0u) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+      if (g + (uint32_t)d * NT < nfull) hist_add8(hist, v[d]);
+    g += (nfull - g + NT - 1) / NT * NT;  // the first of this thread's groups past the full ones
+  }
   for (; g < ngroups; g += NT) {
     if (g < nfull) {
       hist_add8(hist, rsrc_load16(rs, g * 16u, 0u));
