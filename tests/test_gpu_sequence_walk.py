@@ -163,3 +163,20 @@ def test_walk_threshold_both_sides():
         assert np.array_equal(a_rows[okr], ref["accepted_len"][: B - 1][okr])
         assert np.array_equal(o_rows[okr], ref["out_tokens"][: B - 1][okr])
         note("threshold B=%d/%d T=%g k=%d p=%g: %d flagged" % (B - 1, B, T, top_k, top_p, int((~ok).sum())))
+
+
+@pytest.mark.parametrize("V", [40000, 40003])
+def test_walk_count_tail_vectors(V):
+    """Vocabularies whose rows leave each thread two or three full 16-byte
+    vectors after the prefetched ones (loaded together at the end of the
+    count), plus a partial group at V = 40003, on the position-task kernel."""
+    from tests.test_gpu_parity import oracle_stochastic
+    rs = np.random.default_rng(V)
+    B, k = 2 * torch.cuda.get_device_properties(0).multi_processor_count, 2
+    t, d, toks, u = _case(rs, B, k, V, 1.0, 0, 0.95)
+    ref = oracle_stochastic(t, d, toks, u, 1.0, 0, 0.95)
+    ok = ref["flags"] == 0
+    acc, out = _walk_only(t, d, toks, u, 1.0, 0, 0.95)
+    assert np.array_equal(acc[ok], ref["accepted_len"][ok])
+    assert np.array_equal(out[ok], ref["out_tokens"][ok])
+    note("count tail V=%d: %d sequences, %d flagged" % (V, B, int((~ok).sum())))
