@@ -406,6 +406,98 @@ def pin_boundary_flags(orc):
 
 
 # ---------------------------------------------------------------------------
+def cut_masses(l: np.ndarray, T: float, top_k: int, top_p: float):
+    """Brute force of the top-p cut over distinct values (numpy): with pi the
+    probabilities renormalised over the top-k set, M(v) = sum of pi over
+    logits >= v.  The cut is the largest distinct value v with M(v) >= top_p
+    (the shortest descending prefix that reaches top_p, ties kept; the lowest
+    value if rounding leaves none).  Returns (mass strictly above the cut, mass
+    at or above it)."""
+    l = l.astype(np.float64)
+    keep = np.ones(l.size, bool)
+    if 0 < top_k < l.size:
+        keep &= l >= np.sort(l)[::-1][top_k - 1]
+    kept = l[keep]
+    w = np.exp((kept - kept.max()) / T)
+    w /= w.sum()
+    vals = np.unique(kept)[::-1]  # distinct values, descending
+    M = np.array([w[kept >= v].sum() for v in vals])
+    reach = np.nonzero(M >= top_p)[0]
+    i = int(reach[0]) if reach.size else vals.size - 1
+    above = float(M[i - 1]) if i > 0 else 0.0
+    return above, float(M[i])
+
+
+def _near_cut(above, at, top_p):
+    return abs(above - top_p) <= 1e-6 or abs(at - top_p) <= 1e-6
+
+
+def pin_topp_boundary_flag(orc):
+    """Flag bit 2 (a top-p cut mass within 1e-6 of top_p): the oracle's masses
+    strictly above and at its cut equal the distinct-value brute force, and
+    the flag of a sequence whose rows are all the given row is set exactly
+    when one of those masses lies within 1e-6 of top_p.  Random rows (mostly
+    far from a boundary), rows whose top_p is placed at a cumulative boundary
+    plus an offset from -5e-6 to 5e-6, rows with ties at the cut, and top-k
+    followed by top-p."""
+    rs = np.random.default_rng(97)
+    cases = []
+    for trial in range(30):  # random rows
+        V = int(rs.integers(3, 300))
+        l = rs.normal(0, rs.choice([0.5, 1.0, 3.0]), V).astype(np.float32)
+        cases.append((l, float(rs.choice([0.7, 1.0, 1.5])), int(rs.choice([0, 0, 5, 40])),
+                      float(rs.uniform(0.3, 0.99))))
+    for trial in range(36):  # top_p at a cumulative boundary plus an offset
+        V = int(rs.integers(4, 200))
+        l = rs.normal(0, 1.5, V).astype(np.float32)
+        if trial % 3 == 0:
+            l = np.round(l * 4) / 4  # ties at the cut
+        T = float(rs.choice([0.8, 1.0]))
+        top_k = int(rs.choice([0, 0, 10]))
+        kept = l.astype(np.float64)
+        if 0 < top_k < V:
+            kept = kept[kept >= np.sort(kept)[::-1][top_k - 1]]
+        w = np.exp((kept - kept.max()) / T)
+        w /= w.sum()
+        vals = np.unique(kept)[::-1]
+        M = np.array([w[kept >= v].sum() for v in vals])
+        inner = M[(M > 0.05) & (M < 0.95)]
+        if inner.size == 0:
+            continue
+        off = [-5e-6, -1.5e-6, -8e-7, -3e-7, 0.0, 3e-7, 8e-7, 1.5e-6, 5e-6][trial % 9]
+        cases.append((l, T, top_k, float(rs.choice(inner)) + off))
+    n_near = n_far = 0
+    for l, T, top_k, top_p in cases:
+        above, at = cut_masses(l, T, top_k, top_p)
+        d = min(abs(above - top_p), abs(at - top_p))
+        if abs(d - 1e-6) < 1e-10:
+            continue  # rounding could decide either way right at the bound
+        ok, _, st = orc.process_row(l, T, top_k, top_p)
+        assert ok
+        if abs(at - top_p) > 1e-12:  # else either cut is right to the last bit (both near)
+            assert abs(st["mass_above_cut"] - above) < 1e-12, (st, above, at, top_p)
+            assert abs(st["mass_at_cut"] - at) < 1e-12, (st, above, at, top_p)
+        # k = 1, every row the same row: q = p, so the draft is accepted and
+        # the target rows 0 and 1 and the draft row 0 are all consulted
+        tb = np.broadcast_to(l, (1, 2, l.size))
+        db = np.broadcast_to(l, (1, 1, l.size))
+        tok = int(np.argmax(l))
+        r = orc.verify_stochastic(tb, db, np.array([[tok]], np.int32),
+                                  np.array([[0.5, 0.5]], np.float32), T, top_k, top_p)
+        assert r["accepted_len"][0] == 1
+        near = _near_cut(above, at, top_p)
+        assert bool(r["flags"][0] & 4) == near, (above, at, top_p, r["flags"][0])
+        n_near += near
+        n_far += not near
+    assert n_near >= 15 and n_far >= 35, (n_near, n_far)
+    # top-p off: no cut, no flag
+    l = rs.normal(0, 1, 50).astype(np.float32)
+    r = orc.verify_stochastic(np.broadcast_to(l, (1, 2, 50)), np.broadcast_to(l, (1, 1, 50)),
+                              np.array([[0]], np.int32), np.array([[0.5, 0.5]], np.float32))
+    assert r["flags"][0] & 4 == 0
+
+
+# ---------------------------------------------------------------------------
 def pin_chi_square(orc, n=1_000_000):
     """10^6 draws of the worked example: the emitted first token follows the
     target law (0.6, 0.3, 0.1) (chi-square, p-value >= 1e-3 at a fixed seed)."""
@@ -592,4 +684,4 @@ def pin_lmhead_greedy(orc, greedy=None):
 
 ALL_PINS = [pin_lmhead_greedy, pin_logits_processors, pin_outcome_lookup, pin_pooled_rows, pin_worked_example, pin_law_of_decision_map, pin_softmax_and_filters,
             pin_acceptance_rate, pin_special_cases, pin_greedy, pin_bf16_decode,
-            pin_invalid_inputs, pin_boundary_flags, pin_chi_square]
+            pin_invalid_inputs, pin_boundary_flags, pin_topp_boundary_flag, pin_chi_square]

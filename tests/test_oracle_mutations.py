@@ -35,6 +35,12 @@ MUTATIONS = {
                                               "if (!pres[k].valid) valid = 0;", 1),
     "ill-formed position past the stop invalidates": ("if (isnan(alpha[j])) {\n        valid = 0;\n        break;\n      }\n      if (!((double)ub[j] < alpha[j])) {\n        n = j;\n        break;\n      }",
                                                       "if (isnan(alpha[j])) {\n        valid = 0;\n        break;\n      }\n      if (!((double)ub[j] < alpha[j]) && n == k) {\n        n = j;\n      }", 1),
+    "top-p boundary flag never set": ("f |= ORC_NEAR_TOPP;", "(void)0;", 2),
+    "top-p boundary flag always set": ("flags[b] = f;", "flags[b] = f | (top_p < 1.0 ? ORC_NEAR_TOPP : 0);", 1),
+    "mass above the cut counts its ties": ("if (scratch[j] > t_p) above += pi;",
+                                           "if (scratch[j] >= t_p) above += pi;", 1),
+    "boundary distance 1e-3 instead of 1e-6": ("return fabs(a - b) <= 1e-6;",
+                                               "return fabs(a - b) <= 1e-3;", 1),
 }
 
 FAST_PINS = [p for p in pins.ALL_PINS if p is not pins.pin_chi_square]
