@@ -177,7 +177,12 @@ class Oracle:
                                             _ptr(flags))
         if rc != 0:
             raise MemoryError("oracle allocation failed")
-        return {"accepted_len": acc, "out_tokens": out, "accept_prob": ap, "flags": flags}
+        # the inputs travel with the results, so that a check of a flagged
+        # sequence can recompute its rows under either side of a decision
+        inputs = {"target": target, "draft": draft, "tokens": tokens, "uniforms": uniforms,
+                  "temperature": float(temperature), "top_k": int(top_k), "top_p": float(top_p)}
+        return {"accepted_len": acc, "out_tokens": out, "accept_prob": ap, "flags": flags,
+                "inputs": inputs}
 
     def verify_greedy(self, target, tokens):
         """Greedy verify.  Returns (accepted_len [B], out_tokens [B][k+1])."""
@@ -383,17 +388,31 @@ def lmhead_logits(hidden_bits, weight_bits, rows=None, chunk=16384):
     return L, S
 
 
-def lmhead_greedy(hidden_bits, weight_bits, tokens):
+def lmhead_tie_candidates(L, S, d):
+    """Per row of fp64 logits L (with S the sums of |products|, from
+    lmhead_logits) the tokens whose logit lies within the fp32 summation
+    bound gamma_d (S_top + S_x) of the largest: the argmaxes a kernel that
+    accumulates in fp32 may report.  A list of index arrays, one per row."""
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    best = np.argmax(L, axis=1)
+    top = L[np.arange(len(L)), best]
+    stop = S[np.arange(len(L)), best]
+    return [np.nonzero(L[r] >= top[r] - gamma * (stop[r] + S[r]))[0] for r in range(len(L))]
+
+
+def lmhead_greedy(hidden_bits, weight_bits, tokens, logits=None):
     """Greedy verify on LM-head logits (the encyclopedia entry's greedy rule:
     compare each draft with the target's most probable token, replace the
     first mismatch; lowest index on ties).  Returns (accepted_len [B],
     out_tokens [B][k+1], near_tie [B][k+1]): near_tie marks rows where another
     token's logit lies within the fp32 summation bound gamma_d (|a| + |b|)
     of the largest (gamma_d = d u / (1 - d u), u = 2^-24), so that a kernel
-    accumulating in fp32 may report either."""
+    accumulating in fp32 may report either.  logits: (L, S) of lmhead_logits
+    when already computed."""
     B, k1, d = hidden_bits.shape
     k = k1 - 1
-    L, S = lmhead_logits(hidden_bits, weight_bits)
+    L, S = lmhead_logits(hidden_bits, weight_bits) if logits is None else logits
     u = 2.0 ** -24
     gamma = d * u / (1 - d * u)
     best = np.argmax(L, axis=1)  # first maximum

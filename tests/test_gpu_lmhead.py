@@ -1,8 +1,8 @@
 """Fused LM head + greedy verify on the GPU against the oracle's fp64 logits
 (exact products of the bf16 inputs): every sequence whose consulted rows have
 no near tie (another logit within the fp32 summation bound of the largest)
-must match exactly; at near ties the GPU's token must be one of the tied
-candidates.  Row counts cover the one, two and four 16-row blocks of the
+must match exactly; at near ties every argmax the GPU acted on must be one of
+the tied candidates, and its stop the first draft that differs from it.  Row counts cover the one, two and four 16-row blocks of the
 kernel; vocabularies are ragged against its 256-wide tiles."""
 from __future__ import annotations
 
@@ -30,14 +30,16 @@ def _tokens(rs, best, V, p_random=0.25):
     return toks.astype(np.int32)
 
 
-def _check(h, w, toks, label, hidden=None, weight=None):
+def _check(h, w, toks, label, hidden=None, weight=None, logits=None):
     acc, out = sv.verify_greedy_lmhead(hidden if hidden is not None else _dev_bf16(h),
                                        weight if weight is not None else _dev_bf16(w),
                                        torch.from_numpy(toks).to(DEV))
     torch.cuda.synchronize()
     acc, out = acc.cpu().numpy(), out.cpu().numpy()
-    racc, rout, near = oracle.lmhead_greedy(h, w, toks)
+    L, S = logits if logits is not None else oracle.lmhead_logits(h, w)
+    racc, rout, near = oracle.lmhead_greedy(h, w, toks, logits=(L, S))
     B, k1 = near.shape
+    k, V = k1 - 1, w.shape[0]
     consulted = np.zeros_like(near)
     for b in range(B):
         n = racc[b] if racc[b] >= 0 else k1 - 1
@@ -45,7 +47,28 @@ def _check(h, w, toks, label, hidden=None, weight=None):
     clean = ~(near & consulted).any(axis=1)
     assert np.array_equal(acc[clean], racc[clean]), label
     assert np.array_equal(out[clean], rout[clean]), label
-    note("%s: %d sequences, %d with a near tie where consulted" % (label, B, int((~clean).sum())))
+    # near ties: the GPU's argmax of every row it consulted is one of the
+    # tied candidates, and its stop is the first draft that differs from it
+    cand = None
+    for b in np.nonzero(~clean)[0]:
+        if cand is None:
+            cand = oracle.lmhead_tie_candidates(L, S, h.shape[-1])
+        n = int(acc[b])
+        rows = [b * k1 + j for j in range(k1)]
+        where = "%s: near-tie sequence %d gpu n=%d out=%s" % (label, b, n, list(out[b]))
+        if n < 0:  # an out-of-range draft reached through tied matches
+            j = next((j for j in range(k) if not 0 <= toks[b, j] < V), -1)
+            assert j >= 0, where
+            assert all(toks[b, i] in cand[rows[i]] for i in range(j)), where
+            assert (out[b] == -1).all(), where
+            continue
+        assert all(0 <= toks[b, i] < V and toks[b, i] in cand[rows[i]] for i in range(n)), where
+        assert np.array_equal(out[b, :n], toks[b, :n]) and (out[b, n + 1:] == -1).all(), where
+        assert out[b, n] in cand[rows[n]], where
+        if n < k:
+            assert 0 <= toks[b, n] < V and out[b, n] != toks[b, n], where
+    note("%s: %d sequences, %d with a near tie where consulted (each checked against its "
+         "tied candidates)" % (label, B, int((~clean).sum())))
     return acc, out, racc, near
 
 
@@ -83,10 +106,10 @@ def test_lmhead_full_size_greedy_shape():
     rs = np.random.default_rng(8)
     for B in (1, 48):
         h, w, vs = workloads.lmhead(B, 8, 4096, 151936, seed=3, boost=0.3)
-        L, _ = oracle.lmhead_logits(h, w)
+        L, S = oracle.lmhead_logits(h, w)
         best = np.argmax(L, axis=1).reshape(B, 9)
-        _check(h, w, _tokens(rs, best, 151936, 0.15), "lmhead full size B=%d" % B)
-        del L
+        _check(h, w, _tokens(rs, best, 151936, 0.15), "lmhead full size B=%d" % B, logits=(L, S))
+        del L, S
 
 
 def test_lmhead_matches_unfused_gpu_path():

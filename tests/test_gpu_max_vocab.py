@@ -57,7 +57,10 @@ def test_max_vocabulary_stochastic(rows, dtype, T, top_k, top_p, reject):
     ref = oracle.verify_stochastic(t, d, toks, u, T, top_k, top_p)
     acc, out, ap = gpu_stochastic(t, d, toks, u, T, top_k, top_p)
     label = "V=2^24 %s T=%g k=%d p=%g%s" % (dtype, T, top_k, top_p, " reject" if reject else "")
-    compare_stochastic(ref, acc, out, ap, fp32=(dtype == "f32"), label=label)
+    # one sequence whose draws sit among breakpoints ~1e-7 apart: flagged
+    # as a rule, so the bound is the whole batch (its result is checked
+    # admissible instead)
+    compare_stochastic(ref, acc, out, ap, fp32=(dtype == "f32"), label=label, max_flag_frac=1.0)
     flags, n = int(ref["flags"][0]), int(acc[0])
     if flags & ORC_NEAR_ACCEPT == 0 and flags & ORC_NEAR_TOPP == 0:
         # only the draw is near a boundary: the decisions match exactly

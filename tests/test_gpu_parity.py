@@ -38,7 +38,11 @@ def oracle_stochastic(target, draft, tokens, u, T, top_k, top_p, threads=8):
     for t in ths:
         t.join()
     parts = [p for p in parts if p is not None]
-    return {k: np.concatenate([p[k] for p in parts]) for k in parts[0]}
+    ref = {k: np.concatenate([p[k] for p in parts]) for k in parts[0] if k != "inputs"}
+    ref["inputs"] = {"target": target, "draft": draft, "tokens": np.asarray(tokens, np.int32),
+                     "uniforms": np.asarray(u, np.float32), "temperature": float(T),
+                     "top_k": int(top_k), "top_p": float(top_p)}
+    return ref
 
 
 def draft_tokens_from_oracle(w, threads=8):
@@ -126,38 +130,51 @@ def test_config3_parity_full():
     compare_stochastic(ref, acc, out, ap, fp32=False, label="c3 full (B=64)")
 
 
-def _sampled_full_size(cfg, n_check, label):
+def full_size_case(cfg, threads=16):
+    """Every sequence of a workload at its full size, drafts drawn by the
+    oracle's sampler from the processed q (the proposer's own draw), and the
+    oracle's results for all of them."""
     c = workloads.CONFIGS[cfg]
-    w = workloads.generate(cfg, threads=16)
-    note("%s: inputs generated" % label)
-    rs = np.random.default_rng(cfg)
-    check = np.sort(rs.choice(c.B, size=n_check, replace=False))
-    toks = rs.integers(0, c.V, size=(c.B, c.k)).astype(np.int32)
-    sub = workloads.generate(cfg, seqs=check)
-    toks[check] = draft_tokens_from_oracle(sub)
+    w = workloads.generate(cfg, threads=threads)
+    note("c%d: inputs generated" % cfg)
+    toks = draft_tokens_from_oracle(w, threads)
+    note("c%d: drafts sampled" % cfg)
+    ref = oracle_stochastic(w.target, w.draft, toks, w.uniforms, c.temperature, c.top_k, c.top_p,
+                            threads)
+    note("c%d: oracle done" % cfg)
+    return w, toks, ref
+
+
+def test_config4_parity_full_size():
+    """Workload 4 at full size (256 x 8 positions, V = 262144, fp32): every
+    sequence against the oracle."""
+    w, toks, ref = full_size_case(4)
+    c = w.config
     acc, out, ap = gpu_stochastic(w.target, w.draft, toks, w.uniforms, c.temperature, c.top_k,
                                   c.top_p)
-    note("%s: gpu done" % label)
-    # invariants on every sequence
-    k = c.k
-    assert ((acc >= 0) & (acc <= k)).all()
-    for b in range(c.B):
-        n = acc[b]
-        assert np.array_equal(out[b, :n], toks[b, :n])
-        assert 0 <= out[b, n] < c.V
-        assert (out[b, n + 1:] == -1).all()
-    ref = oracle_stochastic(sub.target, sub.draft, toks[check], sub.uniforms, c.temperature,
-                            c.top_k, c.top_p)
-    return compare_stochastic(ref, acc, out, ap, rows=check, fp32=(c.dtype == "f32"),
-                              label=label)
+    compare_stochastic(ref, acc, out, ap, fp32=True, label="c4 full size (B=256), all checked")
 
 
-def test_config4_parity_full_size_sampled():
-    _sampled_full_size(4, 12, "c4 full size (B=256), 12 checked")
-
-
-def test_config5_parity_full_size_sampled():
-    _sampled_full_size(5, 12, "c5 full size (B=512), 12 checked")
+def test_config5_parity_full_size():
+    """Workload 5 at full size (512 branch sequences x 4 positions,
+    V = 151936, bf16, top-p 0.95): every sequence against the oracle, on the
+    position-task kernel (the benchmarked call: no alpha) and on the
+    whole-sequence walk (alpha requested)."""
+    w, toks, ref = full_size_case(5)
+    c = w.config
+    tt, dd = to_dev(w.target), to_dev(w.draft)
+    tk, uu = torch.from_numpy(toks).to(DEV), torch.from_numpy(w.uniforms).to(DEV)
+    assert sv.verify_stochastic_path(tt, dd, top_p=c.top_p) == sv.SPEC_PATH_TASK_QUEUE
+    acc, out = sv.verify_stochastic(tt, dd, tk, uu, temperature=c.temperature, top_k=c.top_k,
+                                    top_p=c.top_p)
+    torch.cuda.synchronize()
+    compare_stochastic(ref, acc.cpu().numpy(), out.cpu().numpy(), None, fp32=False,
+                       label="c5 full size (B=512) task queue, all checked")
+    assert sv.verify_stochastic_path(tt, dd, top_p=c.top_p, return_accept_prob=True) == \
+        sv.SPEC_PATH_SEQUENCE_WALK
+    acc2, out2, ap2 = gpu_stochastic(tt, dd, toks, w.uniforms, c.temperature, c.top_k, c.top_p)
+    compare_stochastic(ref, acc2, out2, ap2, fp32=False,
+                       label="c5 full size (B=512) walk with alpha, all checked")
 
 
 # ---------------------------------------------------------------------------

@@ -44,7 +44,9 @@ def _check(tp, tm, dp, dm, toks, u, T, top_k, top_p, label):
     fp32 = tp.dtype == np.float32
     ref = oracle.verify_stochastic_pooled(tp, tm, dp, dm, toks, u, T, top_k, top_p)
     acc, out, ap = _gpu_pooled(tp, tm, dp, dm, toks, u, T, top_k, top_p)
-    compare_stochastic(ref, acc, out, ap, fp32=fp32, label=label)
+    # pooled rows are shared: a target row whose top-p cut lies near top_p
+    # flags every branch (up to 16) that reads it, so flags come in groups
+    compare_stochastic(ref, acc, out, ap, fp32=fp32, label=label, max_flag_frac=0.4)
     acc2, out2 = _gpu_pooled(tp, tm, dp, dm, toks, u, T, top_k, top_p, alpha=False)
     assert np.array_equal(acc, acc2) and np.array_equal(out, out2), label
     return ref, acc, out, ap
@@ -254,19 +256,14 @@ def test_pooled_workspace_left_zero(path):
     assert int(wsg.count_nonzero()) == 0
 
 
-def test_config5_pooled_full_size_sampled():
+def test_config5_pooled_full_size():
     """The branch fan-out workload (32 requests x 16 branches, k = 4,
     V = 151936, bf16, top-p 0.95) with each request's target rows held once:
-    160 target rows instead of 10240.  Every sequence equals the dense call
-    on the materialised rows; 12 sampled sequences equal the oracle."""
-    c = workloads.CONFIGS[5]
-    w = workloads.generate(5, threads=16)
-    note("c5 pooled: inputs generated")
-    rs = np.random.default_rng(5)
-    check = np.sort(rs.choice(c.B, size=12, replace=False))
-    toks = rs.integers(0, c.V, size=(c.B, c.k)).astype(np.int32)
-    sub = workloads.generate(5, seqs=check)
-    toks[check] = oracle.sample_drafts(sub.draft, sub.draft_u, c.temperature, c.top_k, c.top_p, 8)
+    160 target rows instead of 2,560.  Every sequence equals the dense call
+    on the materialised rows and is checked against the oracle."""
+    from tests.test_gpu_parity import full_size_case
+    w, toks, ref = full_size_case(5)
+    c = w.config
     k1 = c.k + 1
     tp = np.ascontiguousarray(w.target[::c.branches].reshape(-1, c.V))
     tm = (np.arange(c.B) // c.branches)[:, None] * k1 + np.arange(k1)[None, :]
@@ -280,9 +277,7 @@ def test_config5_pooled_full_size_sampled():
     acc_d, out_d, ap_d = (x.cpu().numpy() for x in r)
     assert np.array_equal(acc, acc_d) and np.array_equal(out, out_d)
     assert np.array_equal(ap, ap_d, equal_nan=True)
-    ref = oracle.verify_stochastic(sub.target, sub.draft, toks[check], sub.uniforms,
-                                   c.temperature, c.top_k, c.top_p)
-    compare_stochastic(ref, acc, out, ap, rows=check, fp32=False, label="c5 pooled, 12 checked")
+    compare_stochastic(ref, acc, out, ap, fp32=False, label="c5 pooled (B=512), all checked")
 
 
 def test_pooled_walk_max_k():

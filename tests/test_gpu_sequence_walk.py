@@ -45,16 +45,21 @@ def _walk_only(target, draft, toks, u, T, top_k, top_p):
     return acc.cpu().numpy(), out.cpu().numpy()
 
 
+def _path(tt, dd, T, top_k, top_p, alpha):
+    return sv.verify_stochastic_path(tt, dd, temperature=T, top_k=top_k, top_p=top_p,
+                                     return_accept_prob=alpha)
+
+
 def _check(t, d, toks, u, T, top_k, top_p, label, tt=None, dd=None):
     ref = oracle.verify_stochastic(t, d, toks, u, T, top_k, top_p)
     tt = to_dev(t) if tt is None else tt
     dd = to_dev(d) if dd is None else dd
+    assert _path(tt, dd, T, top_k, top_p, True) == sv.SPEC_PATH_SEQUENCE_WALK, label
+    assert _path(tt, dd, T, top_k, top_p, False) == sv.SPEC_PATH_TASK_QUEUE, label
     acc, out, ap = gpu_stochastic(tt, dd, toks, u, T, top_k, top_p)
-    compare_stochastic(ref, acc, out, ap, fp32=False, label=label + " alpha requested")
+    compare_stochastic(ref, acc, out, ap, fp32=False, label=label + " alpha requested (walk)")
     acc2, out2 = _walk_only(tt, dd, toks, u, T, top_k, top_p)
-    ok = ref["flags"] == 0
-    assert np.array_equal(acc2[ok], ref["accepted_len"][ok]), label
-    assert np.array_equal(out2[ok], ref["out_tokens"][ok]), label
+    compare_stochastic(ref, acc2, out2, None, fp32=False, label=label + " task queue")
     # both modes take the same decisions (same statistics, same draws)
     assert np.array_equal(acc, acc2) and np.array_equal(out, out2), label
     return ref
@@ -154,29 +159,36 @@ def test_walk_threshold_both_sides():
     for T, top_k, top_p in [(1.0, 0, 0.95), (0.8, 20, 1.0)]:
         t, d, toks, u = _case(rs, B, k, V, T, top_k, top_p)
         ref = oracle.verify_stochastic(t, d, toks, u, T, top_k, top_p)
-        ok = ref["flags"] == 0
+        ref1 = oracle.verify_stochastic(t[: B - 1], d[: B - 1], toks[: B - 1], u[: B - 1], T,
+                                        top_k, top_p)
+        assert _path(to_dev(t), to_dev(d), T, top_k, top_p, False) == sv.SPEC_PATH_TASK_QUEUE
+        assert _path(to_dev(t[: B - 1]), to_dev(d[: B - 1]), T, top_k, top_p, False) == \
+            sv.SPEC_PATH_ROW_PASS
         a_walk, o_walk = _walk_only(t, d, toks, u, T, top_k, top_p)
         a_rows, o_rows = _walk_only(t[: B - 1], d[: B - 1], toks[: B - 1], u[: B - 1], T, top_k, top_p)
-        assert np.array_equal(a_walk[ok], ref["accepted_len"][ok])
-        assert np.array_equal(o_walk[ok], ref["out_tokens"][ok])
-        okr = ok[: B - 1]
-        assert np.array_equal(a_rows[okr], ref["accepted_len"][: B - 1][okr])
-        assert np.array_equal(o_rows[okr], ref["out_tokens"][: B - 1][okr])
-        note("threshold B=%d/%d T=%g k=%d p=%g: %d flagged" % (B - 1, B, T, top_k, top_p, int((~ok).sum())))
+        label = "threshold T=%g k=%d p=%g" % (T, top_k, top_p)
+        compare_stochastic(ref, a_walk, o_walk, None, fp32=False, label=label + " B=%d task queue" % B)
+        compare_stochastic(ref1, a_rows, o_rows, None, fp32=False, label=label + " B=%d row pass" % (B - 1))
 
 
 @pytest.mark.parametrize("V", [40000, 40003])
 def test_walk_count_tail_vectors(V):
     """Vocabularies whose rows leave each thread two or three full 16-byte
     vectors after the prefetched ones (loaded together at the end of the
-    count), plus a partial group at V = 40003, on the position-task kernel."""
+    count), and at V = 40003 a partial last group: its rows sit at a padded
+    stride of 40,008 elements, so that they stay 16-byte aligned and the
+    position-task kernel (asserted) reads them."""
     from tests.test_gpu_parity import oracle_stochastic
     rs = np.random.default_rng(V)
     B, k = 2 * torch.cuda.get_device_properties(0).multi_processor_count, 2
     t, d, toks, u = _case(rs, B, k, V, 1.0, 0, 0.95)
     ref = oracle_stochastic(t, d, toks, u, 1.0, 0, 0.95)
-    ok = ref["flags"] == 0
-    acc, out = _walk_only(t, d, toks, u, 1.0, 0, 0.95)
-    assert np.array_equal(acc[ok], ref["accepted_len"][ok])
-    assert np.array_equal(out[ok], ref["out_tokens"][ok])
-    note("count tail V=%d: %d sequences, %d flagged" % (V, B, int((~ok).sum())))
+    S = (V + 7) // 8 * 8
+    tp = np.zeros((B, k + 1, S), np.uint16)
+    tp[:, :, :V] = t
+    dp = np.zeros((B, k, S), np.uint16)
+    dp[:, :, :V] = d
+    tt, dd = to_dev(tp)[:, :, :V], to_dev(dp)[:, :, :V]
+    assert _path(tt, dd, 1.0, 0, 0.95, False) == sv.SPEC_PATH_TASK_QUEUE
+    acc, out = _walk_only(tt, dd, toks, u, 1.0, 0, 0.95)
+    compare_stochastic(ref, acc, out, None, fp32=False, label="count tail V=%d task queue" % V)
