@@ -24,7 +24,7 @@ import torch
 __all__ = ["lib", "verify_stochastic", "verify_greedy", "logits_process", "workspace_size",
            "verify_stochastic_pooled", "verify_greedy_pooled", "workspace_size_pooled",
            "tree_branches", "outcome_lookup", "logits_apply", "verify_greedy_lmhead",
-           "status_string", "SpecError",
+           "status_string", "SpecError", "verify_stochastic_path", "device_cu_count",
            "library_path"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +33,9 @@ _LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 SPEC_OK, SPEC_ERR_INVALID_ARG, SPEC_ERR_UNSUPPORTED, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = range(5)
 SPEC_DTYPE_F32, SPEC_DTYPE_BF16 = 0, 1
 SPEC_OP_STOCHASTIC, SPEC_OP_GREEDY, SPEC_OP_PROCESS, SPEC_OP_GREEDY_LMHEAD = 0, 1, 2, 3
+SPEC_PATH_ROW_PASS, SPEC_PATH_TASK_QUEUE, SPEC_PATH_SEQUENCE_WALK = 0, 1, 2
+PATH_NAMES = {SPEC_PATH_ROW_PASS: "row pass", SPEC_PATH_TASK_QUEUE: "task queue",
+              SPEC_PATH_SEQUENCE_WALK: "sequence walk"}
 
 
 class spec_logits_t(ctypes.Structure):
@@ -108,6 +111,11 @@ def lib():
             L.spec_logits_apply.restype = ctypes.c_int
             L.spec_outcome_lookup.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp, vp, vp]
             L.spec_outcome_lookup.restype = ctypes.c_int
+            L.spec_verify_stochastic_path.argtypes = [spec_logits_t, spec_logits_t, i32, i32, i32,
+                                                      P(spec_sampling_t), i32, vp]
+            L.spec_verify_stochastic_path.restype = ctypes.c_int
+            L.spec_device_cu_count.argtypes = [vp]
+            L.spec_device_cu_count.restype = ctypes.c_int
             L.spec_status_string.argtypes = [ctypes.c_int]
             L.spec_status_string.restype = ctypes.c_char_p
             _lib = L
@@ -128,19 +136,72 @@ def workspace_size(op: int, B: int, k: int, V: int, temperature: float = 1.0, to
     return int(lib().spec_workspace_size(int(op), int(B), int(k), int(V), ctypes.byref(s)))
 
 
-# One zero-filled workspace per device, grown on demand.  The library leaves
-# it zero-filled after every call, so calls ordered on one stream can share it.
+# One zero-filled workspace per (device, stream), grown on demand.  The
+# library leaves a workspace zero-filled after every call, so calls ordered on
+# one stream can share it; calls on different streams get different buffers
+# (the kernels' queue words must not be shared by calls that may overlap).  A
+# buffer is zero-filled on the stream that uses it, and a grown buffer
+# replaces the old one only on that stream, after the calls queued there.
 _ws = {}
 
 
-def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    key = device.index if device.index is not None else torch.cuda.current_device()
+def _workspace(device: torch.device, nbytes: int, stream) -> torch.Tensor:
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    key = (dev, st.cuda_stream)
     with _lock:
         buf = _ws.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            with torch.cuda.stream(st):
+                buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             _ws[key] = buf
     return buf
+
+
+def _out_tensor(t, shape, dtype, dev, what):
+    """A caller's output tensor: on the logits' device, of the right dtype
+    and shape, contiguous; anything else raises before any launch."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % what)
+    if t.device != dev:
+        raise ValueError("%s must live on %s, got %s" % (what, dev, t.device))
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s, got %s %s"
+                         % (what, dtype, tuple(shape), t.dtype, tuple(t.shape)))
+    return t
+
+
+def _outputs(out, B, k, dev, with_ap):
+    """(accepted_len, out_tokens[, accept_prob]) allocated, or the caller's
+    checked."""
+    if out is None:
+        acc = torch.empty(B, dtype=torch.int32, device=dev)
+        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
+        ap = torch.empty((B, k), dtype=torch.float32, device=dev) if with_ap else None
+        return acc, toks, ap
+    acc = _out_tensor(out[0], (B,), torch.int32, dev, "accepted_len")
+    toks = _out_tensor(out[1], (B, k + 1), torch.int32, dev, "out_tokens")
+    ap = out[2] if len(out) > 2 else None
+    if with_ap and ap is None:
+        raise ValueError("return_accept_prob needs an accept_prob tensor in out")
+    if ap is not None:
+        ap = _out_tensor(ap, (B, k), torch.float32, dev, "accept_prob")
+    return acc, toks, ap
+
+
+def _workspace_arg(workspace, dev, need, stream):
+    """The caller's workspace (checked: a contiguous byte tensor on the
+    call's device holding at least `need` bytes), or the default one of the
+    call's (device, stream)."""
+    if workspace is None:
+        return _workspace(dev, need, stream)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != dev or \
+            not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % dev)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError("workspace holds %d bytes, the call needs %d"
+                         % (workspace.numel() * workspace.element_size(), need))
+    return workspace
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -161,9 +222,9 @@ def _logits(t: torch.Tensor, rows: int) -> spec_logits_t:
     return spec_logits_t(t.data_ptr(), _dtype_code(t), 0, t.stride(0), t.stride(1))
 
 
-def _stream(stream) -> int:
+def _stream(stream, dev=None) -> int:
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
     return stream.cuda_stream
 
 
@@ -185,29 +246,48 @@ def verify_stochastic(target: torch.Tensor, draft: torch.Tensor, draft_tokens: t
     tgt, drf = _logits(target, k + 1), _logits(draft, k)
     if draft.shape[0] != B or target.shape[0] != B or draft.shape[2] != V:
         raise ValueError("target, draft and draft_tokens disagree on B or V")
-    tokens = draft_tokens.to(torch.int32).contiguous()
-    u = uniforms.to(torch.float32).contiguous()
+    dev = target.device
+    if draft.device != dev:
+        raise ValueError("target and draft must live on one device")
+    tokens = draft_tokens.to(device=dev, dtype=torch.int32).contiguous()
+    u = uniforms.to(device=dev, dtype=torch.float32).contiguous()
     if tuple(u.shape) != (B, k + 1):
         raise ValueError("uniforms must be [B][k+1]")
-    dev = target.device
-    if out is None:
-        acc = torch.empty(B, dtype=torch.int32, device=dev)
-        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-        ap = torch.empty((B, k), dtype=torch.float32, device=dev) if return_accept_prob else None
-    else:
-        acc, toks, ap = out
+    acc, toks, ap = _outputs(out, B, k, dev, return_accept_prob)
     s = _sampling(temperature, top_k, top_p)
     need = lib().spec_workspace_size(SPEC_OP_STOCHASTIC, B, k, V, ctypes.byref(s))
     if need == 0:
         _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size")
-    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws = _workspace_arg(workspace, dev, need, stream)
     rc = lib().spec_verify_stochastic(tgt, drf, tokens.data_ptr(), u.data_ptr(), B, k, V,
                                       ctypes.byref(s), acc.data_ptr(), toks.data_ptr(),
                                       ap.data_ptr() if ap is not None else None,
                                       ws.data_ptr(), ws.numel() * ws.element_size(),
-                                      _stream(stream))
+                                      _stream(stream, dev))
     _check(rc, "spec_verify_stochastic")
     return (acc, toks, ap) if return_accept_prob else (acc, toks)
+
+
+def verify_stochastic_path(target: torch.Tensor, draft: torch.Tensor, k: int | None = None, *,
+                           temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
+                           return_accept_prob: bool = False, stream=None) -> int:
+    """The kernel path (SPEC_PATH_*) verify_stochastic takes for these logits
+    and settings; nothing is launched."""
+    k = draft.shape[1] if k is None else k
+    tgt, drf = _logits(target, k + 1), _logits(draft, k)
+    s = _sampling(temperature, top_k, top_p)
+    rc = lib().spec_verify_stochastic_path(tgt, drf, target.shape[0], k, target.shape[2],
+                                           ctypes.byref(s), int(bool(return_accept_prob)),
+                                           _stream(stream, target.device))
+    if rc < 0:
+        _check(-rc, "spec_verify_stochastic_path")
+    return rc
+
+
+def device_cu_count(stream=None) -> int:
+    """The compute-unit count the library sizes its grids by (cached once per
+    device); the stream's device, or the current one."""
+    return int(lib().spec_device_cu_count(stream.cuda_stream if stream is not None else None))
 
 
 def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out=None,
@@ -217,19 +297,17 @@ def verify_greedy(target: torch.Tensor, draft_tokens: torch.Tensor, *, out=None,
     B, k = draft_tokens.shape
     V = target.shape[2]
     tgt = _logits(target, k + 1)
-    tokens = draft_tokens.to(torch.int32).contiguous()
+    if target.shape[0] != B:
+        raise ValueError("target and draft_tokens disagree on B")
     dev = target.device
-    if out is None:
-        acc = torch.empty(B, dtype=torch.int32, device=dev)
-        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    else:
-        acc, toks = out
+    tokens = draft_tokens.to(device=dev, dtype=torch.int32).contiguous()
+    acc, toks, _ = _outputs(out, B, k, dev, False)
     need = lib().spec_workspace_size(SPEC_OP_GREEDY, B, k, V, None)
     if need == 0:
         _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size")
-    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws = _workspace_arg(workspace, dev, need, stream)
     rc = lib().spec_verify_greedy(tgt, tokens.data_ptr(), B, k, V, acc.data_ptr(), toks.data_ptr(),
-                                  ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+                                  ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream, dev))
     _check(rc, "spec_verify_greedy")
     return acc, toks
 
@@ -259,10 +337,10 @@ def logits_process(logits: torch.Tensor, *, temperature: float = 1.0, top_k: int
     need = lib().spec_workspace_size(SPEC_OP_PROCESS, R, 0, V, ctypes.byref(s))
     if need == 0:
         _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size")
-    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws = _workspace_arg(workspace, dev, need, stream)
     rc = lib().spec_logits_process(desc, R, V, ctypes.byref(s), stats.data_ptr(),
                                    probs.data_ptr() if probs is not None else None,
-                                   ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+                                   ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream, dev))
     _check(rc, "spec_logits_process")
     out = {"max_logit": stats[:, 0], "threshold": stats[:, 1], "log_norm": stats[:, 2],
            "valid": stats[:, 3].view(torch.int32)}
@@ -324,22 +402,19 @@ def verify_stochastic_pooled(target_pool: torch.Tensor, draft_pool: torch.Tensor
     u = uniforms.to(device=dev, dtype=torch.float32).contiguous()
     if tuple(u.shape) != (B, k + 1):
         raise ValueError("uniforms must be [B][k+1]")
-    if out is None:
-        acc = torch.empty(B, dtype=torch.int32, device=dev)
-        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-        ap = torch.empty((B, k), dtype=torch.float32, device=dev) if return_accept_prob else None
-    else:
-        acc, toks, ap = out
+    if draft_pool.device != dev:
+        raise ValueError("target and draft pools must live on one device")
+    acc, toks, ap = _outputs(out, B, k, dev, return_accept_prob)
     s = _sampling(temperature, top_k, top_p)
     need = lib().spec_workspace_size_pooled(SPEC_OP_STOCHASTIC, Pt, Pd, B, k, V, ctypes.byref(s))
     if need == 0:
         _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size_pooled")
-    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws = _workspace_arg(workspace, dev, need, stream)
     rc = lib().spec_verify_stochastic_pooled(
         tgt, Pt, tmap.data_ptr() if tmap is not None else None, drf, Pd,
         dmap.data_ptr() if dmap is not None else None, tokens.data_ptr(), u.data_ptr(), B, k, V,
         ctypes.byref(s), acc.data_ptr(), toks.data_ptr(), ap.data_ptr() if ap is not None else None,
-        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+        ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream, dev))
     _check(rc, "spec_verify_stochastic_pooled")
     return (acc, toks, ap) if return_accept_prob else (acc, toks)
 
@@ -355,19 +430,15 @@ def verify_greedy_pooled(target_pool: torch.Tensor, draft_tokens: torch.Tensor, 
     dev = target_pool.device
     tmap = _row_map(target_map, (B, k + 1), dev)
     tokens = draft_tokens.to(device=dev, dtype=torch.int32).contiguous()
-    if out is None:
-        acc = torch.empty(B, dtype=torch.int32, device=dev)
-        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    else:
-        acc, toks = out
+    acc, toks, _ = _outputs(out, B, k, dev, False)
     need = lib().spec_workspace_size_pooled(SPEC_OP_GREEDY, Pt, 0, B, k, V, None)
     if need == 0:
         _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size_pooled")
-    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws = _workspace_arg(workspace, dev, need, stream)
     rc = lib().spec_verify_greedy_pooled(tgt, Pt, tmap.data_ptr() if tmap is not None else None,
                                          tokens.data_ptr(), B, k, V, acc.data_ptr(),
                                          toks.data_ptr(), ws.data_ptr(),
-                                         ws.numel() * ws.element_size(), _stream(stream))
+                                         ws.numel() * ws.element_size(), _stream(stream, dev))
     _check(rc, "spec_verify_greedy_pooled")
     return acc, toks
 
@@ -424,9 +495,11 @@ def outcome_lookup(accepted_len: torch.Tensor, out_tokens: torch.Tensor, pred_le
     B = accepted_len.shape[0]
     k = out_tokens.shape[1] - 1
     P = pred_len.shape[1]
+    if not accepted_len.is_cuda:
+        raise ValueError("accepted_len must live in device memory")
     dev = accepted_len.device
     acc = accepted_len.to(torch.int32).contiguous()
-    out = out_tokens.to(torch.int32).contiguous()
+    out = out_tokens.to(device=dev, dtype=torch.int32).contiguous()
     pl = pred_len.to(device=dev, dtype=torch.int32).contiguous()
     pt = pred_token.to(device=dev, dtype=torch.int32).contiguous()
     if tuple(out.shape) != (B, k + 1) or tuple(pl.shape) != (B, P) or tuple(pt.shape) != (B, P):
@@ -435,7 +508,7 @@ def outcome_lookup(accepted_len: torch.Tensor, out_tokens: torch.Tensor, pred_le
     cnt = torch.empty(1, dtype=torch.int32, device=dev) if return_count else None
     rc = lib().spec_outcome_lookup(acc.data_ptr(), out.data_ptr(), B, k, pl.data_ptr(),
                                    pt.data_ptr(), P, hit.data_ptr(),
-                                   cnt.data_ptr() if cnt is not None else None, _stream(stream))
+                                   cnt.data_ptr() if cnt is not None else None, _stream(stream, dev))
     _check(rc, "spec_outcome_lookup")
     return (hit, cnt) if return_count else hit
 
@@ -478,7 +551,7 @@ def logits_apply(logits: torch.Tensor, *, allow: torch.Tensor | None = None,
     proc = spec_processors_t(ap, a_s, a_p, pp, p_s, p_p, float(theta))
     src = spec_logits_t(logits.data_ptr(), _dtype_code(logits), 0, logits.stride(0), logits.stride(1))
     dst = spec_logits_t(out.data_ptr(), _dtype_code(out), 0, out.stride(0), out.stride(1))
-    rc = lib().spec_logits_apply(src, S, rows, V, ctypes.byref(proc), dst, _stream(stream))
+    rc = lib().spec_logits_apply(src, S, rows, V, ctypes.byref(proc), dst, _stream(stream, dev))
     _check(rc, "spec_logits_apply")
     return out
 
@@ -499,18 +572,16 @@ def verify_greedy_lmhead(hidden: torch.Tensor, weight: torch.Tensor, draft_token
         raise ValueError("hidden must be [B][k+1][d] with the weight's d")
     dev = hidden.device
     tokens = draft_tokens.to(device=dev, dtype=torch.int32).contiguous()
-    if out is None:
-        acc = torch.empty(B, dtype=torch.int32, device=dev)
-        toks = torch.empty((B, k + 1), dtype=torch.int32, device=dev)
-    else:
-        acc, toks = out
+    if weight.device != dev:
+        raise ValueError("hidden and weight must live on one device")
+    acc, toks, _ = _outputs(out, B, k, dev, False)
     need = lib().spec_workspace_size(SPEC_OP_GREEDY_LMHEAD, B, k, V, None)
     if need == 0:
         _check(SPEC_ERR_INVALID_ARG, "spec_workspace_size")
-    ws = workspace if workspace is not None else _workspace(dev, need)
+    ws = _workspace_arg(workspace, dev, need, stream)
     rc = lib().spec_verify_greedy_lmhead(hidden.data_ptr(), hidden.stride(0), hidden.stride(1),
                                          weight.data_ptr(), weight.stride(0), d, tokens.data_ptr(),
                                          B, k, V, acc.data_ptr(), toks.data_ptr(), ws.data_ptr(),
-                                         ws.numel() * ws.element_size(), _stream(stream))
+                                         ws.numel() * ws.element_size(), _stream(stream, dev))
     _check(rc, "spec_verify_greedy_lmhead")
     return acc, toks

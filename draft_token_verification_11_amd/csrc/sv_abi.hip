@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "specverify.h"
 #include "sv_kernels.hpp"
@@ -186,21 +187,47 @@ bool row_pass_fits(const Layout& L, int dtype, bool vec) {
 
 float log2e_over(float T) { return float(1.4426950408889634 / double(T)); }
 
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+// The compute-unit count of each device, queried once per device (the first
+// call on a device, with a thread-safe once) and kept until the process ends.
+// Grids are sized by the device of the stream a call is enqueued on.
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultCus = 256;  // used when the device cannot be queried
+std::once_flag g_cus_once[kMaxDevices];
+int g_cus[kMaxDevices];
+
+int query_cus(int dev) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
-    cus = 256;
+    cus = kDefaultCus;
   return cus;
+}
+
+int stream_device(hipStream_t st) {
+  int dev = -1;
+  if (st != nullptr) {
+    hipDevice_t d = -1;
+    if (hipStreamGetDevice(st, &d) == hipSuccess) dev = d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    dev = -1;
+  }
+  return dev;
+}
+
+int device_cus(hipStream_t st) {
+  const int dev = stream_device(st);
+  if (dev < 0) return kDefaultCus;
+  if (dev >= kMaxDevices) return query_cus(dev);
+  std::call_once(g_cus_once[dev], [dev] { g_cus[dev] = query_cus(dev); });
+  return g_cus[dev];
 }
 
 int walk_grid_for(int cus) { return cus < kMaxWalkGrid ? cus : kMaxWalkGrid; }
 
 // Workgroups of the persistent filter: one per CU, a multiple of 8 (one
 // range of rows per XCD), no more than needed.
-int persistent_grid(int64_t rows) {
-  int64_t g = device_cus();
+int persistent_grid(int64_t rows, int cus) {
+  int64_t g = cus;
   if (rows < g) g = rows;
   g = (g + 7) / 8 * 8;
   return int(g);
@@ -210,6 +237,16 @@ int persistent_grid(int64_t rows) {
 // pays off once every CU has several sequences to take from the queue;
 // smaller batches spread their rows over the chip instead.
 constexpr int kSeqPerCu = 2;
+
+// Which kernels a stochastic call runs (spec_path_t): aligned bf16 rows with
+// at least kSeqPerCu sequences per CU read rows in walk order in one kernel
+// -- the position-task queue, or the whole-sequence walk when alpha is asked
+// for (it is reported past the stop, so every row is read); anything else a
+// row pass over every row followed by the per-sequence tail.
+int stochastic_path(int dtype, bool vec, int64_t B, int cus, bool want_alpha) {
+  if (dtype != SPEC_DTYPE_BF16 || !vec || B < int64_t(kSeqPerCu) * cus) return SPEC_PATH_ROW_PASS;
+  return want_alpha ? SPEC_PATH_SEQUENCE_WALK : SPEC_PATH_TASK_QUEUE;
+}
 
 constexpr int kPrefetch = 2;  // 16-byte vectors per thread prefetched for the next row
 constexpr int kLoadDepth = 8;  // 16-byte loads in flight per thread in the row stream
@@ -252,13 +289,13 @@ void launch_probs(const Layout& L, const sv::RowMap& map, int64_t V, float a, co
 
 template <typename T, bool VEC>
 void launch_filter(const Layout& L, const sv::RowMap& map, int64_t V, float a,
-                   const spec_sampling_t& s, sv::RowStat* rs, hipStream_t st) {
+                   const spec_sampling_t& s, sv::RowStat* rs, hipStream_t st, int cus) {
   const dim3 grid(unsigned(L.rows)), block(kFilterThreads);
   if constexpr (sizeof(T) == 2) {
     if (VEC) {
       sv::FilterArgs F{map, V, L.rows, a, s.top_k, s.top_p, rs};
       hipLaunchKernelGGL((sv::k_filter_bf16_persistent<true, kPrefetch, kLoadDepth>),
-                         dim3(persistent_grid(L.rows)), block, 0, st, F);
+                         dim3(persistent_grid(L.rows, cus)), block, 0, st, F);
     } else {
       hipLaunchKernelGGL((sv::k_filter_bf16_hist<VEC>), grid, block, 0, st, map, V, a, s.top_k,
                          s.top_p, rs);
@@ -290,7 +327,7 @@ template <typename T, bool VEC>
 struct StochasticRun {
   static void run(const Layout& L, const sv::RowMap& map, int64_t B, int64_t V, float a,
                   const spec_sampling_t& s, sv::TailArgs& args, char* ws, hipStream_t st,
-                  int walk_grid) {
+                  int walk_grid, int cus) {
     if constexpr (sizeof(T) == 2 && VEC) {
       if (walk_grid > 0 && !args.accept_prob) {
         sv::TaskArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
@@ -314,7 +351,7 @@ struct StochasticRun {
     }
     if (L.filtered) {
       auto* rs = reinterpret_cast<sv::RowStat*>(ws + L.rowstat_off);
-      launch_filter<T, VEC>(L, map, V, a, s, rs, st);
+      launch_filter<T, VEC>(L, map, V, a, s, rs, st, cus);
       args.rowstat = rs;
       args.part = nullptr;
     } else if (V <= kDirectMaxV) {
@@ -330,7 +367,7 @@ struct StochasticRun {
     args.nchunks = L.nchunks;
     // small batches: the draws spread over the chip instead of one tail
     // workgroup per sequence reading its two rows alone
-    const bool split = VEC && L.split_draw && L.draw_chunks >= 2 && 2 * B <= device_cus();
+    const bool split = VEC && L.split_draw && L.draw_chunks >= 2 && 2 * B <= cus;
     auto* jobs = reinterpret_cast<sv::DrawJob*>(ws + L.jobs_off);
     auto* dsums = reinterpret_cast<double*>(ws + L.dsums_off);
     args.jobs = split ? jobs : nullptr;
@@ -356,11 +393,11 @@ struct GreedyRun {
 template <typename T, bool VEC>
 struct ProcessRun {
   static void run(const Layout& L, const sv::RowMap& map, int64_t V, float a, const spec_sampling_t& s,
-                  spec_row_stats_t* row_stats, float* probs, char* ws, hipStream_t st) {
+                  spec_row_stats_t* row_stats, float* probs, char* ws, hipStream_t st, int cus) {
     auto* rs = reinterpret_cast<sv::RowStat*>(ws + L.rowstat_off);
     sv::Partial* part = nullptr;
     if (L.filtered) {
-      launch_filter<T, VEC>(L, map, V, a, s, rs, st);
+      launch_filter<T, VEC>(L, map, V, a, s, rs, st, cus);
     } else {
       part = reinterpret_cast<sv::Partial*>(ws + L.part_off);
       launch_partials<T, VEC>(L, map, V, a, part, st);
@@ -379,7 +416,7 @@ template <typename T, bool VEC>
 struct PooledStochasticRun {
   static void run(const Layout& L, const sv::RowMap& map, int64_t B, int64_t V, float a,
                   const spec_sampling_t& s, sv::TailArgs& args, char* ws, hipStream_t st,
-                  int walk_grid) {
+                  int walk_grid, int cus) {
     auto* rs = reinterpret_cast<sv::RowStat*>(ws + L.rowstat_off);
     int64_t clear_bytes = 0;
     if constexpr (sizeof(T) == 2 && VEC) {
@@ -388,7 +425,7 @@ struct PooledStochasticRun {
         const int64_t nt = map.nt;
         sv::FilterArgs F{map, V, nt, a, s.top_k, s.top_p, rs};
         hipLaunchKernelGGL((sv::k_filter_bf16_persistent<true, kPrefetch, kLoadDepth>),
-                           dim3(persistent_grid(nt)), dim3(kFilterThreads), 0, st, F);
+                           dim3(persistent_grid(nt, cus)), dim3(kFilterThreads), 0, st, F);
         sv::SeqArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
                       args.accepted_len, args.out_tokens, args.accept_prob,
                       reinterpret_cast<uint32_t*>(ws + L.queue_off), rs,
@@ -400,7 +437,7 @@ struct PooledStochasticRun {
     }
     if (clear_bytes == 0) {
       if (L.filtered) {
-        launch_filter<T, VEC>(L, map, V, a, s, rs, st);
+        launch_filter<T, VEC>(L, map, V, a, s, rs, st, cus);
         args.rowstat = rs;
         args.part = nullptr;
         clear_bytes = L.rows * int64_t(sizeof(sv::RowStat));
@@ -479,10 +516,9 @@ int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft, const int3
   const Layout L = make_layout(SPEC_OP_STOCHASTIC, B, k, V, sampling);
   if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
   const bool vec = vec_ok(target) && vec_ok(draft);
-  // the whole-sequence walk: aligned bf16 rows, at least kSeqPerCu sequences per CU
-  const int cus = device_cus();
-  const int walk_grid =
-      (target.dtype == SPEC_DTYPE_BF16 && vec && int64_t(B) >= int64_t(kSeqPerCu) * cus) ? walk_grid_for(cus) : 0;
+  const int cus = device_cus(static_cast<hipStream_t>(stream));
+  const int path = stochastic_path(target.dtype, vec, B, cus, accept_prob != nullptr);
+  const int walk_grid = path != SPEC_PATH_ROW_PASS ? walk_grid_for(cus) : 0;
   if (!walk_grid && (!row_pass_fits(L, target.dtype, vec) || !grid_fits(B, kTailThreads)))
     return SPEC_ERR_UNSUPPORTED;
 
@@ -502,7 +538,7 @@ int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft, const int3
   (void)hipGetLastError();
   dispatch<StochasticRun>(target.dtype, vec, L, map, int64_t(B), int64_t(V), a, *sampling, args,
                           static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
-                          walk_grid);
+                          walk_grid, cus);
   return finish_launch();
 }
 
@@ -545,7 +581,7 @@ int spec_logits_process(spec_logits_t logits, int32_t R, int32_t V, const spec_s
   auto st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   dispatch<ProcessRun>(logits.dtype, vec_ok(logits), L, map, int64_t(V), a, *sampling, row_stats,
-                       probs, static_cast<char*>(workspace), st);
+                       probs, static_cast<char*>(workspace), st, device_cus(st));
   // Leave the workspace zero-filled, as the contract promises.
   const int64_t words = int64_t(L.total / 16);
   hipLaunchKernelGGL(sv::k_clear, dim3(unsigned((words + 255) / 256)), dim3(256), 0, st,
@@ -591,7 +627,7 @@ int spec_verify_stochastic_pooled(spec_logits_t target_pool, int32_t n_target_ro
   const Layout L = make_pooled_layout(SPEC_OP_STOCHASTIC, n_target_rows, n_draft_rows, k, V, sampling);
   if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
   const bool vec = vec_ok(target_pool) && vec_ok(draft_pool);
-  const int cus = device_cus();
+  const int cus = device_cus(static_cast<hipStream_t>(stream));
   const int walk_grid =
       (target_pool.dtype == SPEC_DTYPE_BF16 && vec && int64_t(B) >= int64_t(kSeqPerCu) * cus)
           ? walk_grid_for(cus) : 0;
@@ -614,7 +650,7 @@ int spec_verify_stochastic_pooled(spec_logits_t target_pool, int32_t n_target_ro
   (void)hipGetLastError();
   dispatch<PooledStochasticRun>(target_pool.dtype, vec, L, map, int64_t(B), int64_t(V), args.a,
                                 *sampling, args, static_cast<char*>(workspace),
-                                static_cast<hipStream_t>(stream), walk_grid);
+                                static_cast<hipStream_t>(stream), walk_grid, cus);
   return finish_launch();
 }
 
@@ -756,6 +792,22 @@ int spec_outcome_lookup(const int32_t* accepted_len, const int32_t* out_tokens, 
                        hit_count);
   return finish_launch();
 }
+
+int spec_verify_stochastic_path(spec_logits_t target, spec_logits_t draft, int32_t B, int32_t k,
+                                int32_t V, const spec_sampling_t* sampling, int32_t with_accept_prob,
+                                void* stream) {
+  int rc;
+  if ((rc = check_sizes(B, k, V, true)) != SPEC_OK) return -rc;
+  if ((rc = check_sampling(sampling)) != SPEC_OK) return -rc;
+  if ((rc = check_logits(target, V)) != SPEC_OK) return -rc;
+  if ((rc = check_logits(draft, V)) != SPEC_OK) return -rc;
+  if (target.dtype != draft.dtype) return -SPEC_ERR_INVALID_ARG;
+  const bool vec = vec_ok(target) && vec_ok(draft);
+  return stochastic_path(target.dtype, vec, B, device_cus(static_cast<hipStream_t>(stream)),
+                         with_accept_prob != 0);
+}
+
+int spec_device_cu_count(void* stream) { return device_cus(static_cast<hipStream_t>(stream)); }
 
 const char* spec_status_string(int status) {
   switch (status) {

@@ -287,6 +287,30 @@ int spec_outcome_lookup(const int32_t* accepted_len, const int32_t* out_tokens, 
                         int32_t k, const int32_t* pred_len, const int32_t* pred_token,
                         int32_t P, int32_t* hit_index, int32_t* hit_count, void* stream);
 
+/* Kernel paths of a stochastic verify call (spec_verify_stochastic_path). */
+typedef enum {
+  SPEC_PATH_ROW_PASS = 0,      /* a pass over every row, then one tail per sequence */
+  SPEC_PATH_TASK_QUEUE = 1,    /* one kernel of position tasks, rows read in walk order */
+  SPEC_PATH_SEQUENCE_WALK = 2  /* one kernel walking whole sequences (accept_prob asked for) */
+} spec_path_t;
+
+/* The path spec_verify_stochastic takes for these arguments on the device of
+ * `stream` (nothing is launched; the logits' data is not read): aligned bf16
+ * rows (16-byte aligned base and strides) in batches of at least two
+ * sequences per compute unit are read in walk order by one kernel, the
+ * task queue or, when accept_prob is requested (with_accept_prob != 0), the
+ * whole-sequence walk; other calls take the row pass.  Returns a
+ * spec_path_t, or minus a spec_status_t for arguments the call would
+ * reject (sizes, settings, logits descriptors). */
+int spec_verify_stochastic_path(spec_logits_t target, spec_logits_t draft, int32_t B, int32_t k,
+                                int32_t V, const spec_sampling_t* sampling /* host */,
+                                int32_t with_accept_prob, void* stream);
+
+/* The compute-unit count the library sizes its grids by on the device of
+ * `stream` (NULL: the current device): queried once per device and kept
+ * until the process ends; 256 when no device can be queried. */
+int spec_device_cu_count(void* stream);
+
 /* Static description of a status code. */
 const char* spec_status_string(int status);
 

@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
         "spec_logits_apply", "spec_logits_process", "spec_outcome_lookup", "spec_status_string",
         "spec_verify_greedy", "spec_verify_greedy_lmhead",
         "spec_verify_greedy_pooled", "spec_verify_stochastic", "spec_verify_stochastic_pooled",
-        "spec_workspace_size", "spec_workspace_size_pooled"])
+        "spec_workspace_size", "spec_workspace_size_pooled", "spec_verify_stochastic_path",
+        "spec_device_cu_count"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -245,3 +246,84 @@ def test_lmhead_validation():
     assert call(wstr=32) == sv.SPEC_ERR_INVALID_ARG        # weight stride < d
     assert call(work=None) == sv.SPEC_ERR_WORKSPACE
     assert call(B=0) == sv.SPEC_ERR_INVALID_ARG
+
+
+def test_cu_count_cached_and_thread_safe():
+    """The CU count is queried once per device behind a thread-safe once: the
+    same value from every thread and call.  Without a visible device the
+    library falls back to 256 (that of an MI355X)."""
+    import threading
+    import torch
+    L = sv.lib()
+    vals = []
+
+    def work():
+        for _ in range(200):
+            vals.append(L.spec_device_cu_count(None))
+
+    ths = [threading.Thread(target=work) for _ in range(8)]
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    assert len(set(vals)) == 1
+    if torch.cuda.is_available():
+        assert vals[0] == torch.cuda.get_device_properties(0).multi_processor_count
+    else:
+        assert vals[0] == 256
+
+
+def test_stochastic_path_rules():
+    """The path a stochastic call takes, from the arguments alone (host only:
+    the logits are never read).  With the 256-CU fallback (no device) or an
+    MI355X, 512 aligned bf16 sequences take the task queue (the walk with
+    alpha), 511 the row pass, as do fp32 rows and misaligned strides."""
+    L = sv.lib()
+    cus = L.spec_device_cu_count(None)
+    s = sv.spec_sampling_t(1.0, 0, 0.95)
+    V, k = 151936, 4
+
+    def path(B, dtype=1, pos=V, ptr=4096, alpha=0):
+        t = sv.spec_logits_t(ptr, dtype, 0, (k + 1) * pos, pos)
+        d = sv.spec_logits_t(ptr, dtype, 0, k * pos, pos)
+        return L.spec_verify_stochastic_path(t, d, B, k, V, ctypes.byref(s), alpha, None)
+
+    assert path(2 * cus) == sv.SPEC_PATH_TASK_QUEUE
+    assert path(2 * cus, alpha=1) == sv.SPEC_PATH_SEQUENCE_WALK
+    assert path(2 * cus - 1) == sv.SPEC_PATH_ROW_PASS
+    assert path(2 * cus, dtype=0) == sv.SPEC_PATH_ROW_PASS
+    assert path(2 * cus, pos=V + 3) == sv.SPEC_PATH_ROW_PASS  # rows not 16-byte aligned
+    assert path(2 * cus, ptr=4098) == sv.SPEC_PATH_ROW_PASS
+    assert path(0) == -sv.SPEC_ERR_INVALID_ARG
+    assert path(2 * cus, pos=V - 1) == -sv.SPEC_ERR_INVALID_ARG
+    bad = sv.spec_sampling_t(0.0, 0, 0.95)
+    t = sv.spec_logits_t(4096, 1, 0, 5 * V, V)
+    assert L.spec_verify_stochastic_path(t, t, 512, k, V, ctypes.byref(bad), 0, None) == \
+        -sv.SPEC_ERR_INVALID_ARG
+
+
+def test_binding_rejects_misplaced_outputs():
+    """Output tensors are checked for device, dtype, shape and contiguity
+    before any launch (a host pointer handed to a kernel would fault)."""
+    import torch
+    dev = torch.device("cpu")
+    good = (torch.empty(4, dtype=torch.int32), torch.empty((4, 3), dtype=torch.int32),
+            torch.empty((4, 2), dtype=torch.float32))
+    acc, toks, ap = sv._outputs(good, 4, 2, dev, True)
+    assert acc is good[0] and ap is good[2]
+    with pytest.raises(ValueError):
+        sv._outputs(good, 4, 2, torch.device("meta"), True)  # wrong device
+    with pytest.raises(ValueError):
+        sv._outputs((good[0].long(), good[1], good[2]), 4, 2, dev, True)  # dtype
+    with pytest.raises(ValueError):
+        sv._outputs((good[0], torch.empty((4, 4), dtype=torch.int32), good[2]), 4, 2, dev, True)
+    with pytest.raises(ValueError):
+        sv._outputs((good[0], torch.empty((3, 4), dtype=torch.int32).t(), good[2]), 4, 2, dev, True)
+    with pytest.raises(ValueError):
+        sv._outputs(good[:2], 4, 2, dev, True)  # alpha asked for, no tensor
+    # logits in host memory are refused before any library call
+    with pytest.raises(ValueError):
+        sv.verify_stochastic(torch.zeros((4, 3, 8)), torch.zeros((4, 2, 8)),
+                             torch.zeros((4, 2), dtype=torch.int32), torch.zeros((4, 3)))
+    with pytest.raises(ValueError):
+        sv.verify_greedy(torch.zeros((4, 3, 8)), torch.zeros((4, 2), dtype=torch.int32))
