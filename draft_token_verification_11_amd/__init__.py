@@ -25,6 +25,7 @@ __all__ = ["lib", "verify_stochastic", "verify_greedy", "logits_process", "works
            "verify_stochastic_pooled", "verify_greedy_pooled", "workspace_size_pooled",
            "tree_branches", "outcome_lookup", "logits_apply", "verify_greedy_lmhead",
            "status_string", "SpecError", "verify_stochastic_path", "device_cu_count",
+           "verify_stochastic_noalloc", "NOALLOC_SCRATCH_BYTES",
            "library_path"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +88,10 @@ def lib():
             L.spec_verify_stochastic.argtypes = [spec_logits_t, spec_logits_t, vp, vp, i32, i32,
                                                  i32, P(spec_sampling_t), vp, vp, vp, vp, sz, vp]
             L.spec_verify_stochastic.restype = ctypes.c_int
+            L.spec_verify_stochastic_noalloc.argtypes = [spec_logits_t, spec_logits_t, vp, vp, i32,
+                                                         i32, i32, P(spec_sampling_t), vp, vp, vp,
+                                                         vp]
+            L.spec_verify_stochastic_noalloc.restype = ctypes.c_int
             L.spec_verify_greedy.argtypes = [spec_logits_t, vp, i32, i32, i32, vp, vp, vp, sz, vp]
             L.spec_verify_greedy.restype = ctypes.c_int
             L.spec_logits_process.argtypes = [spec_logits_t, i32, i32, P(spec_sampling_t), vp, vp,
@@ -266,6 +271,37 @@ def verify_stochastic(target: torch.Tensor, draft: torch.Tensor, draft_tokens: t
                                       _stream(stream, dev))
     _check(rc, "spec_verify_stochastic")
     return (acc, toks, ap) if return_accept_prob else (acc, toks)
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def verify_stochastic_noalloc(target: torch.Tensor, draft: torch.Tensor,
+                              draft_tokens: torch.Tensor, uniforms: torch.Tensor, *, out,
+                              temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
+                              stream=None):
+    """verify_stochastic through spec_verify_stochastic_noalloc: no workspace,
+    the library's per-GPU scratch array instead (calls that may overlap on
+    one GPU race).  Every tensor must already be on the logits' device in
+    its final dtype and layout -- draft_tokens int32 [B][k], uniforms
+    float32 [B][k+1], out = (accepted_len, out_tokens[, accept_prob]) -- so
+    that the call allocates nothing, here or in the library."""
+    B, k = draft_tokens.shape
+    V = target.shape[2]
+    tgt, drf = _logits(target, k + 1), _logits(draft, k)
+    dev = target.device
+    if draft.device != dev or target.shape[0] != B or draft.shape[0] != B or draft.shape[2] != V:
+        raise ValueError("target, draft and draft_tokens disagree on device, B or V")
+    tokens = _out_tensor(draft_tokens, (B, k), torch.int32, dev, "draft_tokens")
+    u = _out_tensor(uniforms, (B, k + 1), torch.float32, dev, "uniforms")
+    acc, toks, ap = _outputs(out, B, k, dev, len(out) > 2 and out[2] is not None)
+    s = _sampling(temperature, top_k, top_p)
+    rc = lib().spec_verify_stochastic_noalloc(tgt, drf, tokens.data_ptr(), u.data_ptr(), B, k, V,
+                                              ctypes.byref(s), acc.data_ptr(), toks.data_ptr(),
+                                              ap.data_ptr() if ap is not None else None,
+                                              _stream(stream, dev))
+    _check(rc, "spec_verify_stochastic_noalloc")
+    return (acc, toks, ap) if ap is not None else (acc, toks)
 
 
 def verify_stochastic_path(target: torch.Tensor, draft: torch.Tensor, k: int | None = None, *,

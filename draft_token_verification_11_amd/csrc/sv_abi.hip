@@ -480,6 +480,49 @@ int finish_launch() {
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
+int check_stochastic_args(const spec_logits_t& target, const spec_logits_t& draft,
+                          const int32_t* draft_tokens, const float* uniforms, int64_t B,
+                          int64_t k, int64_t V, const spec_sampling_t* sampling,
+                          const int32_t* accepted_len, const int32_t* out_tokens) {
+  int rc;
+  if ((rc = check_sizes(B, k, V, true)) != SPEC_OK) return rc;
+  if ((rc = check_sampling(sampling)) != SPEC_OK) return rc;
+  if ((rc = check_logits(target, V)) != SPEC_OK) return rc;
+  if ((rc = check_logits(draft, V)) != SPEC_OK) return rc;
+  if (target.dtype != draft.dtype) return SPEC_ERR_INVALID_ARG;
+  if (!draft_tokens || !uniforms || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
+  return SPEC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace of spec_verify_stochastic_noalloc: one array per GPU in the
+// library's code object, kept until the process ends.  In host code the
+// array's name is only a stand-in for the device symbol: its device address
+// is taken once per device (with that device current) by
+// hipGetSymbolAddress and only that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_rc[kMaxDevices];
+
+// The scratch array's address on device `dev` (nullptr if it cannot be had).
+void* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = -1;
+    hipError_t rc = hipGetDevice(&cur);
+    if (rc == hipSuccess && cur != dev) rc = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (rc == hipSuccess) rc = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+    g_scratch_rc[dev] = rc;
+    g_scratch_ptr[dev] = rc == hipSuccess ? ptr : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -507,12 +550,9 @@ int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft, const int3
                            int32_t* out_tokens, float* accept_prob, void* workspace,
                            size_t workspace_bytes, void* stream) {
   int rc;
-  if ((rc = check_sizes(B, k, V, true)) != SPEC_OK) return rc;
-  if ((rc = check_sampling(sampling)) != SPEC_OK) return rc;
-  if ((rc = check_logits(target, V)) != SPEC_OK) return rc;
-  if ((rc = check_logits(draft, V)) != SPEC_OK) return rc;
-  if (target.dtype != draft.dtype) return SPEC_ERR_INVALID_ARG;
-  if (!draft_tokens || !uniforms || !accepted_len || !out_tokens) return SPEC_ERR_INVALID_ARG;
+  if ((rc = check_stochastic_args(target, draft, draft_tokens, uniforms, B, k, V, sampling,
+                                  accepted_len, out_tokens)) != SPEC_OK)
+    return rc;
   const Layout L = make_layout(SPEC_OP_STOCHASTIC, B, k, V, sampling);
   if ((rc = check_workspace(workspace, workspace_bytes, L)) != SPEC_OK) return rc;
   const bool vec = vec_ok(target) && vec_ok(draft);
@@ -540,6 +580,32 @@ int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft, const int3
                           static_cast<char*>(workspace), static_cast<hipStream_t>(stream),
                           walk_grid, cus);
   return finish_launch();
+}
+
+int spec_verify_stochastic_noalloc(spec_logits_t target, spec_logits_t draft,
+                                   const int32_t* draft_tokens, const float* uniforms, int32_t B,
+                                   int32_t k, int32_t V, const spec_sampling_t* sampling,
+                                   int32_t* accepted_len, int32_t* out_tokens, float* accept_prob,
+                                   void* stream) {
+  int rc;
+  if ((rc = check_stochastic_args(target, draft, draft_tokens, uniforms, B, k, V, sampling,
+                                  accepted_len, out_tokens)) != SPEC_OK)
+    return rc;
+  const Layout L = make_layout(SPEC_OP_STOCHASTIC, B, k, V, sampling);
+  if (L.total > kScratchBytes) return SPEC_ERR_UNSUPPORTED;
+  auto st = static_cast<hipStream_t>(stream);
+  void* ws = scratch_on(stream_device(st));
+  if (!ws) return SPEC_ERR_HIP;
+  // The array keeps whatever the last call on this GPU left: the region the
+  // call uses is zeroed first, by a kernel (no memset node, so the call can
+  // be captured into a graph).
+  const int64_t words = int64_t(L.total / 16);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(sv::k_clear, dim3(unsigned((words + 255) / 256)), dim3(256), 0, st,
+                     static_cast<uint4*>(ws), words);
+  if ((rc = finish_launch()) != SPEC_OK) return rc;
+  return spec_verify_stochastic(target, draft, draft_tokens, uniforms, B, k, V, sampling,
+                                accepted_len, out_tokens, accept_prob, ws, kScratchBytes, stream);
 }
 
 int spec_verify_greedy(spec_logits_t target, const int32_t* draft_tokens, int32_t B, int32_t k,

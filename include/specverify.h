@@ -139,6 +139,26 @@ int spec_verify_stochastic(spec_logits_t target, spec_logits_t draft,
                            float* accept_prob, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* spec_verify_stochastic without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The call allocates nothing: its
+ * kernels use a scratch array of SPEC_NOALLOC_SCRATCH_BYTES in the library's
+ * own code object, one per GPU, held until the process ends.  The caller
+ * still passes every input and output (device pointers, as in
+ * spec_verify_stochastic, with the same results).
+ * Limits: calls whose spec_workspace_size(SPEC_OP_STOCHASTIC, ...) exceeds
+ * SPEC_NOALLOC_SCRATCH_BYTES return SPEC_ERR_UNSUPPORTED before anything is
+ * enqueued.  The region a call uses is zeroed by a kernel at its start.
+ * All calls on one GPU share that GPU's array: calls that may overlap on one
+ * GPU (other streams, other host threads) race and must be ordered by the
+ * caller.  SPEC_ERR_HIP if the array's device address cannot be obtained. */
+#define SPEC_NOALLOC_SCRATCH_BYTES (16u << 20)
+int spec_verify_stochastic_noalloc(spec_logits_t target, spec_logits_t draft,
+                                   const int32_t* draft_tokens, const float* uniforms,
+                                   int32_t B, int32_t k, int32_t V,
+                                   const spec_sampling_t* sampling, int32_t* accepted_len,
+                                   int32_t* out_tokens, float* accept_prob, void* stream);
+
 /* Greedy verify: a*_j = argmax_x target[b][j][x] (lowest index on ties);
  * n = first j < k with draft_tokens[b][j] != a*_j, else k; out_tokens gets
  * the n matching drafts, then a*_n, then -1 padding. */

@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
         "spec_verify_greedy", "spec_verify_greedy_lmhead",
         "spec_verify_greedy_pooled", "spec_verify_stochastic", "spec_verify_stochastic_pooled",
         "spec_workspace_size", "spec_workspace_size_pooled", "spec_verify_stochastic_path",
-        "spec_device_cu_count"])
+        "spec_device_cu_count", "spec_verify_stochastic_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -327,3 +327,22 @@ def test_binding_rejects_misplaced_outputs():
                              torch.zeros((4, 2), dtype=torch.int32), torch.zeros((4, 3)))
     with pytest.raises(ValueError):
         sv.verify_greedy(torch.zeros((4, 3, 8)), torch.zeros((4, 2), dtype=torch.int32))
+
+
+def test_noalloc_rejections_before_any_launch():
+    """The allocation-free call validates like spec_verify_stochastic and
+    rejects shapes whose workspace exceeds its scratch array, before any
+    HIP call (host only)."""
+    L = sv.lib()
+    s = sv.spec_sampling_t(1.0, 0, 0.95)
+    V, k = 151936, 64
+    t = sv.spec_logits_t(4096, 1, 0, 0, V)
+    B = 1 << 20
+    assert L.spec_workspace_size(sv.SPEC_OP_STOCHASTIC, B, k, V, ctypes.byref(s)) > \
+        sv.NOALLOC_SCRATCH_BYTES
+    assert L.spec_verify_stochastic_noalloc(t, t, 4096, 4096, B, k, V, ctypes.byref(s), 4096, 4096,
+                                            None, None) == sv.SPEC_ERR_UNSUPPORTED
+    assert L.spec_verify_stochastic_noalloc(t, t, None, 4096, 4, 4, V, ctypes.byref(s), 4096, 4096,
+                                            None, None) == sv.SPEC_ERR_INVALID_ARG
+    assert L.spec_verify_stochastic_noalloc(t, t, 4096, 4096, 0, 4, V, ctypes.byref(s), 4096, 4096,
+                                            None, None) == sv.SPEC_ERR_INVALID_ARG
