@@ -332,7 +332,7 @@ def run_workload(cfg, args, sv, torch, dev, stream, threads, headline):
     a1_bytes = rows_all * row_bytes  # every row once
     draw_bytes = float(np.mean([draw_rows[i % len(sets)] for i in range(args.steps)])) * row_bytes
     filtered = bool(c.top_k) or c.top_p < 1.0
-    row_kernel = ("k_filter_bf16_persistent (exact bf16 key histogram, top-k/top-p)"
+    row_kernel = ("k_filter_win_persistent (exact bf16 window histogram, two workgroups per CU, top-k/top-p)"
                   if c.dtype == "bf16" and filtered else
                   "k_filter_bisect (fp32 top-k/top-p)" if filtered else
                   "k_row_partials (split-V max / sum of exponentials)")

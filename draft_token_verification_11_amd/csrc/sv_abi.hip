@@ -9,6 +9,7 @@
 
 #include "specverify.h"
 #include "sv_kernels.hpp"
+#include "sv_window.hpp"
 
 namespace {
 
@@ -224,10 +225,10 @@ int device_cus(hipStream_t st) {
 
 int walk_grid_for(int cus) { return cus < kMaxWalkGrid ? cus : kMaxWalkGrid; }
 
-// Workgroups of the persistent filter: one per CU, a multiple of 8 (one
+// Workgroups of the persistent filter: `per_cu` per CU, a multiple of 8 (one
 // range of rows per XCD), no more than needed.
-int persistent_grid(int64_t rows, int cus) {
-  int64_t g = cus;
+int persistent_grid(int64_t rows, int cus, int per_cu = 1) {
+  int64_t g = int64_t(cus) * per_cu;
   if (rows < g) g = rows;
   g = (g + 7) / 8 * 8;
   return int(g);
@@ -293,9 +294,10 @@ void launch_filter(const Layout& L, const sv::RowMap& map, int64_t V, float a,
   const dim3 grid(unsigned(L.rows)), block(kFilterThreads);
   if constexpr (sizeof(T) == 2) {
     if (VEC) {
+      // two 512-thread workgroups per CU, each with a 64 KiB window histogram
       sv::FilterArgs F{map, V, L.rows, a, s.top_k, s.top_p, rs};
-      hipLaunchKernelGGL((sv::k_filter_bf16_persistent<true, kPrefetch, kLoadDepth>),
-                         dim3(persistent_grid(L.rows, cus)), block, 0, st, F);
+      hipLaunchKernelGGL((sv::k_filter_win_persistent<kPrefetch, kLoadDepth>),
+                         dim3(persistent_grid(L.rows, cus, 2)), dim3(sv::kWinThreads), 0, st, F);
     } else {
       hipLaunchKernelGGL((sv::k_filter_bf16_hist<VEC>), grid, block, 0, st, map, V, a, s.top_k,
                          s.top_p, rs);
@@ -424,8 +426,8 @@ struct PooledStochasticRun {
         // target pool statistics first, then the walk over the draft rows
         const int64_t nt = map.nt;
         sv::FilterArgs F{map, V, nt, a, s.top_k, s.top_p, rs};
-        hipLaunchKernelGGL((sv::k_filter_bf16_persistent<true, kPrefetch, kLoadDepth>),
-                           dim3(persistent_grid(nt, cus)), dim3(kFilterThreads), 0, st, F);
+        hipLaunchKernelGGL((sv::k_filter_win_persistent<kPrefetch, kLoadDepth>),
+                           dim3(persistent_grid(nt, cus, 2)), dim3(sv::kWinThreads), 0, st, F);
         sv::SeqArgs A{map, V, args.k, int32_t(B), a, s.top_k, s.top_p, args.tokens, args.u,
                       args.accepted_len, args.out_tokens, args.accept_prob,
                       reinterpret_cast<uint32_t*>(ws + L.queue_off), rs,

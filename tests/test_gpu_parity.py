@@ -358,11 +358,14 @@ def test_bf16_histogram_overflow_falls_back():
     _process_compare(t.reshape(-1, V), 1.0, 0, 0.9, "process overflow rows", False)
 
 
-@pytest.mark.parametrize("case", ["tiny", "huge", "edges", "zeros"])
+@pytest.mark.parametrize("case", ["tiny", "huge", "edges", "edges31", "zeros"])
 def test_bf16_window_edges(case):
     """Extreme bf16 codes: many +-0 (and top-k cuts that fall on 0), non-zero
-    magnitudes below 2^-63, values of 2^65 and above (one-hot rows), and the
-    codes 2^-63 and (2 - 2^-7) 2^64 in rows of ordinary logits."""
+    magnitudes below 2^-63, values of 2^65 and above (one-hot rows), the codes
+    2^-63 and (2 - 2^-7) 2^64 in rows of ordinary logits, and both ends of the
+    row filter's exponent window [2^-31, 2^33) with their neighbours outside
+    it (rows outside the window, or decisions among tiny values, take the
+    exact bisection path)."""
     rs = np.random.default_rng(29)
     B, k, V = 6, 3, 3000
     t = rs.normal(0, 2, (B, k + 1, V)).astype(np.float32)
@@ -383,13 +386,29 @@ def test_bf16_window_edges(case):
         t[:, :, 2] = -hi
         d[:, :, 3] = -hi
         t[0, 1, 4] = hi
+    elif case == "edges31":
+        # both ends of the row filter's exponent window [2^-31, 2^33): the
+        # smallest and largest codes inside it, and their neighbours outside
+        w_lo, w_hi = np.float32(2.0 ** -31), np.float32((2 - 2 ** -7) * 2.0 ** 32)
+        below, above = np.float32((2 - 2 ** -7) * 2.0 ** -32), np.float32(2.0 ** 33)
+        t[:, :, 0] = w_lo
+        t[:, :, 1] = -w_lo
+        t[:, :, 2] = below
+        d[:, :, 3] = -below
+        t[1, :, 4] = w_hi
+        d[2, 0, 5] = -w_hi
+        t[3, 2, 6] = above
+        d[4, 1, 7] = -above
     else:  # many +-0, and rows whose top-k cut falls on 0
         t[:, :, ::3] = 0.0
         t[:, :, 1::6] = -0.0
         t[3] = -np.abs(t[3])
         t[3, :, :100] = 0.0
     tb, db = workloads.to_bf16_bits(t), workloads.to_bf16_bits(d)
-    for T, top_k, top_p in [(1.0, 0, 0.9), (1.0, 50, 1.0), (0.7, 20, 0.8), (1.0, 0, 1.0)]:
+    settings = [(1.0, 0, 0.9), (1.0, 50, 1.0), (0.7, 20, 0.8), (1.0, 0, 1.0)]
+    if case == "tiny":
+        settings.append((0.05, 0, 0.9))  # a temperature at which tiny values' masses differ
+    for T, top_k, top_p in settings:
         toks = oracle.sample_drafts(db, rs.random((B, k)), T, top_k, top_p)
         u = rs.random((B, k + 1)).astype(np.float32)
         acc, out, ap = gpu_stochastic(tb, db, toks, u, T, top_k, top_p)
