@@ -375,12 +375,9 @@ struct StochasticRun {
     args.jobs = split ? jobs : nullptr;
     launch_tail<T, VEC>(B, args, st);
     if (split) {
-      hipLaunchKernelGGL((sv::k_draw_sums<T, VEC>), dim3(unsigned(L.draw_chunks), unsigned(B)),
+      hipLaunchKernelGGL((sv::k_draw_split<T, VEC>), dim3(unsigned(L.draw_chunks), unsigned(B)),
                          dim3(sv::kDrawThreads), 0, st, map, V, args.k, a, jobs, L.draw_chunks,
-                         dsums);
-      hipLaunchKernelGGL((sv::k_draw_pick<T, VEC>), dim3(unsigned(B)), dim3(sv::kDrawThreads), 0,
-                         st, map, V, args.k, a, jobs, L.draw_chunks, dsums, args.u,
-                         args.accepted_len, args.out_tokens);
+                         dsums, args.u, args.accepted_len, args.out_tokens);
     }
   }
 };

@@ -839,9 +839,9 @@ struct TailArgs {
   int32_t* accepted_len;
   int32_t* out_tokens;
   float* accept_prob;
-  // non-null: the correction draw is left to k_draw_sums / k_draw_pick; the
-  // tail writes each valid sequence's job and every output but the drawn
-  // token and the accepted length
+  // non-null: the correction draw is left to k_draw_split; the tail writes
+  // each valid sequence's job and every output but the drawn token and the
+  // accepted length
   DrawJob* jobs = nullptr;
 };
 
@@ -854,6 +854,21 @@ struct TailScratch {
 __device__ __forceinline__ double prob_at(float l, const RowStat& s, float a) {
   if (!(l >= s.thr)) return 0.0;
   return exp2_d(((double)l - (double)s.m) * (double)a) / s.z;
+}
+
+// Buffer descriptor of one aligned bf16 row's full 16-byte groups: the
+// streaming loads then take one 32-bit VGPR offset and a scalar offset per
+// load in flight, which keeps the address registers out of the way (a load
+// past the row's whole groups returns zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint16_t* row, int64_t V) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(row), (short)0,
+                                           (int)((V / 8) * 16), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 rsrc_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                             uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // Inverse-CDF draw in ascending vocabulary order from the normalised residual
@@ -878,7 +893,7 @@ __device__ __forceinline__ float log2_norm(double z) {
   return (float)((double)(e - 1) + (double)__builtin_amdgcn_logf((float)(2.0 * f)));
 }
 
-template <typename T, bool VEC, int NT, int U>
+template <typename T, bool VEC, int NT, int U, int PD = 0>
 __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const DrawStats sp,
                                  const DrawStats sq, float a, int64_t V, float u, double* csum,
                                  int32_t* emit_slot) {
@@ -950,23 +965,64 @@ __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const
     double cacc = 0.0;
     int ci = 0;
     int64_t cend = s0 + cs;
-    for (int64_t s = s0; s < s1; s += U) {
+    // this lane's values of step st (wave-uniform st) into the chunk sums
+    auto account = [&](int64_t st, double ls) {
+      cacc += ls;
+      if (st + 1 == cend || st + 1 == s1) {
+        const double tot = wave_sum(cacc);
+        if (lane == 0) csum[w * kDrawChunks + ci] = tot;
+        ++ci;
+        cacc = 0.0;
+        cend += cs;
+      }
+    };
+    int64_t s = s0;
+    if constexpr (PD > 0 && VEC && sizeof(T) == 2) {
+      // Aligned bf16 rows: a rolling window of PD steps in flight per wave
+      // (one 16-byte vector per lane and row each), refilled as each step
+      // is used, over the steps that lie wholly inside the row.
+      const int64_t sf = min(s1, V / 512);
+      const __amdgpu_buffer_rsrc_t rsp = row_rsrc(prow, V);
+      const __amdgpu_buffer_rsrc_t rsq = row_rsrc(qrow, V);
+      const uint32_t lo = (uint32_t)lane * 16u;
+      uint4 bp[PD], bq[PD];
+#pragma unroll
+      for (int d = 0; d < PD; ++d) {
+        if (s0 + d < sf) {
+          const uint32_t off = (uint32_t)(s0 + d) * 1024u + lo;
+          bp[d] = rsrc_load16(rsp, off, 0u);
+          if (resid) bq[d] = rsrc_load16(rsq, off, 0u);
+        }
+      }
+      for (; s < sf; s += PD) {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+          const int64_t st = s + d;
+          if (st < sf) {
+            Raw8<T> rp, rq;
+            rp.v[0] = bp[d];
+            rq.v[0] = resid ? bq[d] : bp[d];
+            if (st + PD < sf) {
+              const uint32_t off = (uint32_t)(st + PD) * 1024u + lo;
+              bp[d] = rsrc_load16(rsp, off, 0u);
+              if (resid) bq[d] = rsrc_load16(rsq, off, 0u);
+            }
+            float r8[8];
+            account(st, step_values(rp, rq, r8));
+          }
+        }
+      }
+      s = max(s0, sf);
+    }
+    // the remaining steps (all of them for other rows), U at a time
+    for (; s < s1; s += U) {
       Raw8<T> rp[U], rq[U];
       load_batch(s, rp, rq);
 #pragma unroll
       for (int v = 0; v < U; ++v) {
         float r8[8];
         const double ls = step_values(rp[v], rq[v], r8);
-        if (s + v < s1) {
-          cacc += ls;  // this lane's share of the chunk
-          if (s + v + 1 == cend || s + v + 1 == s1) {
-            const double tot = wave_sum(cacc);
-            if (lane == 0) csum[w * kDrawChunks + ci] = tot;
-            ++ci;
-            cacc = 0.0;
-            cend += cs;
-          }
-        }
+        if (s + v < s1) account(s + v, ls);  // this lane's share of the chunk
       }
     }
     block_sync_lds();
@@ -1077,18 +1133,19 @@ __device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const
 // Correction draw spread over the chip, for small batches on the row-pass
 // path (one tail workgroup per sequence would read the two rows at the stop
 // alone while the other CUs sit idle).  The tail writes each sequence's
-// DrawJob; k_draw_sums computes the residual's sum over every chunk of
+// DrawJob; k_draw_split computes the residual's sum over every chunk of
 // kDrawChunk elements of the two rows at the stop (one workgroup per
-// chunk); k_draw_pick finds the chunk where the running sum in ascending
-// vocabulary order passes u S, and the element inside it.  Both kernels
-// form a chunk's sum by the same additions (per-thread fp64 sums of fp32
-// group sums, then one block scan), so the chunk picked from the table
-// always holds the crossing.
+// chunk), and the workgroup that writes a sequence's last chunk sum finds
+// the chunk where the running sum in ascending vocabulary order passes u S,
+// and the element inside it.  A chunk's sum is formed by the same additions
+// both times (per-thread fp64 sums of fp32 group sums, then one block
+// scan), so the chunk picked from the table always holds the crossing.
 struct DrawJob {  // 48 bytes
   DrawStats sp, sq;  // processed target row at the stop, and draft row (unused for the bonus)
   int32_t n;         // the stop (k: the bonus draw from p_k)
   int32_t active;    // 0: nothing to draw (invalid sequence, outputs already written)
-  int32_t pad[2];
+  uint32_t done;     // chunk sums written so far (the last writer draws)
+  int32_t pad;
 };
 constexpr int kDrawThreads = 256;
 constexpr int kDrawGroups = 4;  // groups of 8 elements per thread
@@ -1175,43 +1232,33 @@ __device__ __forceinline__ double block_incl_scan256(double x, double* slots, do
   return base + inc;
 }
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_sums(RowMap map, int64_t V, int k, float a,
-                                                           const DrawJob* __restrict__ jobs,
-                                                           int64_t nch, double* __restrict__ sums) {
-  __shared__ double slots[kDrawThreads / kWave];
-  const int64_t b = blockIdx.y, c = blockIdx.x;
-  const DrawJob J = jobs[b];
-  if (!J.active) return;  // the sums of an inactive sequence stay zero
-  const bool resid = J.n < k;
-  const T* prow = map.template at<T>(b, J.n);
-  const T* qrow = resid ? map.template at<T>(b, k + 1 + J.n) : prow;
-  const float lzp = log2_norm(J.sp.z), lzq = resid ? log2_norm(J.sq.z) : 0.0f;
-  float gs[kDrawGroups];
-  const double x = draw_thread_sum<T, VEC>(prow, qrow, resid, J, lzp, lzq, a, V, c,
-                                           (int)threadIdx.x, gs);
-  double total;
-  (void)block_incl_scan256(x, slots, &total);
-  if (threadIdx.x == 0) sums[b * nch + c] = total;
+// Chunk sums pass between the workgroups of a sequence (on any XCD; the
+// XCDs' L2 caches are not coherent with one another) through atomic
+// read-modify-writes and atomic loads at device scope, without cache
+// flushes.
+__device__ __forceinline__ void sum_publish(double* p, double v) {
+  (void)__hip_atomic_exchange(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v),
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double sum_read(const double* p) {
+  return __builtin_bit_cast(double, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
+// The draw of sequence b from its chunk sums (one workgroup, after every
+// chunk sum is written); writes the emitted token and the accepted length,
+// then leaves the sequence's job and chunk sums zero for the next call.
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kDrawThreads) void k_draw_pick(RowMap map, int64_t V, int k, float a,
-                                                           DrawJob* __restrict__ jobs, int64_t nch,
-                                                           double* __restrict__ sums,
-                                                           const float* __restrict__ u,
-                                                           int32_t* __restrict__ accepted_len,
-                                                           int32_t* __restrict__ out_tokens) {
-  __shared__ double slots[kDrawThreads / kWave];
+__device__ void draw_pick(RowMap map, int64_t V, int k, float a, DrawJob* __restrict__ jobs,
+                          int64_t nch, double* __restrict__ sums, const float* __restrict__ u,
+                          int32_t* __restrict__ accepted_len, int32_t* __restrict__ out_tokens,
+                          int64_t b, const DrawJob& J, double* slots) {
   __shared__ int32_t emit;
   __shared__ int64_t sh_chunk;
   __shared__ double sh_target, sh_S;
   __shared__ int32_t sh_last, sh_pick;
   __shared__ uint64_t sh_hits[kDrawThreads / kWave], sh_pos[kDrawThreads / kWave];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  const int64_t b = blockIdx.x;
-  const DrawJob J = jobs[b];
-  if (!J.active) return;
   const int n = J.n;
   bool resid = n < k;
   const T* prow = map.template at<T>(b, n);
@@ -1226,7 +1273,7 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick(RowMap map, int64_t 
   if (w == 0) {
     double carry = 0.0;
     for (int64_t base = 0; base < nch; base += kWave)
-      carry += wave_sum(base + lane < nch ? sb[base + lane] : 0.0);
+      carry += wave_sum(base + lane < nch ? sum_read(sb + base + lane) : 0.0);
     if (lane == 0) sh_S = carry;
   }
   block_sync_lds();
@@ -1237,10 +1284,10 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick(RowMap map, int64_t 
       const double x = draw_thread_sum<T, VEC>(prow, qrow, false, J, lzp, lzq, a, V, c, tid, gs);
       double total;
       (void)block_incl_scan256(x, slots, &total);
-      if (tid == 0) sb[c] = total;
+      if (tid == 0) sum_publish(sb + c, total);
       block_sync_lds();  // slots are rewritten by the next chunk's scan
     }
-    __syncthreads();  // the new sums (global memory) visible to wave 0
+    __syncthreads();
   }
 
   // Wave 0: S, the target u S, and the first chunk whose running sum
@@ -1248,12 +1295,12 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick(RowMap map, int64_t 
   if (w == 0) {
     double carry = 0.0;
     for (int64_t base = 0; base < nch; base += kWave)
-      carry += wave_sum(base + lane < nch ? sb[base + lane] : 0.0);
+      carry += wave_sum(base + lane < nch ? sum_read(sb + base + lane) : 0.0);
     const double S = carry, target = (double)uu * S;
     int64_t pick = -1, lastpos = -1;
     double before = 0.0, before_last = 0.0, run = 0.0;
     for (int64_t base = 0; base < nch && pick < 0; base += kWave) {
-      const double x = base + lane < nch ? sb[base + lane] : 0.0;
+      const double x = base + lane < nch ? sum_read(sb + base + lane) : 0.0;
       const double inc = wave_incl_scan(x) + run;
       const uint64_t hit = __ballot(base + lane < nch && inc > target);
       const uint64_t pos = __ballot(base + lane < nch && x > 0.0);
@@ -1341,6 +1388,43 @@ __global__ __launch_bounds__(kDrawThreads) void k_draw_pick(RowMap map, int64_t 
   if (tid < (int)(sizeof(DrawJob) / 4)) reinterpret_cast<int32_t*>(jobs + b)[tid] = 0;
 }
 
+// One workgroup per (chunk, sequence): the chunk's sum; the last of a
+// sequence's workgroups to write its sum then draws the token.
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kDrawThreads) void k_draw_split(RowMap map, int64_t V, int k, float a,
+                                                            DrawJob* __restrict__ jobs, int64_t nch,
+                                                            double* __restrict__ sums,
+                                                            const float* __restrict__ u,
+                                                            int32_t* __restrict__ accepted_len,
+                                                            int32_t* __restrict__ out_tokens) {
+  __shared__ double slots[kDrawThreads / kWave];
+  __shared__ int32_t sh_is_last;
+  const int64_t b = blockIdx.y, c = blockIdx.x;
+  const DrawJob J = jobs[b];
+  if (!J.active) return;  // outputs already written; job and sums stay zero
+  const bool resid = J.n < k;
+  const T* prow = map.template at<T>(b, J.n);
+  const T* qrow = resid ? map.template at<T>(b, k + 1 + J.n) : prow;
+  const float lzp = log2_norm(J.sp.z), lzq = resid ? log2_norm(J.sq.z) : 0.0f;
+  float gs[kDrawGroups];
+  const double x = draw_thread_sum<T, VEC>(prow, qrow, resid, J, lzp, lzq, a, V, c,
+                                           (int)threadIdx.x, gs);
+  double total;
+  (void)block_incl_scan256(x, slots, &total);
+  if (threadIdx.x == 0) {
+    sum_publish(sums + b * nch + c, total);
+    // the exchange has completed before the count goes up: a workgroup that
+    // sees the count at nch - 1 finds every chunk's sum in place
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint32_t prev = __hip_atomic_fetch_add(&jobs[b].done, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    sh_is_last = prev + 1u == (uint32_t)nch ? 1 : 0;
+  }
+  block_sync_lds();
+  if (!sh_is_last) return;
+  draw_pick<T, VEC>(map, V, k, a, jobs, nch, sums, u, accepted_len, out_tokens, b, J, slots);
+}
+
 __device__ __forceinline__ void write_draw_job(DrawJob* job, const DrawStats& sp, const DrawStats& sq,
                                                int n) {
   DrawJob J;
@@ -1348,7 +1432,8 @@ __device__ __forceinline__ void write_draw_job(DrawJob* job, const DrawStats& sp
   J.sq = sq;
   J.n = n;
   J.active = 1;
-  J.pad[0] = J.pad[1] = 0;
+  J.done = 0u;
+  J.pad = 0;
   *job = J;
 }
 
@@ -1504,7 +1589,7 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   const T* prow = A.map.at<T>(b, n);
   const T* qrow = has_q ? A.map.at<T>(b, k + 1 + n) : prow;
   const int32_t emitted =
-      residual_draw<T, VEC, NT, sizeof(T) == 2 ? 4 : 2>(prow, qrow, has_q, draw_stats(TS.st[n]),
+      residual_draw<T, VEC, NT, sizeof(T) == 2 ? 4 : 2, 4>(prow, qrow, has_q, draw_stats(TS.st[n]),
                                 draw_stats(has_q ? TS.st[k + 1 + n] : TS.st[n]), a, V,
                                 A.u[b * (k + 1) + k], TS.csum, &TS.emit);
   for (int j = tid; j <= k; j += NT) {
@@ -1532,12 +1617,11 @@ __global__ __launch_bounds__(512) void k_tail(TailArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent bf16 filter: one 1024-thread workgroup per CU walks its rows
-// (XCD-aware: the workgroups of XCD x take the rows of one contiguous range,
-// so a sequence's rows are read by one XCD close together in time).  While a
-// row's histogram is scanned, the first PF vectors per thread of the next row
-// are already loading (the scan's barriers order LDS only, so they do not
-// wait for those loads).
+// Arguments of the persistent bf16 filter (sv_window.hpp), and the row
+// streaming of the kernels that keep a row's histogram in LDS: while a row's
+// histogram is scanned, the first PF vectors per thread of the next row are
+// already loading (the scan's barriers order LDS only, so they do not wait
+// for those loads).
 struct FilterArgs {
   RowMap map;
   int64_t V;
@@ -1547,20 +1631,6 @@ struct FilterArgs {
   float top_p;
   RowStat* stats;
 };
-
-// Buffer descriptor of one aligned bf16 row's full 16-byte groups: the
-// streaming loads then take one 32-bit VGPR offset and a scalar offset per
-// load in flight, which keeps the address registers out of the way.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint16_t* row, int64_t V) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(row), (short)0,
-                                           (int)((V / 8) * 16), 0x00020000);
-}
-
-__device__ __forceinline__ uint4 rsrc_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
-                                             uint32_t soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)soff, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
 
 // Streams one aligned bf16 row into the (cleared) histogram, D 16-byte loads
 // in flight per thread; the first PF vectors of each thread come from `pf`
@@ -1629,40 +1699,6 @@ __device__ __forceinline__ void prefetch_row(uint4 (&pf)[PF], const uint16_t* ro
   for (int j = 0; j < PF; ++j) {
     const uint32_t g = tid + (uint32_t)j * 1024u;
     if (g < nfull) pf[j] = rsrc_load16(rs, tid * 16u, (uint32_t)j * 16384u);
-  }
-}
-
-template <bool VEC, int PF, int D>
-__global__ __launch_bounds__(1024) void k_filter_bf16_persistent(FilterArgs F) {
-  static_assert(VEC, "aligned rows only");
-  constexpr int NT = 1024;
-  __shared__ uint32_t hist[32768];
-  __shared__ HistScratch S;
-  const int nwg = gridDim.x;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int per_xcd = nwg >> 3;  // nwg is a multiple of 8
-  const int64_t rx = (F.R + 7) / 8;
-  const int64_t r_lo = (int64_t)xcd * rx, r_hi = min(F.R, r_lo + rx);
-  const int64_t V = F.V;
-
-  uint4 pf[PF];
-  int64_t r = r_lo + slot;
-  if (r < r_hi) prefetch_row(pf, F.map.template row<uint16_t>(r), V);
-  hist_clear(hist);  // afterwards each row's scan leaves the histogram zero
-  for (; r < r_hi; r += per_xcd) {
-    const uint16_t* row = F.map.template row<uint16_t>(r);
-    block_sync_lds();
-    hist_count_stream<PF, D>(hist, row, V, pf, true);
-    block_sync_lds();
-    // the next row's first vectors land while this row's histogram is scanned
-    if (r + per_xcd < r_hi) prefetch_row(pf, F.map.template row<uint16_t>(r + per_xcd), V);
-    if (hist_row_stats(hist, S, V, F.a, F.top_k, F.top_p, F.stats + r) == 2) {
-      block_sync_lds();
-      filter_row_bisect_call<uint16_t, VEC, NT>(row, V, F.a, F.top_k, F.top_p, F.stats + r,
-                                                 S.dslot, S.uslot);
-      block_sync_lds();
-      hist_clear(hist);
-    }
   }
 }
 
@@ -1786,12 +1822,13 @@ __device__ __noinline__ int help_resolve(uint64_t* ent, uint64_t prev, uint32_t 
 
 // Out of line, with scalar arguments, so that its registers do not burden
 // the walk's streaming loop.
+template <int U = 2, int PD = 0>
 __device__ __forceinline__ int32_t residual_draw_call(const uint16_t* prow, const uint16_t* qrow,
                                                    bool has_q, float pm, float pthr, double pz,
                                                    float qm, float qthr, double qz, float a,
                                                    int64_t V, float u, double* csum,
                                                    int32_t* emit_slot) {
-  return residual_draw<uint16_t, true, 1024, 2>(prow, qrow, has_q, DrawStats{pm, pthr, pz},
+  return residual_draw<uint16_t, true, 1024, U, PD>(prow, qrow, has_q, DrawStats{pm, pthr, pz},
                                              DrawStats{qm, qthr, qz}, a, V, u, csum, emit_slot);
 }
 

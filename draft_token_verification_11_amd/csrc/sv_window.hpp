@@ -42,10 +42,12 @@ struct WinScratch {
   uint32_t lcnt[kWinListMax];  // count of entry i
   float gmass[kWinListMax];    // mass of entry i (first kTop entries)
   uint32_t side[8];            // side counters (kSides used)
-  uint32_t wcount[8];
+  uint32_t wcount[16];
   double dslot[16];
   uint32_t uslot[16];
-  uint32_t tk, tk_entry, fallback;
+  uint32_t tk, tk_entry, fallback, nl;
+  float m;      // the row's max logit, between the two parts of the scan
+  float top_p;  // the call's top_p, set once by the kernel: read from LDS at the cut
   RowStat res;
 };
 
@@ -63,11 +65,17 @@ __device__ __forceinline__ uint32_t win_ent_key(uint32_t ent, uint32_t j) {
   return ent == kEntZero ? kKey16PosZero : kKey16NegInf;
 }
 
+template <int NT>
 __device__ __forceinline__ void win_clear(uint32_t* hist, uint32_t* side) {
   uint4* h4 = reinterpret_cast<uint4*>(hist);
-  for (int i = opaque_tid(); i < kWinWords / 4; i += kWinThreads) h4[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = opaque_tid(); i < kWinWords / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
   if (opaque_tid() < 8) side[opaque_tid()] = 0u;
 }
+
+// Zeroes the groups on S's list and the side counters (threads 0..NT-1 of
+// those calling, index t).
+template <int NT>
+__device__ __forceinline__ void win_clear_listed(uint32_t* hist, WinScratch& S, int t);
 
 __device__ __forceinline__ void win_inc(uint32_t* hist, uint32_t byte_off) {
   atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(hist) + byte_off), 1u);
@@ -120,10 +128,10 @@ __device__ __forceinline__ void win_add8(uint32_t* hist, uint32_t* side, uint4 v
 // Streams one aligned bf16 row into the (cleared) window histogram, D 16-byte
 // loads in flight per thread; the first PF vectors of each thread come from
 // `pf` when pf_ok (prefetched during the previous row's scan).
-template <int PF, int D>
+template <int PF, int D, int NTH>
 __device__ __forceinline__ void win_count_stream(uint32_t* hist, uint32_t* side, const uint16_t* row,
                                                  int64_t V, const uint4 (&pf)[PF], bool pf_ok) {
-  constexpr uint32_t NT = kWinThreads;
+  constexpr uint32_t NT = NTH;
   uint32_t tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const uint32_t nfull = (uint32_t)(V / 8);
@@ -172,7 +180,7 @@ __device__ __forceinline__ void win_count_stream(uint32_t* hist, uint32_t* side,
   }
 }
 
-template <int PF>
+template <int PF, int NT>
 __device__ __forceinline__ void win_prefetch_row(uint4 (&pf)[PF], const uint16_t* row, int64_t V) {
   const uint32_t nfull = (uint32_t)(V / 8);
   const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, V);
@@ -180,65 +188,96 @@ __device__ __forceinline__ void win_prefetch_row(uint4 (&pf)[PF], const uint16_t
   asm volatile("" : "+v"(tid));
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
-    const uint32_t g = tid + (uint32_t)j * kWinThreads;
-    if (g < nfull) pf[j] = rsrc_load16(rs, tid * 16u, (uint32_t)j * kWinThreads * 16u);
+    const uint32_t g = tid + (uint32_t)j * NT;
+    if (g < nfull) pf[j] = rsrc_load16(rs, tid * 16u, (uint32_t)j * NT * 16u);
   }
 }
 
-// Row statistics from a filled window histogram (all 512 threads).  Returns 0
-// on success (RowStat in S.res and, if given, *out), 1 for an invalid row
-// (written), 2 when the row needs the exact bisection path (nothing written;
-// the histogram is left as it is for the caller to clear).  Leaves the
-// histogram and side counters zero when it returns 0 or 1.
-__device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int64_t V, float a,
-                                             int top_k, float top_p, RowStat* out) {
-  constexpr int NT = kWinThreads;
+template <int NT>
+__device__ __forceinline__ void win_clear_listed(uint32_t* hist, WinScratch& S, int t) {
+  uint4* h4 = reinterpret_cast<uint4*>(hist);
+  const uint32_t nl = S.nl;
+  for (uint32_t i = (uint32_t)t >> 4; i < nl; i += NT / 16) {
+    const uint32_t e = S.list[i];
+    if (e < (uint32_t)kWinGroups) {
+      const uint32_t sg = e >= 128u ? e - 128u : 255u - e;
+      h4[sg * 16u + ((uint32_t)t & 15u)] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  if (t < 8) S.side[t] = 0u;
+}
+
+// Row statistics from a filled window histogram (S.top_p must hold top_p),
+// every thread of the NT-thread workgroup, in two parts.  win_stats_list
+// builds the list of non-empty entries and finds the max and the top-k key;
+// win_stats_mass then computes the masses, the normaliser and the top-p
+// cut.  Between the two, the row's figures live in S.  Results: 0 success
+// (RowStat in S.res and, if given, *out), 1 invalid row (written), 2 the row
+// needs the exact bisection path (nothing written; the histogram is left as
+// it is for the caller to clear).  The histogram and side counters are left
+// zero after 0 or 1.
+template <int NT>
+__device__ __forceinline__ int win_stats_list(uint32_t* hist, WinScratch& S, int64_t V, float a,
+                                              int top_k, RowStat* out) {
+  static_assert(NT == 512 || NT == 1024, "two or four threads per key group");
+  constexpr int NW = NT / kWave;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & (kWave - 1);
   const int wv = tid / kWave;
   const bool use_k = top_k > 0 && (int64_t)top_k < V;
-  const bool use_p = top_p < 1.0f;
-
-  // Totals of key-ordered group kg = 255 - tid/2, half tid&1 each (8
-  // rotated 16-byte reads); the two halves meet by a lane swap.  Waves 0..3
-  // hold the positive groups (descending), waves 4..7 the negative ones.
-  const uint32_t gi = (uint32_t)tid >> 1;
-  const uint32_t kg = 255u - gi;
-  uint32_t cnt = 0;
-  {
-    const uint32_t sg = kg >= 128u ? kg - 128u : 255u - kg;
-    const uint4* h4 = reinterpret_cast<const uint4*>(hist) + sg * 16u + ((uint32_t)tid & 1u) * 8u;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint4 w = h4[(j + gi) & 7u];
-      cnt += w.x + w.y + w.z + w.w;
-    }
-    cnt += (uint32_t)__builtin_amdgcn_mov_dpp((int)cnt, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-  }
   const uint32_t s_zero = S.side[kSideZero], s_ninf = S.side[kSideNegInf];
   const uint32_t s_bad = S.side[kSideBad], s_huge = S.side[kSideHuge];
   const uint32_t s_tneg = S.side[kSideTinyNeg], s_tpos = S.side[kSideTinyPos];
   const uint32_t tiny = s_tneg + s_tpos;
   const uint32_t zcnt = s_zero + tiny;  // the zero entry: zeros and tiny values
-  const bool own = (tid & 1) == 0 && cnt != 0;
-  const uint64_t ball = __ballot(own);
-  if (lane == 0) S.wcount[wv] = (uint32_t)__popcll(ball);
-  block_sync_lds();
-  uint32_t off = 0, npos = 0, nwin = 0;
-#pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const uint32_t c = S.wcount[v];
-    if (v < wv) off += c;
-    if (v < 4) npos += c;
-    nwin += c;
-  }
   const uint32_t nz = zcnt != 0u ? 1u : 0u;
-  if (own) {
-    const uint32_t pos = off + (wv >= 4 ? nz : 0u) + (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
-    S.list[pos] = (uint16_t)kg;
-    S.lcnt[pos] = cnt;
+  auto gsum = [&](uint32_t kg, uint32_t first, uint32_t R, uint32_t rot) -> uint32_t {
+    // R of the 16 16-byte words of key-ordered group kg, from `first`, rotated
+    const uint32_t sg = kg >= 128u ? kg - 128u : 255u - kg;
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist) + sg * 16u + first;
+    uint32_t c = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < R; ++j) {
+      const uint4 w = h4[(j + rot) % R];
+      c += w.x + w.y + w.z + w.w;
+    }
+    return c;
+  };
+
+  // The list of non-empty entries in descending key order: positive window
+  // groups (kg 255..128), the zero entry, negative groups (127..0), -inf.
+  uint32_t npos = 0, nwin = 0;
+  {
+    // the TPG threads of key-ordered group kg = 255 - tid/TPG take a share
+    // each, met by lane swaps; the first half of the waves holds the positive
+    // groups (descending), the second half the negative ones
+    constexpr uint32_t TPG = NT / kWinGroups;
+    const uint32_t gi = (uint32_t)tid / TPG;
+    uint32_t cnt = gsum(255u - gi, ((uint32_t)tid % TPG) * (16u / TPG), 16u / TPG, gi);
+    cnt += (uint32_t)__builtin_amdgcn_mov_dpp((int)cnt, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    if (TPG == 4)
+      cnt += (uint32_t)__builtin_amdgcn_mov_dpp((int)cnt, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    const bool own = (uint32_t)tid % TPG == 0u && cnt != 0;
+    const uint64_t ball = __ballot(own);
+    if (lane == 0) S.wcount[wv] = (uint32_t)__popcll(ball);
+    block_sync_lds();
+    uint32_t off = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const uint32_t c = S.wcount[v];
+      if (v < wv) off += c;
+      if (v < NW / 2) npos += c;
+      nwin += c;
+    }
+    if (own) {
+      const uint32_t pos =
+          off + (wv >= NW / 2 ? nz : 0u) + (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
+      S.list[pos] = (uint16_t)(255u - gi);
+      S.lcnt[pos] = cnt;
+    }
   }
+  const uint32_t nl = nwin + nz + (s_ninf ? 1u : 0u);
   if (tid == 0) {
     if (nz) {
       S.list[npos] = kEntZero;
@@ -248,9 +287,9 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
       S.list[nwin + nz] = kEntNegInf;
       S.lcnt[nwin + nz] = s_ninf;
     }
+    S.nl = nl;
     S.fallback = 0u;
   }
-  const uint32_t nl = nwin + nz + (s_ninf ? 1u : 0u);
   block_sync_lds();
 
   auto kcount = [&](uint32_t ent, uint32_t j) -> uint32_t {
@@ -258,33 +297,21 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
     if (j != 0u) return 0u;
     return ent == kEntZero ? zcnt : s_ninf;
   };
-  auto clear_listed = [&]() {
-    uint4* h4 = reinterpret_cast<uint4*>(hist);
-    for (uint32_t i = (uint32_t)tid >> 4; i < nl; i += NT / 16) {
-      const uint32_t e = S.list[i];
-      if (e < (uint32_t)kWinGroups) {
-        const uint32_t sg = e >= 128u ? e - 128u : 255u - e;
-        h4[sg * 16u + ((uint32_t)tid & 15u)] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    if (tid < 8) S.side[tid] = 0u;
-  };
-  auto invalid = [&]() {
+  // NaN/+inf, or no finite logit (finite values outside the window count)
+  if (s_bad || ((nl == 0u || S.list[0] == kEntNegInf) && s_huge == 0u)) {
     if (tid == 0) {
       RowStat st = {__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
       S.res = st;
       if (out) *out = st;
     }
     block_sync_lds();
-    clear_listed();
+    win_clear_listed<NT>(hist, S, tid);
     return 1;
-  };
-  if (s_bad) return invalid();
+  }
   // huge finite values, or tiny ones whose exponentials at this temperature
   // would not all equal 2^(-m a): the exact path
   if (s_huge || (tiny && a > 16.0f)) return 2;
   const uint32_t e0 = S.list[0];
-  if (nl == 0u || e0 == kEntNegInf) return invalid();  // no finite logit
   uint32_t max_key;
   if (e0 == kEntZero) {
     if (s_tpos || !s_zero) return 2;  // the max is a tiny value
@@ -293,14 +320,14 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
     const uint64_t nzm = __ballot(kcount(e0, (uint32_t)lane) != 0u);
     max_key = win_key(e0, 63u - (uint32_t)__clzll((long long)nzm));
   }
-  const float m = value_of_key16(max_key);
 
-  // Wave 0, with top-k: the top-k key by exact counts.
+  // Wave 0 (or the one wave): the max, and with top-k the top-k key by exact counts.
+  if (wv == 0 && lane == 0) {
+    S.m = value_of_key16(max_key);
+    S.tk = 0;
+    S.tk_entry = nl - 1;
+  }
   if (use_k && wv == 0) {
-    if (lane == 0) {
-      S.tk = 0;
-      S.tk_entry = nl - 1;
-    }
     uint32_t carry = 0;
     for (uint32_t base = 0; base < nl; base += kWave) {
       const uint32_t x = (base + lane < nl) ? S.lcnt[base + lane] : 0u;
@@ -323,12 +350,33 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
       carry = bcast(inc, kWave - 1);
     }
   }
-  if (use_k) {
-    block_sync_lds();
-    if (S.fallback) return 2;
-  }
-  const uint32_t tk = use_k ? S.tk : 0u;
-  const uint32_t last = use_k ? S.tk_entry : nl - 1;
+  block_sync_lds();
+  return S.fallback ? 2 : 0;
+}
+
+// The second part (every thread of the NT-thread workgroup), after
+// win_stats_list returned 0 for this histogram and S.
+template <int NT>
+__device__ __forceinline__ int win_stats_mass(uint32_t* hist, WinScratch& S, int64_t V, float a,
+                                              int top_k, float top_p, RowStat* out) {
+  constexpr int NW = NT / kWave;
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & (kWave - 1);
+  const int wv = tid / kWave;
+  const bool use_k = top_k > 0 && (int64_t)top_k < V;
+  const bool use_p = top_p < 1.0f;
+  const uint32_t zcnt = S.side[kSideZero] + S.side[kSideTinyNeg] + S.side[kSideTinyPos];
+  const uint32_t tiny = S.side[kSideTinyNeg] + S.side[kSideTinyPos];
+  const uint32_t s_ninf = S.side[kSideNegInf];
+  const float m = S.m;
+  const uint32_t tk = S.tk;
+  const uint32_t last = S.tk_entry;
+  auto kcount = [&](uint32_t ent, uint32_t j) -> uint32_t {
+    if (ent < (uint32_t)kWinGroups) return hist[win_idx(win_key(ent, j))];
+    if (j != 0u) return 0u;
+    return ent == kEntZero ? zcnt : s_ninf;
+  };
 
   // Masses over keys >= tk, one wave per entry; the first kTop entries keep
   // their totals for the cut.
@@ -338,7 +386,7 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
     return key >= tk ? key_mass(key, kcount(ent, j), m, a) : 0.0f;
   };
   float acc = 0.0f;
-  for (uint32_t i = (uint32_t)wv; i <= last; i += NT / kWave) {
+  for (uint32_t i = (uint32_t)wv; i <= last; i += NW) {
     const float e = emass(S.list[i], (uint32_t)lane);
     acc += e;
     if (i < kTop) {
@@ -356,14 +404,14 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
   if (wv == 0) {
     double zk = 0.0;
 #pragma unroll
-    for (int v = 0; v < NT / kWave; ++v) zk += S.dslot[v];
+    for (int v = 0; v < NW; ++v) zk += S.dslot[v];
     uint32_t thr_key = tk;
     double z = zk;
     bool fb = false;
     if (use_p) {
-      float tp = top_p;
-      asm volatile("" : "+v"(tp));
-      const double target = (double)tp * zk;
+      // top_p comes from LDS here: a register copy held across the scan
+      // would be spilled, and its reload would wait for the loads in flight
+      const double target = (double)S.top_p * zk;
       double carry = 0.0;
       for (uint32_t base = 0; base <= last; base += kWave) {
         const bool in = base + lane <= last;
@@ -425,8 +473,16 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
   }
   block_sync_lds();
   if (S.fallback) return 2;
-  clear_listed();
+  win_clear_listed<NT>(hist, S, tid);
   return 0;
+}
+
+// Both parts, every thread of the NT-thread workgroup.
+template <int NT>
+__device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int64_t V, float a,
+                                             int top_k, float top_p, RowStat* out) {
+  const int r = win_stats_list<NT>(hist, S, V, a, top_k, out);
+  return r != 0 ? r : win_stats_mass<NT>(hist, S, V, a, top_k, top_p, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -449,20 +505,21 @@ void k_filter_win_persistent(FilterArgs F) {
 
   uint4 pf[PF];
   int64_t r = r_lo + slot;
-  if (r < r_hi) win_prefetch_row(pf, F.map.template row<uint16_t>(r), V);
-  win_clear(hist, S.side);  // afterwards each row's scan leaves the histogram zero
+  if (threadIdx.x == 0) S.top_p = F.top_p;
+  if (r < r_hi) win_prefetch_row<PF, kWinThreads>(pf, F.map.template row<uint16_t>(r), V);
+  win_clear<kWinThreads>(hist, S.side);  // afterwards each row's scan leaves the histogram zero
   for (; r < r_hi; r += per_xcd) {
     const uint16_t* row = F.map.template row<uint16_t>(r);
     block_sync_lds();
-    win_count_stream<PF, D>(hist, S.side, row, V, pf, true);
+    win_count_stream<PF, D, kWinThreads>(hist, S.side, row, V, pf, true);
     block_sync_lds();
-    if (r + per_xcd < r_hi) win_prefetch_row(pf, F.map.template row<uint16_t>(r + per_xcd), V);
-    if (win_row_stats(hist, S, V, F.a, F.top_k, F.top_p, F.stats + r) == 2) {
+    if (r + per_xcd < r_hi) win_prefetch_row<PF, kWinThreads>(pf, F.map.template row<uint16_t>(r + per_xcd), V);
+    if (win_row_stats<kWinThreads>(hist, S, V, F.a, F.top_k, F.top_p, F.stats + r) == 2) {
       block_sync_lds();
       filter_row_bisect_call<uint16_t, true, kWinThreads>(row, V, F.a, F.top_k, F.top_p,
                                                            F.stats + r, S.dslot, S.uslot);
       __syncthreads();
-      win_clear(hist, S.side);
+      win_clear<kWinThreads>(hist, S.side);
     }
   }
 }

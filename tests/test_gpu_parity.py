@@ -361,7 +361,8 @@ def test_bf16_histogram_overflow_falls_back():
 @pytest.mark.parametrize("case", ["tiny", "huge", "edges", "edges31", "zeros"])
 def test_bf16_window_edges(case):
     """Extreme bf16 codes: many +-0 (and top-k cuts that fall on 0), non-zero
-    magnitudes below 2^-63, values of 2^65 and above (one-hot rows), the codes
+    magnitudes below 2^-63, values of 2^65 and above (one-hot rows), rows
+    whose finite values all lie above the filter's exponent window, the codes
     2^-63 and (2 - 2^-7) 2^64 in rows of ordinary logits, and both ends of the
     row filter's exponent window [2^-31, 2^33) with their neighbours outside
     it (rows outside the window, or decisions among tiny values, take the
@@ -380,6 +381,10 @@ def test_bf16_window_edges(case):
         d[1, 0, 4] = -5e20
         t[2, 2, 5] = np.float32(2.0 ** 65)
         t[3, 0, 6] = -np.float32(2.0 ** 65)
+        # rows whose finite values all lie above the window, some -inf
+        t[4, 1] = t[4, 1] * np.float32(2.0 ** 40)
+        t[4, 1, ::7] = -np.inf
+        d[5, 2] = d[5, 2] * np.float32(2.0 ** 36)
     elif case == "edges":
         t[:, :, 0] = lo
         t[:, :, 1] = -lo

@@ -98,6 +98,52 @@ def test_walk_extreme_k():
         assert ref["accepted_len"].max() >= k // 2
 
 
+def test_walk_window_edges():
+    """Extreme bf16 codes in both whole-sequence kernels: many +-0 and top-k
+    cuts that fall on 0, tiny and huge values among ordinary logits, rows
+    whose finite values are all huge, and both ends of the row filter's
+    exponent window [2^-31, 2^33) with their neighbours outside it."""
+    rs = np.random.default_rng(53)
+    B, k, V = _batch(), 3, 1000
+    w_lo, w_hi = np.float32(2.0 ** -31), np.float32((2 - 2 ** -7) * 2.0 ** 32)
+    below, above = np.float32((2 - 2 ** -7) * 2.0 ** -32), np.float32(2.0 ** 33)
+    for T, top_k, top_p in [(1.0, 0, 0.9), (0.7, 20, 0.8), (1.0, 50, 1.0)]:
+        t = rs.normal(0, 2, (B, k + 1, V)).astype(np.float32)
+        d = (t[:, :k] + rs.normal(0, 0.7, (B, k, V))).astype(np.float32)
+        for b in range(0, 20):  # many zeros
+            t[b, :, ::3] = 0.0
+            t[b, :, 1::6] = -0.0
+        for b in range(20, 40):  # non-positive rows: top-k cuts on 0
+            t[b] = -np.abs(t[b])
+            t[b, :, :100] = 0.0
+            d[b] = -np.abs(d[b])
+            d[b, :, :60] = 0.0
+        for b in range(40, 60):  # tiny values
+            t[b, :, :5] = 1e-25
+            d[b, 0, 7] = -3e-30
+        for b in range(60, 80):  # huge values among ordinary ones
+            t[b, 1, 3] = 1e25
+            d[b, 0, 4] = -5e20
+        for b in range(80, 100):  # every finite value huge, some -inf
+            t[b, 0] = t[b, 0] * np.float32(2.0 ** 40)
+            t[b, 0, ::7] = -np.inf
+            if b < 90:
+                d[b, 0] = d[b, 0] * np.float32(2.0 ** 40)
+        for b in range(100, 120):  # the window's ends and their outside neighbours
+            t[b, :, 0] = w_lo
+            t[b, :, 1] = -w_lo
+            t[b, :, 2] = below
+            d[b, :, 3] = -below
+            t[b, 1, 4] = w_hi
+            d[b, 0, 5] = -w_hi
+            t[b, 2, 6] = above
+            d[b, 1, 7] = -above
+        tb, db = workloads.to_bf16_bits(t), workloads.to_bf16_bits(d)
+        toks = oracle.sample_drafts(db, rs.random((B, k)), T, top_k, top_p)
+        u = rs.random((B, k + 1)).astype(np.float32)
+        _check(tb, db, toks, u, T, top_k, top_p, "window edges T=%g k=%d p=%g" % (T, top_k, top_p))
+
+
 def test_walk_ill_formed_positions():
     """Invalid rows and tokens count where the walk consults them."""
     rs = np.random.default_rng(47)
