@@ -541,7 +541,42 @@ def headline_extras(c, args, sv, torch, dev, stream, sets, step, acc, out, timer
         next_rows["lmhead_greedy_B%d" % Bl] = r
         log("  fused LM head + greedy (B=%d, k=8, d=%d): %.4f ms, unfused %.4f ms"
             % (Bl, d, r["fused_ms"], r["unfused_bf16_matmul_then_verify_ms"]))
-        del Wh, Wt, Hd
+        # The stochastic rule has no fused kernel: what such a kernel would
+        # have to beat is the two heads' products (target rows from the
+        # target's head, draft rows from a head of the draft model's own)
+        # followed by the stochastic verify over the logits they produce.
+        Wd = (torch.randn((c.V, d), device=dev, generator=gh) / d ** 0.5).to(torch.bfloat16)
+        Wdt = Wd.t().contiguous()
+        Hq = torch.randn((Bl, 8, d), device=dev, generator=gh).to(torch.bfloat16)
+        su = torch.rand((Bl, 9), device=dev, generator=gh)
+        stok = torch.randint(0, c.V, (Bl, 8), device=dev, generator=gh, dtype=torch.int32)
+        sws = torch.zeros(sv.workspace_size(sv.SPEC_OP_STOCHASTIC, Bl, 8, c.V, 0.7),
+                          dtype=torch.uint8, device=dev)
+        tl = torch.empty((Bl, 9, c.V), dtype=torch.bfloat16, device=dev)
+        dl = torch.empty((Bl, 8, c.V), dtype=torch.bfloat16, device=dev)
+
+        def products(i):
+            torch.matmul(Hd.reshape(-1, d), Wt, out=tl.view(-1, c.V))
+            torch.matmul(Hq.reshape(-1, d), Wdt, out=dl.view(-1, c.V))
+
+        def verify_only(i):
+            sv.verify_stochastic(tl, dl, stok, su, temperature=0.7, workspace=sws, stream=stream)
+
+        def unfused_s(i):
+            products(i)
+            verify_only(i)
+
+        rs_ = {"B": Bl, "k": 8, "d": d, "V": c.V, "temperature": 0.7,
+               "two_bf16_matmuls_ms": timer.ms(products, args.steps, 1),
+               "verify_stochastic_ms": timer.ms(verify_only, args.steps, 1),
+               "unfused_total_ms": timer.ms(unfused_s, args.steps, 1)}
+        # the bytes such a fused kernel could not avoid: both heads once
+        rs_["heads_bytes"] = 2 * c.V * d * 2
+        rs_["floor_ms_at_peak_hbm"] = rs_["heads_bytes"] / (PEAK_HBM_GBPS * 1e9) * 1e3
+        next_rows["lmhead_stochastic_unfused_B%d" % Bl] = rs_
+        log("  stochastic LM head, unfused (B=%d): products %.4f ms + verify %.4f ms = %.4f ms"
+            % (Bl, rs_["two_bf16_matmuls_ms"], rs_["verify_stochastic_ms"], rs_["unfused_total_ms"]))
+        del Wh, Wt, Hd, Wd, Wdt, Hq, tl, dl
     log("  logits_apply over %d rows: %.4f ms = %.0f GB/s; outcome lookup: %d hits of %d planted"
         % (c.B * (2 * c.k + 1), ms_a, next_rows["logits_apply"]["achieved_GBps"],
            next_rows["outcome_lookup"]["hits"], next_rows["outcome_lookup"]["planted"]))
