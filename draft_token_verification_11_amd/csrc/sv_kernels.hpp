@@ -894,7 +894,7 @@ __device__ __forceinline__ float log2_norm(double z) {
 }
 
 template <typename T, bool VEC, int NT, int U, int PD = 0>
-__device__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const DrawStats sp,
+__device__ __forceinline__ int32_t residual_draw(const T* prow, const T* qrow, bool has_q, const DrawStats sp,
                                  const DrawStats sq, float a, int64_t V, float u, double* csum,
                                  int32_t* emit_slot) {
   constexpr int NW = NT / kWave;
