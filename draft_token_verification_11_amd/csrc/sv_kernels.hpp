@@ -2901,16 +2901,24 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(LmHeadArgs A) {
 // buffered: the next stage's 16-byte global loads are in flight while the
 // current stage's fragments are read from LDS and multiplied, so every
 // fragment is loaded from memory once per workgroup instead of once per
-// wave.  LDS rows are padded by 16 bytes so that the 16 rows a fragment
-// read touches fall on different banks.  With one stage in flight per
-// workgroup the kernel is bound by memory latency, so it is built for two
-// workgroups per CU (at most 80 KiB of LDS and 256 registers per lane
-// each), whose stages overlap.
+// wave.  LDS rows are stored with their 16-byte chunks permuted by row
+// (an XOR swizzle), so that the rows a fragment read touches fall on
+// different banks.  With one stage in flight per workgroup the kernel is
+// bound by memory latency, so it is built for two workgroups per CU (at
+// most 80 KiB of LDS and 256 registers per lane each), whose stages overlap.
 template <int BM, int BN, int BK>
 __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
   constexpr int WM = BM / 2, WN = BN / 2;       // this wave's block
   constexpr int MBk = WM / 16, NBk = WN / 16;   // its MFMA blocks
-  constexpr int kRow = BK + 8;                  // bf16 per padded LDS row
+  // LDS rows of BK bf16, unpadded; the 16-byte chunk c of row r is stored at
+  // chunk c ^ f(r), so that the 16-byte accesses of any eight consecutive
+  // lanes -- a fragment read's eight rows at one chunk, a stage store's rows
+  // and chunks -- fall on the 32 banks without conflict (measured against
+  // rows padded by 16 bytes: 5 % faster at 144 and 432 rows)
+  constexpr int kRow = BK;
+  constexpr int kChunks = BK / 8, kSh = kChunks == 4 ? 1 : 0;
+  static_assert(kChunks == 4 || kChunks == 8, "stages of 32 or 64 along d");
+  auto swz = [](int r, int c) { return c ^ ((r >> kSh) & (kChunks - 1)); };
   constexpr int TPR = BK / 8;                   // threads per row in the global -> LDS copy
   constexpr int RPP = 256 / TPR;                // rows per pass
   constexpr int NPA = BM / RPP, NPB = BN / RPP;  // passes
@@ -2960,11 +2968,15 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
   };
   auto store_stage = [&](int buf, const uint4 (&ra)[NPA], const uint4 (&rb)[NPB]) {
 #pragma unroll
-    for (int i = 0; i < NPA; ++i)
-      *reinterpret_cast<uint4*>(&As[buf][(r0 + RPP * i) * kRow + 8 * cc]) = ra[i];
+    for (int i = 0; i < NPA; ++i) {
+      const int r = r0 + RPP * i;
+      *reinterpret_cast<uint4*>(&As[buf][r * kRow + 8 * swz(r, cc)]) = ra[i];
+    }
 #pragma unroll
-    for (int i = 0; i < NPB; ++i)
-      *reinterpret_cast<uint4*>(&Bs[buf][(r0 + RPP * i) * kRow + 8 * cc]) = rb[i];
+    for (int i = 0; i < NPB; ++i) {
+      const int r = r0 + RPP * i;
+      *reinterpret_cast<uint4*>(&Bs[buf][r * kRow + 8 * swz(r, cc)]) = rb[i];
+    }
   };
 
   sv_f32x4 acc[MBk][NBk];
@@ -2986,13 +2998,17 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
     for (int ks = 0; ks < BK; ks += 32) {
       sv_bf16x8 af[MBk], bfr[NBk];
 #pragma unroll
-      for (int mb = 0; mb < MBk; ++mb)
+      for (int mb = 0; mb < MBk; ++mb) {
+        const int r = wm * WM + 16 * mb + r16;
         af[mb] = __builtin_bit_cast(sv_bf16x8, *reinterpret_cast<const uint4*>(
-                     &As[buf][(wm * WM + 16 * mb + r16) * kRow + ks + kq]));
+                     &As[buf][r * kRow + 8 * swz(r, (ks + kq) / 8)]));
+      }
 #pragma unroll
-      for (int nb = 0; nb < NBk; ++nb)
+      for (int nb = 0; nb < NBk; ++nb) {
+        const int r = wn * WN + 16 * nb + r16;
         bfr[nb] = __builtin_bit_cast(sv_bf16x8, *reinterpret_cast<const uint4*>(
-                      &Bs[buf][(wn * WN + 16 * nb + r16) * kRow + ks + kq]));
+                      &Bs[buf][r * kRow + 8 * swz(r, (ks + kq) / 8)]));
+      }
 #pragma unroll
       for (int mb = 0; mb < MBk; ++mb)
 #pragma unroll
