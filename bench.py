@@ -339,7 +339,8 @@ def run_workload(cfg, args, sv, torch, dev, stream, threads, headline):
     achieved_rows = a1_bytes / (ms_rows / 1e3) / 1e9
     direct = not filtered and c.V <= 4096  # the tail computes such rows' statistics itself
     if path != sv.SPEC_PATH_ROW_PASS:
-        kernel = "k_verify_task_bf16 (position-task queue, exact bf16 key histogram)"
+        kernel = ("k_verify_pair_bf16 (position-task queue; a position's target and draft rows "
+                  "counted at once into two exact bf16 window histograms)")
         alg_bytes = float(np.mean([walk_rows[i % len(sets)] for i in range(args.steps)])) * \
             row_bytes + draw_bytes
         kernel_ms = ms

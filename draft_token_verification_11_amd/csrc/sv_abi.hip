@@ -337,7 +337,7 @@ struct StochasticRun {
                        reinterpret_cast<uint32_t*>(ws + L.queue_off),
                        reinterpret_cast<uint32_t*>(ws + L.slots_off),
                        reinterpret_cast<uint32_t*>(ws + L.slots_off) + (B * args.k + kMaxWalkGrid)};
-        hipLaunchKernelGGL((sv::k_verify_task_bf16<kPrefetch, kLoadDepth>),
+        hipLaunchKernelGGL((sv::k_verify_pair_bf16<kPrefetch, kLoadDepth>),
                            dim3(unsigned(walk_grid)), dim3(kFilterThreads), 0, st, A);
         return;
       }

@@ -2195,11 +2195,13 @@ __global__ __launch_bounds__(1024) void k_verify_seq_bf16(SeqArgs A) {
 // to the queue.  Task (s, k) counts the bonus row and draws from it.  Tasks
 // are taken in queue order (the B position-0 tasks first), so the sequences
 // advance position by position across the whole batch and the call does not
-// end with a few workgroups walking long sequences alone.
+// end with a few workgroups walking long sequences alone.  The kernel is
+// k_verify_pair_bf16 (sv_window.hpp); the queue's words and helpers are here.
 //
 // Once workgroups wait for work (the end of a call), a task appends its
-// successor (s, j + 1) as soon as it starts, before its own ratio test: the
-// successor's rows are then counted while position j is still being decided.
+// successor (s, j + 1) as soon as its rows are counted, before its own ratio
+// test: the successor's rows are then counted while position j is still
+// being decided.
 // A task commits its outcome only after every earlier position of its
 // sequence has passed (the per-sequence word `seqstate`); it is dropped when
 // the sequence stopped before it.  So the outputs depend on the rows up to
@@ -2295,236 +2297,6 @@ constexpr uint32_t kNoClaim = 0xFFFFFFFFu;
 // the rest of the taker's current task (up to a correction draw) while other
 // workgroups sit idle.
 constexpr uint32_t kClaimMargin = 64;
-
-struct TaskScratch {
-  RowStat st[2];  // target and draft row of the current position
-  double csum[16 * kDrawChunks];  // residual-draw chunk sums
-  int32_t emit;
-  uint32_t nidx;   // queue position taken for the next task (kNoClaim: none yet)
-  uint32_t next;   // its task once known (0: slot not written yet)
-  int32_t formed, accepted, keep, last;
-};
-
-template <int PF, int D>
-__global__ __launch_bounds__(1024) void k_verify_task_bf16(TaskArgs A) {
-  constexpr int NT = 1024;
-  __shared__ uint32_t hist[32768];
-  __shared__ HistScratch S;
-  __shared__ TaskScratch Q;
-  auto TID = []() {
-    int t = threadIdx.x;
-    asm volatile("" : "+v"(t));
-    return t;
-  };
-  const int64_t V = A.V;
-  const int k = A.k, k1 = k + 1, nr = 2 * k + 1;
-  const uint32_t B = (uint32_t)A.B;
-
-  uint4 pf[PF];
-  const uint16_t* pf_row = nullptr;  // the row whose first vectors pf holds
-  hist_clear(hist);
-  if (TID() == 0) Q.next = task_wait(atomicAdd(&A.queue[0], 1u), A.slots, B, (uint32_t)k1);
-  block_sync_lds();
-  uint32_t task = Q.next;
-
-  while (task != kTaskExit) {
-    const bool early = (task & kTaskSpec) != 0u;  // appended before j - 1 was decided
-    task &= ~kTaskSpec;
-    const int64_t b = (int64_t)((task - 1u) / (uint32_t)k1);
-    const int j = (int)((task - 1u) - (uint32_t)b * (uint32_t)k1);
-    const bool bonus = j == k;
-    const uint16_t* trow = A.map.template row<uint16_t>(b * nr + j);
-    const uint16_t* drow = bonus ? trow : A.map.template row<uint16_t>(b * nr + k1 + j);
-    // Thread 0 keeps round trips to the device-wide counters off the path
-    // between a row's count and its scan (a load issued before a count is
-    // waited for when the count's first vectors are used, one issued before
-    // a scan is not): at the start it loads the drafted token, its accept
-    // draw and the queue figures; after the first row's count the two
-    // logits of the ratio test, and it appends the successor early when
-    // workgroups wait for work and takes the next queue position early when
-    // plenty of tasks are queued; after that row's scan it reads the claimed
-    // position's task, whose first row is prefetched while the draft row is
-    // scanned.
-    int32_t tok = 0;
-    float uj = 0.0f, lt = 0.0f, ld = 0.0f;
-    bool spec = false, claim = false;
-    uint32_t q_head = 0, q_app = 0, q_seq = 0, nidx = kNoClaim, nx0 = 0u;
-    if (TID() == 0) {
-      q_head = ld_agent32(&A.queue[0]);
-      q_app = task_appended(A.queue);
-      if (!bonus) {
-        tok = A.tokens[b * k + j];
-        uj = A.u[b * k1 + j];
-        if (early) q_seq = ld_agent32(A.seqstate + b);
-      }
-    }
-    bool valid = true, stop = true;
-    int n = j;
-    // target row j (or the bonus row)
-    hist_count_stream<PF, D>(hist, trow, V, pf, trow == pf_row);
-    if (TID() == 0) {
-      if (!bonus) {
-        if (tok >= 0 && (int64_t)tok < V) {
-          lt = __builtin_bit_cast(float, (uint32_t)trow[tok] << 16);
-          ld = __builtin_bit_cast(float, (uint32_t)drow[tok] << 16);
-        }
-        if (q_head > B + q_app && (q_seq & kSeqStop) == 0u) {
-          task_append(A.queue, A.slots, (task + 1u) | kTaskSpec);
-          spec = true;
-        }
-      }
-      claim = B + q_app > q_head + kClaimMargin;
-      if (claim) nidx = atomicAdd(&A.queue[0], 1u);
-    }
-    block_sync_lds();
-    // while the histogram is scanned: the draft row (a bonus task prefetches nothing)
-    pf_row = bonus ? nullptr : drow;
-    if (pf_row) prefetch_row(pf, pf_row, V);
-    // the row's figures stay in S.res (LDS) until the next row's scan: a
-    // register copy would be held, and spilled, across the draft row's count
-    if (hist_row_stats(hist, S, V, A.a, A.top_k, A.top_p, nullptr) == 2) {
-      block_sync_lds();
-      filter_row_bisect_call<uint16_t, true, NT>(trow, V, A.a, A.top_k, A.top_p, &S.res, S.dslot,
-                                                  S.uslot);
-      __syncthreads();
-      hist_clear(hist);
-    }
-    const bool t_valid = S.res.valid != 0;
-    if (TID() == 0) {
-      Q.st[0] = S.res;
-      // the claimed position (if any) passes to the end of the task, whatever
-      // path it takes; the draft row's path also reads its task now
-      Q.nidx = nidx;
-      Q.next = 0u;
-      if (claim && !bonus) nx0 = task_peek(nidx, A.slots, B, (uint32_t)k1);
-    }
-    if (bonus) {
-      valid = t_valid;
-    } else if (!t_valid) {  // ill-formed position
-      valid = false;
-    } else {
-      // draft row j
-      hist_count_stream<PF, D>(hist, drow, V, pf, drow == pf_row);
-      if (TID() == 0) Q.next = nx0;
-      block_sync_lds();
-      const uint32_t nx = Q.next;
-      pf_row = nullptr;
-      if (nx != 0u && nx != kTaskExit) {
-        const uint32_t nt = (nx & ~kTaskSpec) - 1u;
-        const int64_t nb = (int64_t)(nt / (uint32_t)k1);
-        const int nj = (int)(nt - (uint32_t)nb * (uint32_t)k1);
-        pf_row = A.map.template row<uint16_t>(nb * nr + nj);
-        prefetch_row(pf, pf_row, V);
-      }
-      if (hist_row_stats(hist, S, V, A.a, A.top_k, A.top_p, nullptr) == 2) {
-        block_sync_lds();
-        filter_row_bisect_call<uint16_t, true, NT>(drow, V, A.a, A.top_k, A.top_p, &S.res,
-                                                    S.dslot, S.uslot);
-        __syncthreads();
-        hist_clear(hist);
-      }
-      if (TID() == 0) {
-        const RowStat st_d = S.res;
-        const RowStat st_t = Q.st[0];
-        Q.st[1] = st_d;
-        const bool formed = st_t.valid && st_d.valid && tok >= 0 && (int64_t)tok < V;
-        bool acc = false;
-        if (formed) {
-          const double p = prob_at(lt, st_t, A.a);
-          const double q = prob_at(ld, st_d, A.a);
-          const double alpha = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-          acc = (double)uj < alpha;
-        }
-        Q.formed = formed ? 1 : 0;
-        Q.accepted = acc ? 1 : 0;
-      }
-      block_sync_lds();
-      valid = Q.formed != 0;
-      stop = !(valid && Q.accepted != 0);
-    }
-    // Commit once every earlier position has passed.  A task appended early
-    // waits for the task of position j - 1, which was taken from the queue
-    // before this one was appended and commits without waiting on anything
-    // later; any other task was appended by that commit.
-    if (TID() == 0) {
-      int keep = 1;
-      if (early) {
-        uint32_t d;
-        while (((d = ld_agent32(A.seqstate + b)) & kSeqStop) == 0u && d < (uint32_t)j)
-          __builtin_amdgcn_s_sleep(1);
-        keep = (d & kSeqStop) == 0u;
-      }
-      if (keep) {
-        if (spec) task_publish(A.seqstate + b, stop ? (kSeqStop | (uint32_t)j) : (uint32_t)(j + 1));
-        else if (!stop) task_append(A.queue, A.slots, task + 1u);
-      }
-      Q.keep = keep;
-    }
-    block_sync_lds();
-    if (Q.keep && stop) {
-      // correction from the residual of the two rows at n, or the bonus draw
-      int32_t emitted = -1;
-      if (valid) {
-        const RowStat& sp = Q.st[0];
-        const RowStat& sq = Q.st[bonus ? 0 : 1];
-        emitted = residual_draw_call(trow, drow, !bonus, sp.m, sp.thr, sp.z, sq.m, sq.thr, sq.z,
-                                     A.a, V, A.u[b * k1 + k], Q.csum, &Q.emit);
-      }
-      int32_t* out = A.out_tokens + b * k1;
-      for (int t = TID(); t <= k; t += NT) {
-        int32_t v = -1;
-        if (valid) {
-          if (t < n) v = A.tokens[b * k + t];
-          else if (t == n) v = emitted;
-        }
-        out[t] = v;
-      }
-      if (TID() == 0) A.accepted_len[b] = valid ? n : -1;
-    }
-    // Every task, kept or dropped, counts as finished after its appends: the
-    // count reaching every task ever appended means none is left, so none
-    // can be appended any more, and the queue positions past the last task
-    // tell each workgroup to leave.
-    // A workgroup that already holds its next task cannot have finished the
-    // last one (that task is unfinished), so it does not wait for the count;
-    // its later finishes reach the counter after this one (same address,
-    // same wave).  Otherwise the position for the next task is taken in the
-    // same round trip.
-    if (TID() == 0) {
-      if (Q.next != 0u) {
-        (void)__hip_atomic_fetch_add(task_af(A.queue), 1ull, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        const uint64_t af = __hip_atomic_fetch_add(task_af(A.queue), 1ull, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT) + 1ull;
-        const uint32_t i = Q.nidx != kNoClaim ? Q.nidx : atomicAdd(&A.queue[0], 1u);
-        const uint32_t P = (uint32_t)(af >> 32);
-        if ((uint32_t)af == B + P)
-          for (uint32_t e = 0; e < gridDim.x; ++e) task_publish(A.slots + P + e, kTaskExit);
-        Q.next = task_wait(i, A.slots, B, (uint32_t)k1);
-      }
-    }
-    block_sync_lds();
-    task = Q.next;
-    block_sync_lds();  // everyone has read Q before the next task writes it
-  }
-
-  // The last workgroup out leaves the queue words, the used slots and the
-  // sequence words zero.
-  if (TID() == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    Q.last = atomicAdd(&A.queue[1], 1u) == gridDim.x - 1 ? 1 : 0;
-  }
-  block_sync_lds();
-  if (Q.last) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const uint32_t used = task_appended(A.queue) + gridDim.x;
-    for (uint32_t i = (uint32_t)TID(); i < used; i += NT) A.slots[i] = 0u;
-    for (uint32_t i = (uint32_t)TID(); i < B; i += NT) A.seqstate[i] = 0u;
-    block_sync_lds();
-    if (TID() < 4) A.queue[TID()] = 0u;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Logits processing: merge (unfiltered) partials or copy (filtered) stats into

@@ -1,5 +1,7 @@
-// sv_window.hpp -- the persistent bf16 row filter at two workgroups per CU,
-// each with a 64 KiB histogram of the bf16 codes in an exponent window.
+// sv_window.hpp -- exact bf16 row statistics from 64 KiB histograms of the
+// bf16 codes in an exponent window: the persistent row filter at two
+// workgroups per CU, and the position-task verify that counts a position's
+// target and draft rows at once into two such histograms.
 //
 // One workgroup per CU with a histogram of every bf16 code (128 KiB of the
 // CU's 160 KiB of LDS) leaves HBM idle while a row's histogram is scanned:
@@ -128,12 +130,12 @@ __device__ __forceinline__ void win_add8(uint32_t* hist, uint32_t* side, uint4 v
 // Streams one aligned bf16 row into the (cleared) window histogram, D 16-byte
 // loads in flight per thread; the first PF vectors of each thread come from
 // `pf` when pf_ok (prefetched during the previous row's scan).
+// Thread `tid` of the NTH counting threads.
 template <int PF, int D, int NTH>
 __device__ __forceinline__ void win_count_stream(uint32_t* hist, uint32_t* side, const uint16_t* row,
-                                                 int64_t V, const uint4 (&pf)[PF], bool pf_ok) {
+                                                 int64_t V, const uint4 (&pf)[PF], bool pf_ok,
+                                                 uint32_t tid) {
   constexpr uint32_t NT = NTH;
-  uint32_t tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
   const uint32_t nfull = (uint32_t)(V / 8);
   const uint32_t ngroups = (uint32_t)((V + 7) / 8);
   const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, V);
@@ -181,11 +183,10 @@ __device__ __forceinline__ void win_count_stream(uint32_t* hist, uint32_t* side,
 }
 
 template <int PF, int NT>
-__device__ __forceinline__ void win_prefetch_row(uint4 (&pf)[PF], const uint16_t* row, int64_t V) {
+__device__ __forceinline__ void win_prefetch_row(uint4 (&pf)[PF], const uint16_t* row, int64_t V,
+                                                 uint32_t tid) {
   const uint32_t nfull = (uint32_t)(V / 8);
   const __amdgpu_buffer_rsrc_t rs = row_rsrc(row, V);
-  uint32_t tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
     const uint32_t g = tid + (uint32_t)j * NT;
@@ -485,6 +486,477 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
   return r != 0 ? r : win_stats_mass<NT>(hist, S, V, a, top_k, top_p, out);
 }
 
+// Two rows at once: threads 0..511 of a 1024-thread workgroup scan one
+// histogram (with its own S), threads 512..1023 the other, t = the thread's
+// index within its half.  The same statistics as win_row_stats<512> for each
+// row, but with no early return: every thread passes the same five barriers
+// whatever either row holds, so the halves never wait at different ones.
+// Returns this half's status: 0 success (S.res), 1 invalid row (S.res
+// written invalid), 2 the row needs the exact bisection path (the histogram
+// is left for the caller to clear).  After 0 or 1 the histogram and side
+// counters are zero.
+__device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int t, int64_t V,
+                                              float a, int top_k, float top_p) {
+  constexpr int NT = 512, NW = NT / kWave;
+  const int lane = t & (kWave - 1);
+  const int wv = t / kWave;
+  const bool use_k = top_k > 0 && (int64_t)top_k < V;
+  const bool use_p = top_p < 1.0f;
+  const uint32_t s_zero = S.side[kSideZero], s_ninf = S.side[kSideNegInf];
+  const uint32_t s_bad = S.side[kSideBad], s_huge = S.side[kSideHuge];
+  const uint32_t s_tneg = S.side[kSideTinyNeg], s_tpos = S.side[kSideTinyPos];
+  const uint32_t tiny = s_tneg + s_tpos;
+  const uint32_t zcnt = s_zero + tiny;  // the zero entry: zeros and tiny values
+  const uint32_t nz = zcnt != 0u ? 1u : 0u;
+
+  // The list of non-empty entries in descending key order (as win_stats_list):
+  // two threads per key-ordered group kg = 255 - t/2, met by a lane swap.
+  uint32_t npos = 0, nwin = 0;
+  {
+    const uint32_t gi = (uint32_t)t / 2u;
+    const uint32_t kg = 255u - gi;
+    const uint32_t sg = kg >= 128u ? kg - 128u : 255u - kg;
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist) + sg * 16u + ((uint32_t)t % 2u) * 8u;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < 8u; ++j) {
+      const uint4 w = h4[(j + gi) % 8u];
+      cnt += w.x + w.y + w.z + w.w;
+    }
+    cnt += (uint32_t)__builtin_amdgcn_mov_dpp((int)cnt, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    const bool own = (uint32_t)t % 2u == 0u && cnt != 0;
+    const uint64_t ball = __ballot(own);
+    if (lane == 0) S.wcount[wv] = (uint32_t)__popcll(ball);
+    block_sync_lds();  // 1
+    uint32_t off = 0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const uint32_t c = S.wcount[v];
+      if (v < wv) off += c;
+      if (v < NW / 2) npos += c;
+      nwin += c;
+    }
+    if (own) {
+      const uint32_t pos =
+          off + (wv >= NW / 2 ? nz : 0u) + (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
+      S.list[pos] = (uint16_t)kg;
+      S.lcnt[pos] = cnt;
+    }
+  }
+  const uint32_t nl = nwin + nz + (s_ninf ? 1u : 0u);
+  if (t == 0) {
+    if (nz) {
+      S.list[npos] = kEntZero;
+      S.lcnt[npos] = zcnt;
+    }
+    if (s_ninf) {
+      S.list[nwin + nz] = kEntNegInf;
+      S.lcnt[nwin + nz] = s_ninf;
+    }
+    S.nl = nl;
+    S.fallback = 0u;
+  }
+  block_sync_lds();  // 2
+
+  auto kcount = [&](uint32_t ent, uint32_t j) -> uint32_t {
+    if (ent < (uint32_t)kWinGroups) return hist[win_idx(win_key(ent, j))];
+    if (j != 0u) return 0u;
+    return ent == kEntZero ? zcnt : s_ninf;
+  };
+  // status, the same in every thread of the half (it depends on LDS only)
+  int st = 0;
+  const uint32_t e0 = nl != 0u ? (uint32_t)S.list[0] : (uint32_t)kEntNegInf;
+  if (s_bad || (e0 == kEntNegInf && s_huge == 0u)) {
+    st = 1;  // NaN/+inf, or no finite logit
+    if (t == 0) S.res = RowStat{__builtin_nanf(""), __builtin_nanf(""), 0.0, 0, {0, 0, 0}};
+  } else if (s_huge || (tiny && a > 16.0f) || (e0 == kEntZero && (s_tpos || !s_zero))) {
+    st = 2;  // huge values, tiny ones at a low temperature, or a tiny max
+  } else {
+    uint32_t max_key;
+    if (e0 == kEntZero) {
+      max_key = kKey16PosZero;
+    } else {
+      const uint64_t nzm = __ballot(kcount(e0, (uint32_t)lane) != 0u);
+      max_key = win_key(e0, 63u - (uint32_t)__clzll((long long)nzm));
+    }
+    if (wv == 0 && lane == 0) {
+      S.m = value_of_key16(max_key);
+      S.tk = 0;
+      S.tk_entry = nl - 1;
+    }
+    if (use_k && wv == 0) {  // the top-k key by exact counts
+      uint32_t carry = 0;
+      for (uint32_t base = 0; base < nl; base += kWave) {
+        const uint32_t x = (base + lane < nl) ? S.lcnt[base + lane] : 0u;
+        const uint32_t inc = wave_incl_scan(x) + carry;
+        const uint64_t hit = __ballot(base + lane < nl && inc >= (uint32_t)top_k);
+        if (hit) {
+          const int L = __ffsll((unsigned long long)hit) - 1;
+          const uint32_t before = bcast(inc - x, L);
+          const uint32_t ek = S.list[base + L];
+          const uint32_t c = kcount(ek, (uint32_t)lane);
+          const uint32_t suf = wave_incl_suffix(c) + before;
+          const uint64_t ok = __ballot(suf >= (uint32_t)top_k);
+          if (lane == 0) {
+            S.tk = win_ent_key(ek, 63u - (uint32_t)__clzll((long long)ok));
+            S.tk_entry = base + L;
+            if (ek == kEntZero && tiny) S.fallback = 1u;
+          }
+          break;
+        }
+        carry = bcast(inc, kWave - 1);
+      }
+    }
+  }
+  block_sync_lds();  // 3
+  if (st == 0 && S.fallback) st = 2;
+
+  // Masses over keys >= tk, one wave per entry; the first kTop entries keep
+  // their totals for the cut (as win_stats_mass).
+  constexpr uint32_t kTop = 32;
+  const float m = S.m;
+  const uint32_t tk = S.tk;
+  const uint32_t last = S.tk_entry;
+  auto emass = [&](uint32_t ent, uint32_t j) -> float {
+    const uint32_t key = win_ent_key(ent, j);
+    return key >= tk ? key_mass(key, kcount(ent, j), m, a) : 0.0f;
+  };
+  if (st == 0) {
+    float acc = 0.0f;
+    for (uint32_t i = (uint32_t)wv; i <= last; i += NW) {
+      const float e = emass(S.list[i], (uint32_t)lane);
+      acc += e;
+      if (i < kTop) {
+        const float gs = wave_sum(e);
+        if (lane == 0) S.gmass[i] = gs;
+      }
+    }
+    const double ws = wave_sum((double)acc);
+    if (lane == 0) S.dslot[wv] = ws;
+  }
+  block_sync_lds();  // 4
+
+  // Wave 0 of the half: the normaliser, then the top-p cut.
+  if (st == 0 && wv == 0) {
+    double zk = 0.0;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) zk += S.dslot[v];
+    uint32_t thr_key = tk;
+    double z = zk;
+    bool fb = false;
+    if (use_p) {
+      const double target = (double)S.top_p * zk;
+      double carry = 0.0;
+      for (uint32_t base = 0; base <= last; base += kWave) {
+        const bool in = base + lane <= last;
+        double x = 0.0;
+        if (base < kTop) x = (in && base + lane < kTop) ? (double)S.gmass[base + lane] : 0.0;
+        const double inc = wave_incl_scan(x) + carry;
+        uint64_t hit = __ballot(in && base + lane < kTop && inc >= target);
+        int L = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
+        double before = L >= 0 ? bcast(inc - x, L) : 0.0;
+        if (L < 0 && base + kWave >= kTop) {
+          double run = bcast(inc, kWave - 1);
+          for (uint32_t i = max(base, kTop); i <= last; ++i) {
+            const double gm = wave_sum((double)emass(S.list[i], (uint32_t)lane));
+            if (run + gm >= target || i == last) {
+              L = (int)(i - base);
+              before = run;
+              break;
+            }
+            run += gm;
+          }
+        }
+        if (L >= 0 || base + kWave > last) {
+          if (L < 0) {  // rounding corner: the last entry
+            L = (int)(last - base);
+            before = bcast(inc - x, L);
+          }
+          const uint32_t ec = S.list[base + L];
+          const double e = (double)emass(ec, (uint32_t)lane);
+          const double suf = wave_incl_suffix(e) + before;
+          const uint64_t ok = __ballot(suf >= target);
+          int pick;
+          if (ok) {
+            pick = 63 - __clzll((long long)ok);
+          } else {  // rounding corner: the lowest key with mass in the entry
+            const uint64_t nzm = __ballot(e > 0.0);
+            pick = nzm ? __ffsll((unsigned long long)nzm) - 1 : 0;
+          }
+          thr_key = max(tk, win_ent_key(ec, (uint32_t)pick));
+          z = bcast(suf, pick);
+          fb = ec == kEntZero && tiny != 0u;
+          break;
+        }
+        carry = bcast(inc, kWave - 1);
+      }
+    }
+    if (lane == 0) {
+      S.fallback = fb ? 1u : 0u;
+      if (!fb)
+        S.res = RowStat{m, (use_k || use_p) ? value_of_key16(thr_key) : -__builtin_inff(), z, 1,
+                        {0, 0, 0}};
+    }
+  }
+  block_sync_lds();  // 5
+  if (st == 0 && S.fallback) st = 2;
+  if (st != 2) win_clear_listed<NT>(hist, S, t);
+  return st;
+}
+
+// ---------------------------------------------------------------------------
+// Stochastic verify for large batches of aligned bf16 rows: the position-task
+// queue (protocol, words and helpers with TaskArgs in sv_kernels.hpp), one
+// 1024-thread workgroup per CU.  A task (s, j) counts target row j with
+// threads 0..511 into one exponent-window histogram and draft row j with
+// threads 512..1023 into another, and scans both at once (win_pair_stats):
+// one scan per position instead of two one after the other, while the count
+// keeps every thread's loads in flight over the two rows.  The bonus task
+// counts and scans its one row with every thread.  Thread kQ makes the
+// queue's round trips: it reads the queue figures as a task starts, appends
+// the successor early and claims the next position (when plenty are queued)
+// once the rows are counted, and reads the claimed slot after the scan; the
+// next task's first vectors are then prefetched during the commit, or after
+// the correction draw when there is one (whose loads take the registers).
+struct PairScratch {
+  double csum[16 * kDrawChunks];  // residual-draw chunk sums
+  int32_t emit;
+  int32_t pst[2];  // the halves' scan statuses
+  uint32_t nidx;   // queue position taken for the next task (kNoClaim: none)
+  uint32_t next;   // its task once known (0: slot not written yet)
+  int32_t formed, accepted, keep, last;
+};
+
+template <int PF, int D>
+__global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
+  constexpr int NT = 1024;
+  constexpr int kQ = 512;
+  __shared__ uint32_t hist[2 * kWinWords];
+  __shared__ WinScratch S[2];
+  __shared__ PairScratch Q;
+  const int64_t V = A.V;
+  const int k = A.k, k1 = k + 1, nr = 2 * k + 1;
+  const uint32_t B = (uint32_t)A.B;
+
+  uint4 pf[PF];
+  uint32_t pf_task = 0u;  // the task whose rows' first vectors pf holds (0: none)
+  win_clear<NT>(hist, S[0].side);
+  win_clear<NT>(hist + kWinWords, S[1].side);
+  if (opaque_tid() == kQ) {
+    S[0].top_p = A.top_p;
+    S[1].top_p = A.top_p;
+    Q.next = task_wait(atomicAdd(&A.queue[0], 1u), A.slots, B, (uint32_t)k1);
+  }
+  block_sync_lds();
+  uint32_t task = Q.next;
+
+  while (task != kTaskExit) {
+    const bool early = (task & kTaskSpec) != 0u;  // appended before j - 1 was decided
+    task &= ~kTaskSpec;
+    const int64_t b = (int64_t)((task - 1u) / (uint32_t)k1);
+    const int j = (int)((task - 1u) - (uint32_t)b * (uint32_t)k1);
+    const bool bonus = j == k;
+    const uint16_t* trow = A.map.template row<uint16_t>(b * nr + j);
+    const uint16_t* drow = bonus ? trow : A.map.template row<uint16_t>(b * nr + k1 + j);
+    // Thread kQ issues no load of the queue's words before its share of the
+    // count: those words are contended, their round trips are slow, and a
+    // wave's loads complete in order, so its count would wait for them.  The
+    // drafted token and its draw (inputs) are read first; the two logits,
+    // the queue figures and the claim of the next position go out after the
+    // count and arrive during the scan (which reads only LDS).
+    int32_t tok = 0;
+    float uj = 0.0f;
+    uint16_t lt16 = 0, ld16 = 0;
+    bool claim = false, spec = false;
+    uint32_t q_head = 0, q_app = 0, q_seq = 0, nidx = kNoClaim;
+    if (opaque_tid() == kQ) {
+      q_head = ld_agent32(&A.queue[0]);
+      q_app = task_appended(A.queue);
+      if (!bonus) {
+        tok = A.tokens[b * k + j];
+        uj = A.u[b * k1 + j];
+        if (early) q_seq = ld_agent32(A.seqstate + b);
+      }
+    }
+    const bool pf_ok = pf_task == task;
+    if (bonus) {
+      win_count_stream<PF, D, NT>(hist, S[0].side, trow, V, pf, pf_ok, (uint32_t)opaque_tid());
+    } else {
+      const uint32_t t = (uint32_t)opaque_tid(), h = t >> 9;
+      win_count_stream<PF, D, NT / 2>(hist + h * kWinWords, S[h].side, h ? drow : trow, V, pf,
+                                       pf_ok, t & (NT / 2 - 1));
+    }
+    if (opaque_tid() == kQ) {
+      if (!bonus && tok >= 0 && (int64_t)tok < V) {
+        lt16 = trow[tok];
+        ld16 = drow[tok];
+      }
+      if (!bonus && q_head > B + q_app && (q_seq & kSeqStop) == 0u) {
+        task_append(A.queue, A.slots, (task + 1u) | kTaskSpec);
+        spec = true;
+      }
+      claim = B + q_app > q_head + kClaimMargin;
+      if (claim) nidx = atomicAdd(&A.queue[0], 1u);
+    }
+    block_sync_lds();
+    if (bonus) {
+      if (win_row_stats<NT>(hist, S[0], V, A.a, A.top_k, A.top_p, nullptr) == 2) {
+        block_sync_lds();
+        filter_row_bisect_call<uint16_t, true, NT>(trow, V, A.a, A.top_k, A.top_p, &S[0].res,
+                                                    S[0].dslot, S[0].uslot);
+        __syncthreads();
+        win_clear<NT>(hist, S[0].side);
+      }
+    } else {
+      const uint32_t t = (uint32_t)opaque_tid(), h = t >> 9;
+      const int st = win_pair_stats(hist + h * kWinWords, S[h], (int)(t & (NT / 2 - 1)), V, A.a,
+                                    A.top_k, A.top_p);
+      if ((t & (NT / 2 - 1)) == 0u) Q.pst[h] = st;
+      block_sync_lds();
+      if (Q.pst[0] == 2 || Q.pst[1] == 2) {
+#pragma unroll 1
+        for (int hh = 0; hh < 2; ++hh) {
+          if (Q.pst[hh] != 2) continue;
+          filter_row_bisect_call<uint16_t, true, NT>(hh ? drow : trow, V, A.a, A.top_k, A.top_p,
+                                                      &S[hh].res, S[hh].dslot, S[hh].uslot);
+          __syncthreads();
+          win_clear<NT>(hist + hh * kWinWords, S[hh].side);
+        }
+        block_sync_lds();
+      }
+    }
+    // The successor appended early when workgroups wait for work; the ratio
+    // test at j; the claimed position's slot read (its task is resolved at
+    // the finish).
+    uint32_t nx0 = 0u;
+    if (opaque_tid() == kQ) {
+      if (claim) nx0 = task_peek(nidx, A.slots, B, (uint32_t)k1);
+      Q.nidx = nidx;
+      const RowStat st_t = S[0].res;
+      bool formed = st_t.valid != 0;
+      bool acc = false;
+      if (!bonus) {
+        const RowStat st_d = S[1].res;
+        formed = formed && st_d.valid && tok >= 0 && (int64_t)tok < V;
+        if (formed) {
+          const float lt = __builtin_bit_cast(float, (uint32_t)lt16 << 16);
+          const float ld = __builtin_bit_cast(float, (uint32_t)ld16 << 16);
+          const double p = prob_at(lt, st_t, A.a);
+          const double q = prob_at(ld, st_d, A.a);
+          const double alpha = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
+          acc = (double)uj < alpha;
+        }
+      }
+      Q.formed = formed ? 1 : 0;
+      Q.accepted = acc ? 1 : 0;
+    }
+    block_sync_lds();
+    const bool valid = Q.formed != 0;
+    const bool stop = bonus || !(valid && Q.accepted != 0);
+    const int n = j;
+    // Commit once every earlier position has passed.  A task appended early
+    // waits for the task of position j - 1, which was taken from the queue
+    // before this one was appended and commits without waiting on anything
+    // later; any other task was appended by that commit.
+    if (opaque_tid() == kQ) {
+      int keep = 1;
+      if (early) {
+        uint32_t d;
+        while (((d = ld_agent32(A.seqstate + b)) & kSeqStop) == 0u && d < (uint32_t)j)
+          __builtin_amdgcn_s_sleep(1);
+        keep = (d & kSeqStop) == 0u;
+      }
+      if (keep) {
+        if (spec) task_publish(A.seqstate + b, stop ? (kSeqStop | (uint32_t)j) : (uint32_t)(j + 1));
+        else if (!stop) task_append(A.queue, A.slots, task + 1u);
+      }
+      Q.keep = keep;
+      Q.next = claim ? nx0 : 0u;
+    }
+    block_sync_lds();
+    // The next task's first vectors: now, unless a correction is drawn first
+    // (its loads take the registers, and the draw leaves time for nothing
+    // else), then after the draw.
+    auto prefetch_task = [&](uint32_t nx) {
+      if (nx == 0u || nx == kTaskExit) return;
+      pf_task = nx & ~kTaskSpec;
+      const uint32_t nt = pf_task - 1u;
+      const int64_t nb = (int64_t)(nt / (uint32_t)k1);
+      const int nj = (int)(nt - (uint32_t)nb * (uint32_t)k1);
+      const uint32_t t = (uint32_t)opaque_tid(), h = t >> 9;
+      if (nj == k)
+        win_prefetch_row<PF, NT>(pf, A.map.template row<uint16_t>(nb * nr + nj), V, t);
+      else
+        win_prefetch_row<PF, NT / 2>(pf, A.map.template row<uint16_t>(nb * nr + nj + h * k1), V,
+                                     t & (NT / 2 - 1));
+    };
+    const bool draws = Q.keep && stop;
+    pf_task = 0u;
+    if (!draws) prefetch_task(Q.next);
+    if (draws) {
+      // correction from the residual of the two rows at n, or the bonus draw
+      int32_t emitted = -1;
+      if (valid) {
+        const RowStat& sp = S[0].res;
+        const RowStat& sq = S[bonus ? 0 : 1].res;
+        emitted = residual_draw_call(trow, drow, !bonus, sp.m, sp.thr, sp.z, sq.m, sq.thr, sq.z,
+                                     A.a, V, A.u[b * k1 + k], Q.csum, &Q.emit);
+      }
+      int32_t* out = A.out_tokens + b * k1;
+      for (int t = opaque_tid(); t <= k; t += NT) {
+        int32_t v = -1;
+        if (valid) {
+          if (t < n) v = A.tokens[b * k + t];
+          else if (t == n) v = emitted;
+        }
+        out[t] = v;
+      }
+      if (opaque_tid() == 0) A.accepted_len[b] = valid ? n : -1;
+    }
+    // Every task, kept or dropped, counts as finished after its appends: the
+    // count reaching every task ever appended means none is left, so none can
+    // be appended any more, and the queue positions past the last task tell
+    // each workgroup to leave.  A workgroup that already holds its next task
+    // cannot have finished the last one, so it does not wait for the count;
+    // otherwise the position for the next task is taken in the same round
+    // trip.
+    if (opaque_tid() == kQ) {
+      if (Q.next != 0u) {
+        (void)__hip_atomic_fetch_add(task_af(A.queue), 1ull, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        const uint64_t af = __hip_atomic_fetch_add(task_af(A.queue), 1ull, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) + 1ull;
+        const uint32_t i = Q.nidx != kNoClaim ? Q.nidx : atomicAdd(&A.queue[0], 1u);
+        const uint32_t P = (uint32_t)(af >> 32);
+        if ((uint32_t)af == B + P)
+          for (uint32_t e = 0; e < gridDim.x; ++e) task_publish(A.slots + P + e, kTaskExit);
+        Q.next = task_wait(i, A.slots, B, (uint32_t)k1);
+      }
+    }
+    block_sync_lds();
+    task = Q.next;
+    if (pf_task == 0u) prefetch_task(task);
+    block_sync_lds();  // everyone has read Q before the next task writes it
+  }
+
+  // The last workgroup out leaves the queue words, the used slots and the
+  // sequence words zero.
+  if (opaque_tid() == kQ) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    Q.last = atomicAdd(&A.queue[1], 1u) == gridDim.x - 1 ? 1 : 0;
+  }
+  block_sync_lds();
+  if (Q.last) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const uint32_t used = task_appended(A.queue) + gridDim.x;
+    for (uint32_t i = (uint32_t)opaque_tid(); i < used; i += NT) A.slots[i] = 0u;
+    for (uint32_t i = (uint32_t)opaque_tid(); i < B; i += NT) A.seqstate[i] = 0u;
+    block_sync_lds();
+    if (opaque_tid() < 4) A.queue[opaque_tid()] = 0u;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Persistent bf16 filter at two 512-thread workgroups per CU: each workgroup
 // walks its rows (XCD-aware: the workgroups of XCD x take the rows of one
@@ -506,14 +978,15 @@ void k_filter_win_persistent(FilterArgs F) {
   uint4 pf[PF];
   int64_t r = r_lo + slot;
   if (threadIdx.x == 0) S.top_p = F.top_p;
-  if (r < r_hi) win_prefetch_row<PF, kWinThreads>(pf, F.map.template row<uint16_t>(r), V);
+  if (r < r_hi) win_prefetch_row<PF, kWinThreads>(pf, F.map.template row<uint16_t>(r), V, opaque_tid());
   win_clear<kWinThreads>(hist, S.side);  // afterwards each row's scan leaves the histogram zero
   for (; r < r_hi; r += per_xcd) {
     const uint16_t* row = F.map.template row<uint16_t>(r);
     block_sync_lds();
-    win_count_stream<PF, D, kWinThreads>(hist, S.side, row, V, pf, true);
+    win_count_stream<PF, D, kWinThreads>(hist, S.side, row, V, pf, true, opaque_tid());
     block_sync_lds();
-    if (r + per_xcd < r_hi) win_prefetch_row<PF, kWinThreads>(pf, F.map.template row<uint16_t>(r + per_xcd), V);
+    if (r + per_xcd < r_hi)
+      win_prefetch_row<PF, kWinThreads>(pf, F.map.template row<uint16_t>(r + per_xcd), V, opaque_tid());
     if (win_row_stats<kWinThreads>(hist, S, V, F.a, F.top_k, F.top_p, F.stats + r) == 2) {
       block_sync_lds();
       filter_row_bisect_call<uint16_t, true, kWinThreads>(row, V, F.a, F.top_k, F.top_p,

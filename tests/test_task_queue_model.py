@@ -1,4 +1,4 @@
-"""A step-by-step model of the position-task queue that k_verify_task_bf16
+"""A step-by-step model of the position-task queue that k_verify_pair_bf16
 runs on the GPU, driven by a random scheduler over many interleavings.
 
 Each workgroup is a generator that yields at every access to the shared
@@ -67,7 +67,7 @@ def workgroup(S: Shared, n_acc, rng, log):
         q_head, q_app = S.head, S.app
         yield "start"
         q_seq = S.seq.get(b, 0) if early else 0
-        yield "count target row"
+        yield "count the rows"
         spec = False
         if not bonus and q_head > B + q_app and not (q_seq & STOP):
             yield from append((task + 1) | SPEC)
@@ -76,15 +76,10 @@ def workgroup(S: Shared, n_acc, rng, log):
         if B + q_app > q_head + MARGIN:
             nidx = take()
             yield "claim"
-        yield "scan target row"
-        nxt = 0
-        if bonus:
-            stop = True
-        else:
-            if nidx is not None:
-                nxt = peek(nidx)
-            yield "count and scan draft row"
-            stop = not (j < n_acc[b])
+        yield "scan the rows"
+        nxt = peek(nidx) if nidx is not None else 0
+        yield "ratio test"
+        stop = bonus or not (j < n_acc[b])
         keep = True
         if early:
             while True:
