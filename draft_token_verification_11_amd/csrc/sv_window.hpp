@@ -67,6 +67,31 @@ __device__ __forceinline__ uint32_t win_ent_key(uint32_t ent, uint32_t j) {
   return ent == kEntZero ? kKey16PosZero : kKey16NegInf;
 }
 
+// Mass of key `lane` of list entry `ent` relative to the max m:
+// count * 2^((v - m) a) for keys >= tk, else 0 (the zero entry's count is
+// zcnt, the -inf entry's mass 0).  The entry is the same in the whole wave,
+// so it is moved to a scalar register and its kind is a scalar branch; the
+// mass needs no branch (every key with a count lies at or below m, so
+// clamping the exponent at 0 changes none of them and keeps the empty keys
+// above m finite).
+__device__ __forceinline__ float win_entry_mass(const uint32_t* hist, uint32_t ent, uint32_t lane,
+                                                float m, float a, uint32_t tk, uint32_t zcnt) {
+  ent = (uint32_t)__builtin_amdgcn_readfirstlane((int)ent);
+  uint32_t key, c;
+  if (ent < (uint32_t)kWinGroups) {
+    key = win_key(ent, lane);
+    c = hist[win_idx(key)];
+  } else if (ent == kEntZero) {
+    key = kKey16PosZero;
+    c = lane == 0u ? zcnt : 0u;
+  } else {  // -inf
+    return 0.0f;
+  }
+  const float x = fminf((value_of_key16(key) - m) * a, 0.0f);
+  const float e = (float)c * __builtin_amdgcn_exp2f(x);
+  return key >= tk ? e : 0.0f;
+}
+
 template <int NT>
 __device__ __forceinline__ void win_clear(uint32_t* hist, uint32_t* side) {
   uint4* h4 = reinterpret_cast<uint4*>(hist);
@@ -369,22 +394,15 @@ __device__ __forceinline__ int win_stats_mass(uint32_t* hist, WinScratch& S, int
   const bool use_p = top_p < 1.0f;
   const uint32_t zcnt = S.side[kSideZero] + S.side[kSideTinyNeg] + S.side[kSideTinyPos];
   const uint32_t tiny = S.side[kSideTinyNeg] + S.side[kSideTinyPos];
-  const uint32_t s_ninf = S.side[kSideNegInf];
   const float m = S.m;
   const uint32_t tk = S.tk;
   const uint32_t last = S.tk_entry;
-  auto kcount = [&](uint32_t ent, uint32_t j) -> uint32_t {
-    if (ent < (uint32_t)kWinGroups) return hist[win_idx(win_key(ent, j))];
-    if (j != 0u) return 0u;
-    return ent == kEntZero ? zcnt : s_ninf;
-  };
 
   // Masses over keys >= tk, one wave per entry; the first kTop entries keep
   // their totals for the cut.
   constexpr uint32_t kTop = 32;
   auto emass = [&](uint32_t ent, uint32_t j) -> float {
-    const uint32_t key = win_ent_key(ent, j);
-    return key >= tk ? key_mass(key, kcount(ent, j), m, a) : 0.0f;
+    return win_entry_mass(hist, ent, j, m, a, tk, zcnt);
   };
   float acc = 0.0f;
   for (uint32_t i = (uint32_t)wv; i <= last; i += NW) {
@@ -618,17 +636,28 @@ __device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int
   const uint32_t tk = S.tk;
   const uint32_t last = S.tk_entry;
   auto emass = [&](uint32_t ent, uint32_t j) -> float {
-    const uint32_t key = win_ent_key(ent, j);
-    return key >= tk ? key_mass(key, kcount(ent, j), m, a) : 0.0f;
+    return win_entry_mass(hist, ent, j, m, a, tk, zcnt);
   };
   if (st == 0) {
+    // four entries per wave at a time, so that their LDS reads and sums
+    // overlap; the additions keep the order of one entry at a time
     float acc = 0.0f;
-    for (uint32_t i = (uint32_t)wv; i <= last; i += NW) {
-      const float e = emass(S.list[i], (uint32_t)lane);
-      acc += e;
-      if (i < kTop) {
-        const float gs = wave_sum(e);
-        if (lane == 0) S.gmass[i] = gs;
+    for (uint32_t i0 = (uint32_t)wv; i0 <= last; i0 += 4 * NW) {
+      float e[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t i = i0 + (uint32_t)(r * NW);
+        e[r] = i <= last ? emass(S.list[i], (uint32_t)lane) : 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc += e[r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t i = i0 + (uint32_t)(r * NW);
+        if (i < kTop) {
+          const float gs = wave_sum(e[r]);
+          if (lane == 0) S.gmass[i] = gs;
+        }
       }
     }
     const double ws = wave_sum((double)acc);
@@ -713,7 +742,8 @@ __device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int
 // one scan per position instead of two one after the other, while the count
 // keeps every thread's loads in flight over the two rows.  The bonus task
 // counts and scans its one row with every thread.  Thread kQ makes the
-// queue's round trips: it reads the queue figures as a task starts, appends
+// queue's round trips: it reads the queue figures, the drafted token, its
+// draw and the two logits of the ratio test as a task starts, appends
 // the successor early and claims the next position (when plenty are queued)
 // once the rows are counted, and reads the claimed slot after the scan; the
 // next task's first vectors are then prefetched during the commit, or after
@@ -776,6 +806,10 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
         tok = A.tokens[b * k + j];
         uj = A.u[b * k1 + j];
         if (early) q_seq = ld_agent32(A.seqstate + b);
+        if (tok >= 0 && (int64_t)tok < V) {  // the two logits of the ratio test
+          lt16 = trow[tok];
+          ld16 = drow[tok];
+        }
       }
     }
     const bool pf_ok = pf_task == task;
@@ -787,10 +821,6 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
                                        pf_ok, t & (NT / 2 - 1));
     }
     if (opaque_tid() == kQ) {
-      if (!bonus && tok >= 0 && (int64_t)tok < V) {
-        lt16 = trow[tok];
-        ld16 = drow[tok];
-      }
       if (!bonus && q_head > B + q_app && (q_seq & kSeqStop) == 0u) {
         task_append(A.queue, A.slots, (task + 1u) | kTaskSpec);
         spec = true;
