@@ -776,8 +776,11 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   // 128 x 256 tiles in 32-wide stages beyond (fewer LDS reads per product;
   // measured best of 128 x 128, 256 x 128 and 128 x 256 at 72 to 864 rows).
   const bool gemm = M > 64, wide = M > 128;
+  // wide: 144-row tiles (the four waves side by side along the vocabulary)
+  // where they leave fewer padded rows than 128-row tiles
+  const bool rows144 = wide && (M + 143) / 144 * 144 < (M + 127) / 128 * 128;
   const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  const int64_t tw = gemm ? (wide ? 256 : 128) : kLmTile, mr = gemm ? 128 : 16 * mb;
+  const int64_t tw = gemm ? (wide ? 256 : 128) : kLmTile, mr = gemm ? (rows144 ? 144 : 128) : 16 * mb;
   const int64_t tiles = (int64_t(V) + tw - 1) / tw;
   const int64_t chunks = (M + mr - 1) / mr;
   const int64_t nblk = tiles * chunks;
@@ -791,7 +794,9 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   auto st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (gemm) {
-    if (wide)
+    if (rows144)
+      hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<144, 256, 32, 1>), dim3(unsigned(grid)), dim3(256), 0, st, A);
+    else if (wide)
       hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<128, 256, 32>), dim3(unsigned(grid)), dim3(256), 0, st, A);
     else
       hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<128, 128, 64>), dim3(unsigned(grid)), dim3(256), 0, st, A);

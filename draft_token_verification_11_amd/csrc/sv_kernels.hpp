@@ -2678,10 +2678,12 @@ __global__ __launch_bounds__(256) void k_lmhead_argmax(LmHeadArgs A) {
 // different banks.  With one stage in flight per workgroup the kernel is
 // bound by memory latency, so it is built for two workgroups per CU (at
 // most 80 KiB of LDS and 256 registers per lane each), whose stages overlap.
-template <int BM, int BN, int BK>
+template <int BM, int BN, int BK, int WGM = 2>
 __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
-  constexpr int WM = BM / 2, WN = BN / 2;       // this wave's block
+  constexpr int WGN = 4 / WGM;                  // the four waves as WGM x WGN blocks
+  constexpr int WM = BM / WGM, WN = BN / WGN;   // this wave's block
   constexpr int MBk = WM / 16, NBk = WN / 16;   // its MFMA blocks
+  static_assert(MBk * 16 * WGM == BM && NBk * 16 * WGN == BN, "whole MFMA blocks per wave");
   // LDS rows of BK bf16, unpadded; the 16-byte chunk c of row r is stored at
   // chunk c ^ f(r), so that the 16-byte accesses of any eight consecutive
   // lanes -- a fragment read's eight rows at one chunk, a stage store's rows
@@ -2693,14 +2695,14 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
   auto swz = [](int r, int c) { return c ^ ((r >> kSh) & (kChunks - 1)); };
   constexpr int TPR = BK / 8;                   // threads per row in the global -> LDS copy
   constexpr int RPP = 256 / TPR;                // rows per pass
-  constexpr int NPA = BM / RPP, NPB = BN / RPP;  // passes
-  static_assert(NPA * RPP == BM && NPB * RPP == BN, "tile rows must fill whole passes");
+  constexpr int NPA = (BM + RPP - 1) / RPP, NPB = BN / RPP;  // passes (the last of A's may be partial)
+  static_assert(NPB * RPP == BN, "head tile rows must fill whole passes");
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kRow];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kRow];
-  __shared__ uint64_t best_s[2][BM];
-  __shared__ uint32_t bad_s[2][BM];
+  __shared__ uint64_t best_s[WGN][BM];
+  __shared__ uint32_t bad_s[WGN][BM];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WGN, wn = w % WGN;
   // XCD-aware order: the workgroups of one XCD take a contiguous range of
   // (tile, chunk) pairs, chunks fastest, so a head tile is reused from L2
   const int64_t nblk = (int64_t)A.n_tiles * A.m_chunks;
@@ -2733,7 +2735,8 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
     const bool in = c + 8 * cc < A.d;  // d is a multiple of 32: whole 16-byte columns
 #pragma unroll
     for (int i = 0; i < NPA; ++i)
-      ra[i] = in ? *reinterpret_cast<const uint4*>(ag[i] + c) : make_uint4(0u, 0u, 0u, 0u);
+      ra[i] = in && r0 + RPP * i < BM ? *reinterpret_cast<const uint4*>(ag[i] + c)
+                                      : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int i = 0; i < NPB; ++i)
       rb[i] = in ? *reinterpret_cast<const uint4*>(bg[i] + c) : make_uint4(0u, 0u, 0u, 0u);
@@ -2742,7 +2745,7 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
 #pragma unroll
     for (int i = 0; i < NPA; ++i) {
       const int r = r0 + RPP * i;
-      *reinterpret_cast<uint4*>(&As[buf][r * kRow + 8 * swz(r, cc)]) = ra[i];
+      if (r < BM) *reinterpret_cast<uint4*>(&As[buf][r * kRow + 8 * swz(r, cc)]) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < NPB; ++i) {
@@ -2795,7 +2798,7 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
   }
 
   // epilogue: per row, the best (order key, lowest index) of this lane's
-  // columns, over the 16 lanes holding the same rows, then over the two
+  // columns, over the 16 lanes holding the same rows, then over the WGN
   // waves sharing those rows; one atomic per (row, tile)
   const int rq = (lane >> 4) * 4;
 #pragma unroll
@@ -2835,8 +2838,13 @@ __global__ __launch_bounds__(256, 2) void k_lmhead_gemm_argmax(LmHeadArgs A) {
   for (int i = tid; i < BM; i += 256) {
     const int64_t m = m0 + i;
     if (m < A.M) {
-      const uint64_t best = best_s[0][i] > best_s[1][i] ? best_s[0][i] : best_s[1][i];
-      const uint32_t bad = bad_s[0][i] | bad_s[1][i];
+      uint64_t best = best_s[0][i];
+      uint32_t bad = bad_s[0][i];
+#pragma unroll
+      for (int g = 1; g < WGN; ++g) {
+        best = best_s[g][i] > best ? best_s[g][i] : best;
+        bad |= bad_s[g][i];
+      }
       if (best) __hip_atomic_fetch_max(A.best + m, best, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (bad) atomicOr(A.bad + m, 1u);
     }
