@@ -561,6 +561,44 @@ __device__ __forceinline__ float key_mass(uint32_t key, uint32_t c, float m, flo
   return c ? (float)c * __builtin_amdgcn_exp2f((value_of_key16(key) - m) * a) : 0.0f;
 }
 
+// A list entry's mass, entry-major: an octet of lanes (eight consecutive
+// lanes, sub = lane % 8) holds the 64 keys of one entry, eight each in
+// ascending key order; x[i] are the masses of keys 8 sub + i.  Each lane sums
+// its eight by a fixed tree, the octet's sums meet by quads and then by the
+// octet (DPP inside the lanes' 16-lane row); lane 8 o + 4 returns the entry's
+// mass.  The 16-bit histogram's scan and the exponent-window scans form their
+// entries' masses by these same additions, so a row's statistics agree bit
+// for bit between the two histograms.
+__device__ __forceinline__ float octet_mass(const float (&x)[8]) {
+  float s = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+  s += Dpp<0xB1>::mov(s, 0.0f);   // quad_perm 1,0,3,2: pairs
+  s += Dpp<0x4E>::mov(s, 0.0f);   // quad_perm 2,3,0,1: quads
+  s += Dpp<0x114>::mov(s, 0.0f);  // row_shr:4: lane 8o + 4 takes quad 8o..8o+3
+  return s;
+}
+
+// Masses of eight keys of one sign whose bf16 codes are rb .. rb + 7 (so
+// ascending magnitude) with counts c[j]: c 2^((v - m) a), the exponent
+// clamped at 0 (every key with a count lies at or below the max m, and the
+// empty keys above it stay finite); with top-k, keys whose value lies below
+// vtk get 0.
+__device__ __forceinline__ void x_masses8(float (&x)[8], const uint32_t (&c)[8], uint32_t rb,
+                                          float m, float a, bool use_k, float vtk) {
+  const uint32_t vb = rb << 16;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float v = __uint_as_float(vb + ((uint32_t)j << 16));
+    x[j] = (float)c[j] * __builtin_amdgcn_exp2f(fminf((v - m) * a, 0.0f));
+  }
+  if (use_k) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = __uint_as_float(vb + ((uint32_t)j << 16));
+      x[j] = v >= vtk ? x[j] : 0.0f;
+    }
+  }
+}
+
 // Row statistics from a filled histogram (all 1024 threads).  Returns 0 on
 // success (RowStat written to S.res and, if given, *out), 1 for an invalid
 // row (written), 2 on counter overflow (nothing written: the caller takes the
@@ -700,69 +738,62 @@ __device__ __forceinline__ int hist_row_stats(uint32_t* hist, HistScratch& S, in
   const uint32_t tk = use_k ? S.tk : 0u;
   const uint32_t last = use_k ? S.tk_entry : nl - 1;  // entries after it lie below tk
 
-  // Masses over keys >= tk: every lane accumulates its keys of the list
-  // entries its wave visits (one wave per entry, lane = key) for the
-  // normaliser; the first kTop entries also get their group totals, which
-  // is where the top-p cut lies for any sensible top_p (deeper entries are
-  // summed on demand below).
-  constexpr uint32_t kTop = 32;
-  float acc = 0.0f;
-  for (uint32_t i = wv; i <= last; i += 16) {
-    const uint32_t key = (uint32_t)S.list[i] * 64 + lane;
-    const float e = key >= tk ? key_mass(key, kcount(key), m, a) : 0.0f;
-    acc += e;
-    if (i < kTop) {
-      const float gs = wave_sum(e);
-      if (lane == 0) S.gmass[i] = gs;
+  // Masses over keys >= tk, entry-major (octet_mass): the entries' masses
+  // into S.gmass.
+  {
+    const uint32_t sub = (uint32_t)tid & 7u;
+    const float vtk = value_of_key16(tk);
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist);
+    for (uint32_t base = 0; base <= last; base += NT / 8) {
+      const uint32_t e = base + (uint32_t)tid / 8u;
+      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (e <= last) {
+        const uint32_t gl = S.list[e];
+        const bool posg = gl >= 512u;
+        // the lane's keys 64 gl + 8 sub .. + 7 in raw-code order (magnitude
+        // order for both signs): 16-byte word q holds the codes rb .. rb + 7
+        const uint32_t q = (posg ? gl - 512u : 1023u - gl) * 8u + (posg ? sub : 7u - sub);
+        const uint32_t rb = 8u * q;
+        const uint4 w = h4[q];
+        uint32_t c[8] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16,
+                         w.z & 0xFFFFu, w.z >> 16, w.w & 0xFFFFu, w.w >> 16};
+        if (rb == 0u) c[0] += c16[0x8000];  // +0 takes the count of -0
+        if (rb == 0x8000u) c[0] = 0u;       // -0
+        x_masses8(x, c, rb, m, a, use_k, vtk);
+      }
+      const float gm = octet_mass(x);
+      if (e <= last && sub == 4u) S.gmass[e] = gm;
     }
   }
-  {
-    const double ws = wave_sum((double)acc);
-    if (lane == 0) S.dslot[wv] = ws;
-  }
-  block_sync_lds();  // group masses and wave sums visible to wave 0
+  block_sync_lds();  // entry masses visible to wave 0
 
-  // Wave 0: the normaliser, then the top-p cut by cumulative mass from the top.
+  // Wave 0: the fp64 prefix over the entries in list order, 64 at a time:
+  // its total is the normaliser; then the top-p cut by cumulative mass from
+  // the top.
   if (wv == 0) {
-    double zk = S.dslot[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) zk += S.dslot[v];
+    double zk = 0.0;
+    for (uint32_t base = 0; base <= last; base += kWave) {
+      const uint32_t i = base + lane;
+      zk = bcast(wave_incl_scan(i <= last ? (double)S.gmass[i] : 0.0) + zk, kWave - 1);
+    }
     uint32_t thr_key = tk;
     double z = zk;
     if (use_p) {
       float tp = top_p;
-      asm volatile("" : "+v"(tp));  // converted here, not held in registers across the walk
+      asm volatile("" : "+v"(tp));  // converted here, not held in registers across the scan
       const double target = (double)tp * zk;
-      double carry = 0.0;
+      // the first entry whose running sum reaches the target (the last one
+      // if rounding leaves none), then inside it the lowest key from which
+      // the keys above still reach it
+      double run = 0.0;
       for (uint32_t base = 0; base <= last; base += kWave) {
         const bool in = base + lane <= last;
-        double x = 0.0;
-        if (base < kTop) {
-          x = (in && base + lane < kTop) ? (double)S.gmass[base + lane] : 0.0;
-        }
-        const double inc = wave_incl_scan(x) + carry;
-        // entries from kTop on: their totals are computed one by one
-        uint64_t hit = __ballot(in && base + lane < kTop && inc >= target);
-        int L = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
-        double before = L >= 0 ? bcast(inc - x, L) : 0.0;
-        if (L < 0 && base + kWave >= kTop) {
-          double run = bcast(inc, kWave - 1);
-          for (uint32_t i = max(base, kTop); i <= last; ++i) {
-            const uint32_t key = (uint32_t)S.list[i] * 64 + lane;
-            const double gm = wave_sum(key >= tk ? (double)key_mass(key, kcount(key), m, a) : 0.0);
-            if (run + gm >= target || i == last) {
-              L = (int)(i - base);
-              before = run;
-              break;
-            }
-            run += gm;
-          }
-        }
-        if (L >= 0 || base + kWave > last) {
-          if (L < 0) {  // rounding corner: the last entry
-            L = (int)(last - base);
-            before = bcast(inc - x, L);
-          }
+        const double x = in ? (double)S.gmass[base + lane] : 0.0;
+        const double inc = wave_incl_scan(x) + run;
+        const uint64_t hit = __ballot(in && inc >= target);
+        if (hit || base + kWave > last) {
+          const int L = hit ? __ffsll((unsigned long long)hit) - 1 : (int)(last - base);
+          const double before = bcast(inc - x, L);
           const uint32_t gc = S.list[base + L];
           const uint32_t key = gc * 64 + lane;
           const double e = key >= tk ? (double)key_mass(key, kcount(key), m, a) : 0.0;
@@ -779,7 +810,7 @@ __device__ __forceinline__ int hist_row_stats(uint32_t* hist, HistScratch& S, in
           z = bcast(suf, pick);
           break;
         }
-        carry = bcast(inc, kWave - 1);
+        run = bcast(inc, kWave - 1);
       }
     }
     if (lane == 0) {

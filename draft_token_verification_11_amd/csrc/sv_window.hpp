@@ -42,7 +42,7 @@ constexpr int kWinListMax = kWinGroups + 2;
 struct WinScratch {
   uint16_t list[kWinListMax];  // non-empty entries in descending key order
   uint32_t lcnt[kWinListMax];  // count of entry i
-  float gmass[kWinListMax];    // mass of entry i (first kTop entries)
+  float gmass[kWinListMax];    // mass of entry i
   uint32_t side[8];            // side counters (kSides used)
   uint32_t wcount[16];
   double dslot[16];
@@ -233,6 +233,133 @@ __device__ __forceinline__ void win_clear_listed(uint32_t* hist, WinScratch& S, 
   if (t < 8) S.side[t] = 0u;
 }
 
+// Masses, normaliser and top-p cut of a window histogram whose list and
+// figures (S.list, S.m, S.tk, S.tk_entry) are set; NT threads, index t; does
+// its work only when `active` (the same value in all NT threads) but passes
+// its two barriers either way.  The entries' masses are formed entry-major
+// (an octet of lanes per entry, eight keys per lane, octet_mass); wave 0 then
+// runs the fp64 prefix over the entries in list order, 64 at a time
+// (chunk_prefix): its total is the normaliser, and the top-p cut lies in the
+// first entry where it reaches top_p times that.  Wave `lead` does that
+// part.  Sets S.res, or S.fallback when the cut lands on the zero entry while
+// tiny values exist.
+template <int NT>
+__device__ __forceinline__ void win_mass_cut(const uint32_t* hist, WinScratch& S, int t, float a,
+                                             bool use_k, bool use_p, uint32_t zcnt, uint32_t tiny,
+                                             bool active, int lead = 0) {
+  const int lane = t & (kWave - 1), wv = t / kWave;
+  const float m = S.m;
+  const uint32_t tk = S.tk, last = S.tk_entry;
+  if (active) {
+    const uint32_t sub = (uint32_t)t & 7u;
+    const float vtk = value_of_key16(tk);
+    for (uint32_t base = 0; base <= last; base += NT / 8) {
+      const uint32_t e = base + (uint32_t)t / 8u;
+      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (e <= last) {
+        const uint32_t ent = S.list[e];
+        // the lane's eight keys in counter order, which is magnitude order
+        // for both signs: counter i0 + j holds the bf16 code rb + j
+        uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = lo;
+        uint32_t rb = 0;
+        if (ent < (uint32_t)kWinGroups) {
+          const uint32_t k0 = win_key(ent, 8u * sub);  // keys k0 .. k0 + 7
+          const bool pos = k0 >= 0x8000u;
+          const uint32_t i0 = win_idx(pos ? k0 : k0 + 7u);
+          rb = pos ? k0 - 0x8000u : 0xFFFFu - (k0 + 7u);
+          const uint4* h4 = reinterpret_cast<const uint4*>(hist + i0);
+          lo = h4[0];
+          hi = h4[1];
+        } else if (ent == kEntZero && sub == 0u) {
+          lo.x = zcnt;  // +0 (code 0) stands for the zeros and tiny values
+        }
+        const uint32_t c[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        x_masses8(x, c, rb, m, a, use_k, vtk);
+      }
+      const float gm = octet_mass(x);
+      if (e <= last && sub == 4u) S.gmass[e] = gm;
+    }
+  }
+  block_sync_lds();
+
+  if (active && wv == lead) {
+    auto emass = [&](uint32_t ent, uint32_t j) -> float {
+      return win_entry_mass(hist, ent, j, m, a, tk, zcnt);
+    };
+    // the prefix over the entries, all its chunks at once
+    constexpr int kC = (kWinListMax + kWave - 1) / kWave;
+    double inc[kC];
+    double run = 0.0;
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      inc[c] = 0.0;
+      if ((uint32_t)(c * kWave) <= last) {
+        const uint32_t i = (uint32_t)(c * kWave + lane);
+        inc[c] = wave_incl_scan(i <= last ? (double)S.gmass[i] : 0.0);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      if ((uint32_t)(c * kWave) <= last) {
+        inc[c] += run;
+        run = bcast(inc[c], kWave - 1);
+      }
+    }
+    const double zk = run;
+    uint32_t thr_key = tk;
+    double z = zk;
+    bool fb = false;
+    if (use_p) {
+      // the first entry whose running sum reaches top_p times the
+      // normaliser (the last entry if rounding leaves none), then inside it
+      // the lowest key from which the keys above still reach it
+      const double target = (double)S.top_p * zk;
+      int cc = -1, L = 0;
+#pragma unroll
+      for (int c = 0; c < kC; ++c) {
+        if (cc < 0 && (uint32_t)(c * kWave) <= last) {
+          const uint64_t hit = __ballot((uint32_t)(c * kWave + lane) <= last && inc[c] >= target);
+          if (hit) {
+            cc = c;
+            L = __ffsll((unsigned long long)hit) - 1;
+          }
+        }
+      }
+      if (cc < 0) {
+        cc = (int)(last / kWave);
+        L = (int)(last % kWave);
+      }
+      double incc = inc[0];
+#pragma unroll
+      for (int c = 1; c < kC; ++c)
+        if (c == cc) incc = inc[c];
+      const uint32_t eL = (uint32_t)(cc * kWave + L);
+      const double before = bcast(incc, L) - (double)S.gmass[eL];
+      const uint32_t ec = S.list[eL];
+      const double e = (double)emass(ec, (uint32_t)lane);
+      const double suf = wave_incl_suffix(e) + before;
+      const uint64_t ok = __ballot(suf >= target);
+      int pick;
+      if (ok) {
+        pick = 63 - __clzll((long long)ok);
+      } else {  // rounding corner: the lowest key with mass in the entry
+        const uint64_t nzm = __ballot(e > 0.0);
+        pick = nzm ? __ffsll((unsigned long long)nzm) - 1 : 0;
+      }
+      thr_key = max(tk, win_ent_key(ec, (uint32_t)pick));
+      z = bcast(suf, pick);
+      fb = ec == kEntZero && tiny != 0u;
+    }
+    if (lane == 0) {
+      S.fallback = fb ? 1u : 0u;
+      if (!fb)
+        S.res = RowStat{m, (use_k || use_p) ? value_of_key16(thr_key) : -__builtin_inff(), z, 1,
+                        {0, 0, 0}};
+    }
+  }
+  block_sync_lds();
+}
+
 // Row statistics from a filled window histogram (S.top_p must hold top_p),
 // every thread of the NT-thread workgroup, in two parts.  win_stats_list
 // builds the list of non-empty entries and finds the max and the top-k key;
@@ -385,113 +512,15 @@ __device__ __forceinline__ int win_stats_list(uint32_t* hist, WinScratch& S, int
 template <int NT>
 __device__ __forceinline__ int win_stats_mass(uint32_t* hist, WinScratch& S, int64_t V, float a,
                                               int top_k, float top_p, RowStat* out) {
-  constexpr int NW = NT / kWave;
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  const int lane = tid & (kWave - 1);
-  const int wv = tid / kWave;
   const bool use_k = top_k > 0 && (int64_t)top_k < V;
   const bool use_p = top_p < 1.0f;
   const uint32_t zcnt = S.side[kSideZero] + S.side[kSideTinyNeg] + S.side[kSideTinyPos];
   const uint32_t tiny = S.side[kSideTinyNeg] + S.side[kSideTinyPos];
-  const float m = S.m;
-  const uint32_t tk = S.tk;
-  const uint32_t last = S.tk_entry;
-
-  // Masses over keys >= tk, one wave per entry; the first kTop entries keep
-  // their totals for the cut.
-  constexpr uint32_t kTop = 32;
-  auto emass = [&](uint32_t ent, uint32_t j) -> float {
-    return win_entry_mass(hist, ent, j, m, a, tk, zcnt);
-  };
-  float acc = 0.0f;
-  for (uint32_t i = (uint32_t)wv; i <= last; i += NW) {
-    const float e = emass(S.list[i], (uint32_t)lane);
-    acc += e;
-    if (i < kTop) {
-      const float gs = wave_sum(e);
-      if (lane == 0) S.gmass[i] = gs;
-    }
-  }
-  {
-    const double ws = wave_sum((double)acc);
-    if (lane == 0) S.dslot[wv] = ws;
-  }
-  block_sync_lds();
-
-  // Wave 0: the normaliser, then the top-p cut by cumulative mass from the top.
-  if (wv == 0) {
-    double zk = 0.0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) zk += S.dslot[v];
-    uint32_t thr_key = tk;
-    double z = zk;
-    bool fb = false;
-    if (use_p) {
-      // top_p comes from LDS here: a register copy held across the scan
-      // would be spilled, and its reload would wait for the loads in flight
-      const double target = (double)S.top_p * zk;
-      double carry = 0.0;
-      for (uint32_t base = 0; base <= last; base += kWave) {
-        const bool in = base + lane <= last;
-        double x = 0.0;
-        if (base < kTop) x = (in && base + lane < kTop) ? (double)S.gmass[base + lane] : 0.0;
-        const double inc = wave_incl_scan(x) + carry;
-        uint64_t hit = __ballot(in && base + lane < kTop && inc >= target);
-        int L = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
-        double before = L >= 0 ? bcast(inc - x, L) : 0.0;
-        if (L < 0 && base + kWave >= kTop) {
-          double run = bcast(inc, kWave - 1);
-          for (uint32_t i = max(base, kTop); i <= last; ++i) {
-            const double gm = wave_sum((double)emass(S.list[i], (uint32_t)lane));
-            if (run + gm >= target || i == last) {
-              L = (int)(i - base);
-              before = run;
-              break;
-            }
-            run += gm;
-          }
-        }
-        if (L >= 0 || base + kWave > last) {
-          if (L < 0) {  // rounding corner: the last entry
-            L = (int)(last - base);
-            before = bcast(inc - x, L);
-          }
-          const uint32_t ec = S.list[base + L];
-          const double e = (double)emass(ec, (uint32_t)lane);
-          const double suf = wave_incl_suffix(e) + before;
-          const uint64_t ok = __ballot(suf >= target);
-          int pick;
-          if (ok) {
-            pick = 63 - __clzll((long long)ok);
-          } else {  // rounding corner: the lowest key with mass in the entry
-            const uint64_t nzm = __ballot(e > 0.0);
-            pick = nzm ? __ffsll((unsigned long long)nzm) - 1 : 0;
-          }
-          thr_key = max(tk, win_ent_key(ec, (uint32_t)pick));
-          z = bcast(suf, pick);
-          fb = ec == kEntZero && tiny != 0u;
-          break;
-        }
-        carry = bcast(inc, kWave - 1);
-      }
-    }
-    if (lane == 0) {
-      RowStat st;
-      st.m = m;
-      st.thr = (use_k || use_p) ? value_of_key16(thr_key) : -__builtin_inff();
-      st.z = z;
-      st.valid = 1;
-      st.pad[0] = st.pad[1] = st.pad[2] = 0;
-      S.fallback = fb ? 1u : 0u;
-      if (!fb) {
-        S.res = st;
-        if (out) *out = st;
-      }
-    }
-  }
-  block_sync_lds();
+  win_mass_cut<NT>(hist, S, tid, a, use_k, use_p, zcnt, tiny, true);
   if (S.fallback) return 2;
+  if (out && tid == 0) *out = S.res;
   win_clear_listed<NT>(hist, S, tid);
   return 0;
 }
@@ -506,15 +535,18 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
 
 // Two rows at once: threads 0..511 of a 1024-thread workgroup scan one
 // histogram (with its own S), threads 512..1023 the other, t = the thread's
-// index within its half.  The same statistics as win_row_stats<512> for each
+// index within its half.  Wave `lead` of the half makes its one-wave steps
+// (the max, the top-k key, the prefix and the cut): with lead 0 for one half
+// and 1 for the other they fall on different SIMDs of the CU, where the
+// halves' first waves share one.  The same statistics as win_row_stats<512> for each
 // row, but with no early return: every thread passes the same five barriers
 // whatever either row holds, so the halves never wait at different ones.
 // Returns this half's status: 0 success (S.res), 1 invalid row (S.res
 // written invalid), 2 the row needs the exact bisection path (the histogram
 // is left for the caller to clear).  After 0 or 1 the histogram and side
 // counters are zero.
-__device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int t, int64_t V,
-                                              float a, int top_k, float top_p) {
+__device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int t, int lead,
+                                              int64_t V, float a, int top_k, float top_p) {
   constexpr int NT = 512, NW = NT / kWave;
   const int lane = t & (kWave - 1);
   const int wv = t / kWave;
@@ -597,12 +629,12 @@ __device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int
       const uint64_t nzm = __ballot(kcount(e0, (uint32_t)lane) != 0u);
       max_key = win_key(e0, 63u - (uint32_t)__clzll((long long)nzm));
     }
-    if (wv == 0 && lane == 0) {
+    if (wv == lead && lane == 0) {
       S.m = value_of_key16(max_key);
       S.tk = 0;
       S.tk_entry = nl - 1;
     }
-    if (use_k && wv == 0) {  // the top-k key by exact counts
+    if (use_k && wv == lead) {  // the top-k key by exact counts
       uint32_t carry = 0;
       for (uint32_t base = 0; base < nl; base += kWave) {
         const uint32_t x = (base + lane < nl) ? S.lcnt[base + lane] : 0u;
@@ -629,105 +661,8 @@ __device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int
   block_sync_lds();  // 3
   if (st == 0 && S.fallback) st = 2;
 
-  // Masses over keys >= tk, one wave per entry; the first kTop entries keep
-  // their totals for the cut (as win_stats_mass).
-  constexpr uint32_t kTop = 32;
-  const float m = S.m;
-  const uint32_t tk = S.tk;
-  const uint32_t last = S.tk_entry;
-  auto emass = [&](uint32_t ent, uint32_t j) -> float {
-    return win_entry_mass(hist, ent, j, m, a, tk, zcnt);
-  };
-  if (st == 0) {
-    // four entries per wave at a time, so that their LDS reads and sums
-    // overlap; the additions keep the order of one entry at a time
-    float acc = 0.0f;
-    for (uint32_t i0 = (uint32_t)wv; i0 <= last; i0 += 4 * NW) {
-      float e[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t i = i0 + (uint32_t)(r * NW);
-        e[r] = i <= last ? emass(S.list[i], (uint32_t)lane) : 0.0f;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc += e[r];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t i = i0 + (uint32_t)(r * NW);
-        if (i < kTop) {
-          const float gs = wave_sum(e[r]);
-          if (lane == 0) S.gmass[i] = gs;
-        }
-      }
-    }
-    const double ws = wave_sum((double)acc);
-    if (lane == 0) S.dslot[wv] = ws;
-  }
-  block_sync_lds();  // 4
-
-  // Wave 0 of the half: the normaliser, then the top-p cut.
-  if (st == 0 && wv == 0) {
-    double zk = 0.0;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) zk += S.dslot[v];
-    uint32_t thr_key = tk;
-    double z = zk;
-    bool fb = false;
-    if (use_p) {
-      const double target = (double)S.top_p * zk;
-      double carry = 0.0;
-      for (uint32_t base = 0; base <= last; base += kWave) {
-        const bool in = base + lane <= last;
-        double x = 0.0;
-        if (base < kTop) x = (in && base + lane < kTop) ? (double)S.gmass[base + lane] : 0.0;
-        const double inc = wave_incl_scan(x) + carry;
-        uint64_t hit = __ballot(in && base + lane < kTop && inc >= target);
-        int L = hit ? __ffsll((unsigned long long)hit) - 1 : -1;
-        double before = L >= 0 ? bcast(inc - x, L) : 0.0;
-        if (L < 0 && base + kWave >= kTop) {
-          double run = bcast(inc, kWave - 1);
-          for (uint32_t i = max(base, kTop); i <= last; ++i) {
-            const double gm = wave_sum((double)emass(S.list[i], (uint32_t)lane));
-            if (run + gm >= target || i == last) {
-              L = (int)(i - base);
-              before = run;
-              break;
-            }
-            run += gm;
-          }
-        }
-        if (L >= 0 || base + kWave > last) {
-          if (L < 0) {  // rounding corner: the last entry
-            L = (int)(last - base);
-            before = bcast(inc - x, L);
-          }
-          const uint32_t ec = S.list[base + L];
-          const double e = (double)emass(ec, (uint32_t)lane);
-          const double suf = wave_incl_suffix(e) + before;
-          const uint64_t ok = __ballot(suf >= target);
-          int pick;
-          if (ok) {
-            pick = 63 - __clzll((long long)ok);
-          } else {  // rounding corner: the lowest key with mass in the entry
-            const uint64_t nzm = __ballot(e > 0.0);
-            pick = nzm ? __ffsll((unsigned long long)nzm) - 1 : 0;
-          }
-          thr_key = max(tk, win_ent_key(ec, (uint32_t)pick));
-          z = bcast(suf, pick);
-          fb = ec == kEntZero && tiny != 0u;
-          break;
-        }
-        carry = bcast(inc, kWave - 1);
-      }
-    }
-    if (lane == 0) {
-      S.fallback = fb ? 1u : 0u;
-      if (!fb)
-        S.res = RowStat{m, (use_k || use_p) ? value_of_key16(thr_key) : -__builtin_inff(), z, 1,
-                        {0, 0, 0}};
-    }
-  }
-  block_sync_lds();  // 5
+  // Masses, normaliser and top-p cut: barriers 4 and 5.
+  win_mass_cut<NT>(hist, S, t, a, use_k, use_p, zcnt, tiny, st == 0, lead);
   if (st == 0 && S.fallback) st = 2;
   if (st != 2) win_clear_listed<NT>(hist, S, t);
   return st;
@@ -839,7 +774,7 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
       }
     } else {
       const uint32_t t = (uint32_t)opaque_tid(), h = t >> 9;
-      const int st = win_pair_stats(hist + h * kWinWords, S[h], (int)(t & (NT / 2 - 1)), V, A.a,
+      const int st = win_pair_stats(hist + h * kWinWords, S[h], (int)(t & (NT / 2 - 1)), h, V, A.a,
                                     A.top_k, A.top_p);
       if ((t & (NT / 2 - 1)) == 0u) Q.pst[h] = st;
       block_sync_lds();
