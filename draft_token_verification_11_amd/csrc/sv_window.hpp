@@ -689,6 +689,7 @@ struct PairScratch {
   int32_t pst[2];  // the halves' scan statuses
   uint32_t nidx;   // queue position taken for the next task (kNoClaim: none)
   uint32_t next;   // its task once known (0: slot not written yet)
+  uint32_t fill;   // the exit fill's first slot when this workgroup finished the last task, else kNoClaim
   int32_t formed, accepted, keep, last;
 };
 
@@ -884,8 +885,10 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
     // each workgroup to leave.  A workgroup that already holds its next task
     // cannot have finished the last one, so it does not wait for the count;
     // otherwise the position for the next task is taken in the same round
-    // trip.
+    // trip.  The workgroup that finishes the last task writes the exit slots
+    // with all its threads (one slot each), then waits on its own position.
     if (opaque_tid() == kQ) {
+      Q.fill = kNoClaim;
       if (Q.next != 0u) {
         (void)__hip_atomic_fetch_add(task_af(A.queue), 1ull, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
@@ -894,12 +897,18 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
                                                    __HIP_MEMORY_SCOPE_AGENT) + 1ull;
         const uint32_t i = Q.nidx != kNoClaim ? Q.nidx : atomicAdd(&A.queue[0], 1u);
         const uint32_t P = (uint32_t)(af >> 32);
-        if ((uint32_t)af == B + P)
-          for (uint32_t e = 0; e < gridDim.x; ++e) task_publish(A.slots + P + e, kTaskExit);
-        Q.next = task_wait(i, A.slots, B, (uint32_t)k1);
+        Q.nidx = i;
+        if ((uint32_t)af == B + P) Q.fill = P;
+        else Q.next = task_wait(i, A.slots, B, (uint32_t)k1);
       }
     }
     block_sync_lds();
+    if (Q.fill != kNoClaim) {
+      for (uint32_t e = (uint32_t)opaque_tid(); e < gridDim.x; e += NT)
+        task_publish(A.slots + Q.fill + e, kTaskExit);
+      if (opaque_tid() == kQ) Q.next = task_wait(Q.nidx, A.slots, B, (uint32_t)k1);
+      block_sync_lds();
+    }
     task = Q.next;
     if (pf_task == 0u) prefetch_task(task);
     block_sync_lds();  // everyone has read Q before the next task writes it
