@@ -706,6 +706,7 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
 
   uint4 pf[PF];
   uint32_t pf_task = 0u;  // the task whose rows' first vectors pf holds (0: none)
+  bool starved = false;   // thread kQ: the last task found workgroups waiting for work
   win_clear<NT>(hist, S[0].side);
   win_clear<NT>(hist + kWinWords, S[1].side);
   if (opaque_tid() == kQ) {
@@ -724,12 +725,12 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
     const bool bonus = j == k;
     const uint16_t* trow = A.map.template row<uint16_t>(b * nr + j);
     const uint16_t* drow = bonus ? trow : A.map.template row<uint16_t>(b * nr + k1 + j);
-    // Thread kQ issues no load of the queue's words before its share of the
-    // count: those words are contended, their round trips are slow, and a
-    // wave's loads complete in order, so its count would wait for them.  The
-    // drafted token and its draw (inputs) are read first; the two logits,
-    // the queue figures and the claim of the next position go out after the
-    // count and arrive during the scan (which reads only LDS).
+    // Thread kQ reads the queue figures, the drafted token, its draw and the
+    // two logits of the ratio test as the task starts; a wave's loads
+    // complete in order, so they arrive with its count's first vectors.
+    // While workgroups wait for work (as the previous task found), the
+    // successor is appended at once, which waits for those loads; otherwise
+    // after the count.
     int32_t tok = 0;
     float uj = 0.0f;
     uint16_t lt16 = 0, ld16 = 0;
@@ -746,7 +747,12 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
           lt16 = trow[tok];
           ld16 = drow[tok];
         }
+        if (starved && q_head > B + q_app && (q_seq & kSeqStop) == 0u) {
+          task_append(A.queue, A.slots, (task + 1u) | kTaskSpec);
+          spec = true;
+        }
       }
+      starved = q_head > B + q_app;
     }
     const bool pf_ok = pf_task == task;
     if (bonus) {
@@ -757,7 +763,7 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
                                        pf_ok, t & (NT / 2 - 1));
     }
     if (opaque_tid() == kQ) {
-      if (!bonus && q_head > B + q_app && (q_seq & kSeqStop) == 0u) {
+      if (!bonus && !spec && q_head > B + q_app && (q_seq & kSeqStop) == 0u) {
         task_append(A.queue, A.slots, (task + 1u) | kTaskSpec);
         spec = true;
       }

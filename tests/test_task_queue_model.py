@@ -67,9 +67,15 @@ def workgroup(S: Shared, n_acc, rng, log):
         q_head, q_app = S.head, S.app
         yield "start"
         q_seq = S.seq.get(b, 0) if early else 0
-        yield "count the rows"
         spec = False
-        if not bonus and q_head > B + q_app and not (q_seq & STOP):
+        # the early successor goes out at the start (while workgroups wait
+        # for work) or once the rows are counted
+        at_start = rng.random() < 0.5
+        if at_start and not bonus and q_head > B + q_app and not (q_seq & STOP):
+            yield from append((task + 1) | SPEC)
+            spec = True
+        yield "count the rows"
+        if not spec and not bonus and q_head > B + q_app and not (q_seq & STOP):
             yield from append((task + 1) | SPEC)
             spec = True
         nidx = None
