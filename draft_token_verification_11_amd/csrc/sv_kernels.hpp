@@ -1851,8 +1851,9 @@ __device__ __noinline__ int help_resolve(uint64_t* ent, uint64_t prev, uint32_t 
   return 1;
 }
 
-// Out of line, with scalar arguments, so that its registers do not burden
-// the walk's streaming loop.
+// The bf16 draw of a 1024-thread workgroup with scalar arguments: U steps
+// per batch in the loop over the remaining steps, and PD steps in flight per
+// wave in the rolling window over a row's whole steps (0: no window).
 template <int U = 2, int PD = 0>
 __device__ __forceinline__ int32_t residual_draw_call(const uint16_t* prow, const uint16_t* qrow,
                                                    bool has_q, float pm, float pthr, double pz,

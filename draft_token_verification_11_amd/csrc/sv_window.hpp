@@ -871,8 +871,10 @@ __global__ __launch_bounds__(1024) void k_verify_pair_bf16(TaskArgs A) {
       if (valid) {
         const RowStat& sp = S[0].res;
         const RowStat& sq = S[bonus ? 0 : 1].res;
-        emitted = residual_draw_call(trow, drow, !bonus, sp.m, sp.thr, sp.z, sq.m, sq.thr, sq.z,
-                                     A.a, V, A.u[b * k1 + k], Q.csum, &Q.emit);
+        // one step per batch and a window of two steps in flight per wave:
+        // what the kernel's register budget holds without spilling in the loop
+        emitted = residual_draw_call<1, 2>(trow, drow, !bonus, sp.m, sp.thr, sp.z, sq.m, sq.thr,
+                                           sq.z, A.a, V, A.u[b * k1 + k], Q.csum, &Q.emit);
       }
       int32_t* out = A.out_tokens + b * k1;
       for (int t = opaque_tid(); t <= k; t += NT) {
