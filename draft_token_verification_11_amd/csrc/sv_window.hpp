@@ -237,10 +237,10 @@ __device__ __forceinline__ void win_clear_listed(uint32_t* hist, WinScratch& S, 
 // figures (S.list, S.m, S.tk, S.tk_entry) are set; NT threads, index t; does
 // its work only when `active` (the same value in all NT threads) but passes
 // its two barriers either way.  The entries' masses are formed entry-major
-// (an octet of lanes per entry, eight keys per lane, octet_mass); wave 0 then
-// runs the fp64 prefix over the entries in list order, 64 at a time
-// (chunk_prefix): its total is the normaliser, and the top-p cut lies in the
-// first entry where it reaches top_p times that.  Wave `lead` does that
+// (an octet of lanes per entry, eight keys per lane, octet_mass); one wave
+// then runs the fp64 prefix over the entries in list order, 64 at a time
+// with every chunk's scan issued together: its total is the normaliser, and
+// the top-p cut lies in the first entry where it reaches top_p times that.  Wave `lead` does that
 // part.  Sets S.res, or S.fallback when the cut lands on the zero entry while
 // tiny values exist.
 template <int NT>
