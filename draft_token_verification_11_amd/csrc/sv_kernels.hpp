@@ -1182,39 +1182,14 @@ constexpr int kDrawThreads = 256;
 constexpr int kDrawGroups = 4;  // groups of 8 elements per thread
 constexpr int64_t kDrawChunk = (int64_t)kDrawThreads * kDrawGroups * 8;  // 8,192 elements
 
-// The residual (or p) of the 8 elements at e, fp32, as in residual_draw.
-template <typename T, bool VEC>
-__device__ __forceinline__ void draw_group(const T* prow, const T* qrow, bool resid,
-                                           const DrawJob& J, float lzp, float lzq, float a,
-                                           int64_t V, int64_t e, float* r8) {
-  Raw8<T> rp, rq;
-  load8_raw<T, VEC>(prow, e, V, rp);
-  if (resid) load8_raw<T, VEC>(qrow, e, V, rq);
-  float lp[8], lq[8];
-  unpack8<T>(rp, lp);
-  if (resid) unpack8<T>(rq, lq);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float p = lp[i] >= J.sp.thr
-                        ? __builtin_amdgcn_exp2f(__builtin_fmaf(lp[i] - J.sp.m, a, -lzp))
-                        : 0.0f;
-    float r = p;
-    if (resid) {
-      const float q = lq[i] >= J.sq.thr
-                          ? __builtin_amdgcn_exp2f(__builtin_fmaf(lq[i] - J.sq.m, a, -lzq))
-                          : 0.0f;
-      r = fmaxf(p - q, 0.0f);
-    }
-    r8[i] = r;
-  }
-}
-
 // This thread's share of chunk c: the fp32 sums of its groups (in element
-// order) and their fp64 total (in group order).
+// order) and their fp64 total (in group order); with r32, also every
+// element's value (the picking workgroup walks them without reading again).
 template <typename T, bool VEC>
 __device__ __forceinline__ double draw_thread_sum(const T* prow, const T* qrow, bool resid,
                                                   const DrawJob& J, float lzp, float lzq, float a,
-                                                  int64_t V, int64_t c, int tid, float* gs) {
+                                                  int64_t V, int64_t c, int tid, float* gs,
+                                                  float* r32 = nullptr) {
   const int64_t e0 = c * kDrawChunk + (int64_t)tid * (kDrawGroups * 8);
   Raw8<T> rp[kDrawGroups], rq[kDrawGroups];
 #pragma unroll
@@ -1241,6 +1216,7 @@ __device__ __forceinline__ double draw_thread_sum(const T* prow, const T* qrow, 
                             : 0.0f;
         r = fmaxf(p - q, 0.0f);
       }
+      if (r32) r32[8 * g + i] = r;
       acc += r;
     }
     gs[g] = acc;
@@ -1360,8 +1336,8 @@ __device__ void draw_pick(RowMap map, int64_t V, int k, float a, DrawJob* __rest
     const int64_t c = sh_chunk;
     const bool last = sh_last != 0;
     const double tc = sh_target;  // the target within chunk c
-    float gs[kDrawGroups];
-    const double x = draw_thread_sum<T, VEC>(prow, qrow, resid, J, lzp, lzq, a, V, c, tid, gs);
+    float gs[kDrawGroups], r32[kDrawGroups * 8];
+    const double x = draw_thread_sum<T, VEC>(prow, qrow, resid, J, lzp, lzq, a, V, c, tid, gs, r32);
     double total;
     const double inc = block_incl_scan256(x, slots, &total);
     // the first thread whose running sum exceeds the target, else the last
@@ -1395,8 +1371,7 @@ __device__ void draw_pick(RowMap map, int64_t V, int k, float a, DrawJob* __rest
           run += (double)gs[g];
           continue;
         }
-        float r8[8];
-        draw_group<T, VEC>(prow, qrow, resid, J, lzp, lzq, a, V, e0 + 8 * g, r8);
+        const float* r8 = r32 + 8 * g;  // the values summed above, the same arithmetic
         for (int i = 0; i < 8; ++i) {
           if (r8[i] > 0.0f) lastpos = e0 + 8 * g + i;
           if (crossing && found < 0 && run + (double)r8[i] > tc) found = e0 + 8 * g + i;
