@@ -779,8 +779,22 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   // wide: 144-row tiles (the four waves side by side along the vocabulary)
   // where they leave fewer padded rows than 128-row tiles
   const bool rows144 = wide && (M + 143) / 144 * 144 < (M + 127) / 128 * 128;
+  // 144-row tiles 192 or 256 entries wide: the chip runs two workgroups per
+  // CU, so a call takes ceil(tiles / slots) rounds of workgroups; the narrower
+  // tile does 3/4 of the work per round at ~7 % lower efficiency per entry
+  // (measured 0.36 vs 0.46 ms at 144 rows, 0.77 vs 0.69 at 432, 1.40 vs 1.22
+  // at 864), so it is taken when r192 * 0.75 * 1.07 < r256
+  bool n192 = false;
+  if (rows144) {
+    const int64_t slots = 2 * int64_t(device_cus(static_cast<hipStream_t>(stream)));
+    const int64_t ch = (M + 143) / 144;
+    const int64_t r256 = ((int64_t(V) + 255) / 256 * ch + slots - 1) / slots;
+    const int64_t r192 = ((int64_t(V) + 191) / 192 * ch + slots - 1) / slots;
+    n192 = r192 * 321 < r256 * 400;
+  }
   const int mb = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  const int64_t tw = gemm ? (wide ? 256 : 128) : kLmTile, mr = gemm ? (rows144 ? 144 : 128) : 16 * mb;
+  const int64_t tw = gemm ? (n192 ? 192 : wide ? 256 : 128) : kLmTile,
+                mr = gemm ? (rows144 ? 144 : 128) : 16 * mb;
   const int64_t tiles = (int64_t(V) + tw - 1) / tw;
   const int64_t chunks = (M + mr - 1) / mr;
   const int64_t nblk = tiles * chunks;
@@ -794,7 +808,9 @@ int spec_verify_greedy_lmhead(const void* hidden, int64_t hidden_seq_stride,
   auto st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (gemm) {
-    if (rows144)
+    if (n192)
+      hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<144, 192, 32, 1>), dim3(unsigned(grid)), dim3(256), 0, st, A);
+    else if (rows144)
       hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<144, 256, 32, 1>), dim3(unsigned(grid)), dim3(256), 0, st, A);
     else if (wide)
       hipLaunchKernelGGL((sv::k_lmhead_gemm_argmax<128, 256, 32>), dim3(unsigned(grid)), dim3(256), 0, st, A);

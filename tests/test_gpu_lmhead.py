@@ -74,7 +74,7 @@ def _check(h, w, toks, label, hidden=None, weight=None, logits=None):
 
 @pytest.mark.parametrize("B,k,d,V", [(1, 8, 256, 5000), (3, 9, 512, 4099), (16, 4, 256, 3000),
                                      (7, 3, 1024, 777), (13, 7, 256, 3001), (37, 7, 96, 3001),
-                                     (40, 6, 96, 3001)])
+                                     (40, 6, 96, 3001), (16, 8, 256, 5003)])
 def test_lmhead_parity(B, k, d, V):
     rs = np.random.default_rng(B * 1000 + V)
     h, w, vs = workloads.lmhead(B, k, d, V, seed=B + V, boost=1.0)
