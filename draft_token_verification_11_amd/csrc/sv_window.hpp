@@ -233,8 +233,9 @@ __device__ __forceinline__ void win_clear_listed(uint32_t* hist, WinScratch& S, 
   if (t < 8) S.side[t] = 0u;
 }
 
-// Masses, normaliser and top-p cut of a window histogram whose list and
-// figures (S.list, S.m, S.tk, S.tk_entry) are set; NT threads, index t; does
+// Masses, normaliser and top-p cut of a window histogram whose list is set,
+// given the row's max m, top-k key tk and last entry at or above it; NT
+// threads, index t; does
 // its work only when `active` (the same value in all NT threads) but passes
 // its two barriers either way.  The entries' masses are formed entry-major
 // (an octet of lanes per entry, eight keys per lane, octet_mass); one wave
@@ -246,10 +247,9 @@ __device__ __forceinline__ void win_clear_listed(uint32_t* hist, WinScratch& S, 
 template <int NT>
 __device__ __forceinline__ void win_mass_cut(const uint32_t* hist, WinScratch& S, int t, float a,
                                              bool use_k, bool use_p, uint32_t zcnt, uint32_t tiny,
-                                             bool active, int lead = 0) {
+                                             bool active, float m, uint32_t tk, uint32_t last,
+                                             int lead = 0) {
   const int lane = t & (kWave - 1), wv = t / kWave;
-  const float m = S.m;
-  const uint32_t tk = S.tk, last = S.tk_entry;
   if (active) {
     const uint32_t sub = (uint32_t)t & 7u;
     const float vtk = value_of_key16(tk);
@@ -518,7 +518,7 @@ __device__ __forceinline__ int win_stats_mass(uint32_t* hist, WinScratch& S, int
   const bool use_p = top_p < 1.0f;
   const uint32_t zcnt = S.side[kSideZero] + S.side[kSideTinyNeg] + S.side[kSideTinyPos];
   const uint32_t tiny = S.side[kSideTinyNeg] + S.side[kSideTinyPos];
-  win_mass_cut<NT>(hist, S, tid, a, use_k, use_p, zcnt, tiny, true);
+  win_mass_cut<NT>(hist, S, tid, a, use_k, use_p, zcnt, tiny, true, S.m, S.tk, S.tk_entry);
   if (S.fallback) return 2;
   if (out && tid == 0) *out = S.res;
   win_clear_listed<NT>(hist, S, tid);
@@ -539,7 +539,7 @@ __device__ __forceinline__ int win_row_stats(uint32_t* hist, WinScratch& S, int6
 // (the max, the top-k key, the prefix and the cut): with lead 0 for one half
 // and 1 for the other they fall on different SIMDs of the CU, where the
 // halves' first waves share one.  The same statistics as win_row_stats<512> for each
-// row, but with no early return: every thread passes the same five barriers
+// row, but with no early return: every thread passes the same barriers (five, four without top-k)
 // whatever either row holds, so the halves never wait at different ones.
 // Returns this half's status: 0 success (S.res), 1 invalid row (S.res
 // written invalid), 2 the row needs the exact bisection path (the histogram
@@ -615,6 +615,7 @@ __device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int
   };
   // status, the same in every thread of the half (it depends on LDS only)
   int st = 0;
+  uint32_t max_key = 0u;
   const uint32_t e0 = nl != 0u ? (uint32_t)S.list[0] : (uint32_t)kEntNegInf;
   if (s_bad || (e0 == kEntNegInf && s_huge == 0u)) {
     st = 1;  // NaN/+inf, or no finite logit
@@ -622,7 +623,6 @@ __device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int
   } else if (s_huge || (tiny && a > 16.0f) || (e0 == kEntZero && (s_tpos || !s_zero))) {
     st = 2;  // huge values, tiny ones at a low temperature, or a tiny max
   } else {
-    uint32_t max_key;
     if (e0 == kEntZero) {
       max_key = kKey16PosZero;
     } else {
@@ -658,11 +658,15 @@ __device__ __forceinline__ int win_pair_stats(uint32_t* hist, WinScratch& S, int
       }
     }
   }
-  block_sync_lds();  // 3
+  // 3: the top-k key; without top-k every thread has the max and the
+  // figures already (the halves agree on use_k, so both skip this barrier)
+  if (use_k) block_sync_lds();
   if (st == 0 && S.fallback) st = 2;
 
   // Masses, normaliser and top-p cut: barriers 4 and 5.
-  win_mass_cut<NT>(hist, S, t, a, use_k, use_p, zcnt, tiny, st == 0, lead);
+  win_mass_cut<NT>(hist, S, t, a, use_k, use_p, zcnt, tiny, st == 0,
+                   use_k ? S.m : value_of_key16(max_key), use_k ? S.tk : 0u,
+                   use_k ? S.tk_entry : nl - 1u, lead);
   if (st == 0 && S.fallback) st = 2;
   if (st != 2) win_clear_listed<NT>(hist, S, t);
   return st;
