@@ -102,6 +102,7 @@ def draft_tokens_on_gpu(sv, torch, draft, draft_u, T, top_k, top_p, chunk_rows=5
 
 
 KERNEL_SOURCES = ["draft_token_verification_11_amd/csrc/sv_kernels.hpp",
+                  "draft_token_verification_11_amd/csrc/sv_window.hpp",
                   "draft_token_verification_11_amd/csrc/sv_device.hpp",
                   "draft_token_verification_11_amd/csrc/sv_abi.hip"]
 
