@@ -1179,8 +1179,8 @@ struct DrawJob {  // 48 bytes
   int32_t pad;
 };
 constexpr int kDrawThreads = 256;
-constexpr int kDrawGroups = 4;  // groups of 8 elements per thread
-constexpr int64_t kDrawChunk = (int64_t)kDrawThreads * kDrawGroups * 8;  // 8,192 elements
+constexpr int kDrawGroups = 2;  // groups of 8 elements per thread
+constexpr int64_t kDrawChunk = (int64_t)kDrawThreads * kDrawGroups * 8;  // 4,096 elements
 
 // This thread's share of chunk c: the fp32 sums of its groups (in element
 // order) and their fp64 total (in group order); with r32, also every

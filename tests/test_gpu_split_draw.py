@@ -1,5 +1,5 @@
 """Parity of the correction draw spread over the chip: small batches
-(B at most half the CU count) of aligned rows spanning several 8,192-element
+(B at most half the CU count) of aligned rows spanning several 4,096-element
 chunks take k_draw_split instead of one tail workgroup per
 sequence.  Ragged vocabularies (last chunk partial, V not a multiple of 8
 vectors), fp32 and bf16, filtered and unfiltered rows, rejections and bonus
