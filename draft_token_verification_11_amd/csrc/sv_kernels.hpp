@@ -1453,6 +1453,26 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   const int64_t V = A.V;
   const float a = A.a;
 
+  // Wave 0, lane j < k: position j's drafted token, its draw and the two
+  // logits at the token (a bad map entry reads flat row 0, which is readable
+  // and decides nothing).  With row records to read they are loaded first,
+  // so that their round trips overlap the records'; when wave 0 merges
+  // partials or reads rows itself, after the statistics.
+  int32_t x_j = -1;
+  float u_j = 0.0f, lt_j = 0.0f, ld_j = 0.0f;
+  auto load_position = [&]() {
+    if (w == 0 && lane < k) {
+      x_j = A.tokens[b * k + lane];
+      u_j = A.u[b * (k + 1) + lane];
+      if (x_j >= 0 && (int64_t)x_j < V) {
+        lt_j = Elem<T>::load1(A.map.at<T>(b, lane) + x_j);
+        ld_j = Elem<T>::load1(A.map.at<T>(b, k + 1 + lane) + x_j);
+      }
+    }
+  };
+  const bool early = A.rowstat != nullptr;
+  if (early) load_position();
+
   // Row statistics of this sequence.  Dense rows belong to this sequence
   // alone and their workspace records are cleared here; pooled records are
   // shared and cleared by a pass of their own after every sequence is done.
@@ -1543,6 +1563,7 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
     }
   }
   block_sync_lds();
+  if (!early) load_position();
 
   // Ratio test (wave 0, lane j = position j).  Positions are walked in
   // order and the first rejection stops the walk: the sequence is invalid
@@ -1551,17 +1572,15 @@ __device__ void seq_tail(const TailArgs& A, int64_t b, TailScratch& TS) {
   if (w == 0) {
     bool formed = false, acc = false;
     if (lane < k) {
-      const int32_t x = A.tokens[b * k + lane];
+      const int32_t x = x_j;
       formed = TS.st[lane].valid != 0 && TS.st[k + 1 + lane].valid != 0 && x >= 0 &&
                (int64_t)x < V;
       float alpha_out = __builtin_nanf("");
       if (formed) {
-        const T* tr = A.map.at<T>(b, lane);
-        const T* dr = A.map.at<T>(b, k + 1 + lane);
-        const double p = prob_at(Elem<T>::load1(tr + x), TS.st[lane], a);
-        const double q = prob_at(Elem<T>::load1(dr + x), TS.st[k + 1 + lane], a);
+        const double p = prob_at(lt_j, TS.st[lane], a);
+        const double q = prob_at(ld_j, TS.st[k + 1 + lane], a);
         const double alpha = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-        acc = (double)A.u[b * (k + 1) + lane] < alpha;
+        acc = (double)u_j < alpha;
         alpha_out = (float)alpha;
       }
       if (A.accept_prob) A.accept_prob[b * k + lane] = alpha_out;
