@@ -29,7 +29,7 @@ def _case(rs, B, k, V, T, top_k, top_p, bf16, noise):
 
 
 @pytest.mark.parametrize("bf16", [True, False])
-@pytest.mark.parametrize("V", [20000, 16392, 65536])
+@pytest.mark.parametrize("V", [20000, 16392, 65536, 8192, 4104])
 def test_split_draw_parity(bf16, V):
     rs = np.random.default_rng(71 + V + bf16)
     B = 37
