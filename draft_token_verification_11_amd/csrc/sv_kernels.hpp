@@ -2321,8 +2321,10 @@ constexpr uint32_t kNoClaim = 0xFFFFFFFFu;
 // row can be prefetched) only when more than kClaimMargin tasks are queued:
 // a position taken before its task is appended would hold that task back for
 // the rest of the taker's current task (up to a correction draw) while other
-// workgroups sit idle.
-constexpr uint32_t kClaimMargin = 64;
+// workgroups sit idle.  Measured at 512 sequences of four positions on 256
+// workgroups: 224 queued tasks 4.8 % faster than 64, 192 3.0-4.4 %, 160 and
+// 256 1.1-1.5 %, 32 5 % slower.
+constexpr uint32_t kClaimMargin = 224;
 
 // ---------------------------------------------------------------------------
 // Logits processing: merge (unfiltered) partials or copy (filtered) stats into
